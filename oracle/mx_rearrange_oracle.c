@@ -1,0 +1,158 @@
+/*
+ * CPU oracle for the grouped MXFP8 scale-factor rearrangement.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. The HIP library never
+ * includes, links or calls it, and this file uses nothing of the HIP library.
+ *
+ * It is the plain definition written out as nested loops over groups, then over
+ * every position of each group's padded matrix, with one byte copied (or a zero
+ * written) per position. Nothing here is blocked, fused or reordered.
+ *
+ * What is computed, and where the pages state it:
+ *   - The target format is the blocked, swizzled scale-factor layout made of
+ *     128x4 tiles ("[mxfp8 moe training] compute prefix sum of group sizes inside
+ *     kernel intead of precomputing", Context; "[mxfp8 moe training] add bench
+ *     script for scale conversion to blocked format kernels for groups along K",
+ *     description above its table).
+ *   - The pages never print the in-tile byte map or the tile order. Reading
+ *     taken here: element (r, c) of a 128x4 tile sits at byte
+ *     (r mod 32)*16 + (r div 32)*4 + c, and the tiles of a matrix follow each
+ *     other row-major over (row block, column block).
+ *   - Groups along M: each group's rows are padded up to a multiple of 128 and
+ *     the groups' padded row ranges follow one another; a group's output start
+ *     is the prefix sum of the padded sizes of the groups before it (page on the
+ *     in-kernel prefix sum, Context and Changes; page on the fallback CUDA
+ *     kernel, Context). Columns are padded up to a multiple of 4.
+ *   - Groups along K: each group's width in scale columns is padded up to a
+ *     multiple of 4, an empty group adds nothing, and rows are padded up to a
+ *     multiple of 128 ("Add CuTeDSL MXFP8 K-groups scale rearrange kernel",
+ *     review: the notes on empty groups and on the zero-initialised output).
+ *     Reading taken here: each group is its own blocked matrix of
+ *     round_up(rows,128) x W_g bytes, stored contiguously from byte
+ *     round_up(rows,128) * (sum of W_h for h < g).
+ *   - Padding bytes are zero (same review, the note on the output being
+ *     allocated with zeros).
+ *   - Output sizes: K groups, round_up(rows,128) * (cols + 4*G) bytes, which is
+ *     the byte count that reproduces every bandwidth figure printed on the
+ *     K-groups pages (bench-script page, results table; CuTeDSL page, both
+ *     results tables). M groups, by the same rule turned on its side:
+ *     (rows + 128*G) * round_up(cols,4) bytes. Bytes past the last group's
+ *     padded end are zero.
+ *   - Group end offsets are cumulative and exclusive: group g covers
+ *     [offs[g-1], offs[g]) with offs[-1] = 0, in rows (M) or scale columns (K).
+ */
+
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EBADPTR (-1)
+#define ORACLE_EBADSHAPE (-2)
+#define ORACLE_EBADGROUPS (-3)
+#define ORACLE_EBADOFFSETS (-6)
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+/* Byte offset of element (r, c), 0 <= r < 128, 0 <= c < 4, inside one 512-byte tile. */
+static int64_t tile_byte(int64_t r, int64_t c) { return (r % 32) * 16 + (r / 32) * 4 + c; }
+
+/*
+ * Byte offset of element (i, j) of a matrix with `ncols` columns (ncols a
+ * multiple of 4, row count a multiple of 128) stored in the blocked layout:
+ * tile (i div 128, j div 4) is tile number (i div 128) * (ncols / 4) + (j div 4).
+ */
+static int64_t blocked_byte(int64_t ncols, int64_t i, int64_t j) {
+    int64_t tile = (i / 128) * (ncols / 4) + (j / 4);
+    return tile * 512 + tile_byte(i % 128, j % 4);
+}
+
+int64_t oracle_M_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
+    return (rows + 128 * (int64_t)num_groups) * round_up(cols, 4);
+}
+
+int64_t oracle_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
+    return round_up(rows, 128) * (cols + 4 * (int64_t)num_groups);
+}
+
+static int check_args(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                      const int32_t *offs, int32_t num_groups, const uint8_t *out,
+                      int64_t out_bytes, int64_t limit) {
+    if (rows < 0 || cols < 0 || ld < cols) return ORACLE_EBADSHAPE;
+    if (num_groups < 1) return ORACLE_EBADGROUPS;
+    if (offs == 0 || (out == 0 && out_bytes > 0) || (scales == 0 && rows * cols > 0))
+        return ORACLE_EBADPTR;
+    int64_t prev = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        if (offs[g] < prev || offs[g] > limit) return ORACLE_EBADOFFSETS;
+        prev = offs[g];
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Groups along M. Group g holds input rows [offs[g-1], offs[g]); its padded
+ * block of round_up(size,128) rows starts at output row out_row, the sum of the
+ * padded sizes of the groups before it. The output rows of all groups together
+ * form one blocked matrix with round_up(cols,4) columns.
+ */
+int oracle_M_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                    const int32_t *offs, int32_t num_groups, uint8_t *out) {
+    int64_t total = oracle_M_groups_out_bytes(rows, cols, num_groups);
+    int rc = check_args(scales, rows, cols, ld, offs, num_groups, out, total, rows);
+    if (rc != ORACLE_OK) return rc;
+    if (total == 0) return ORACLE_OK;
+    int64_t padded_cols = round_up(cols, 4);
+    memset(out, 0, (size_t)total);
+
+    int64_t out_row = 0;
+    int64_t group_start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t size = offs[g] - group_start;
+        int64_t padded_rows = round_up(size, 128);
+        for (int64_t i = 0; i < padded_rows; ++i) {
+            for (int64_t j = 0; j < padded_cols; ++j) {
+                uint8_t v = 0;
+                if (i < size && j < cols) v = scales[(group_start + i) * ld + j];
+                out[blocked_byte(padded_cols, out_row + i, j)] = v;
+            }
+        }
+        out_row += padded_rows;
+        group_start = offs[g];
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Groups along K. Group g holds input columns [offs[g-1], offs[g]); it becomes
+ * its own blocked matrix of round_up(rows,128) rows and round_up(width,4)
+ * columns, stored contiguously from byte round_up(rows,128) * out_col, where
+ * out_col is the sum of the padded widths of the groups before it.
+ */
+int oracle_K_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                    const int32_t *offs, int32_t num_groups, uint8_t *out) {
+    int64_t total = oracle_K_groups_out_bytes(rows, cols, num_groups);
+    int rc = check_args(scales, rows, cols, ld, offs, num_groups, out, total, cols);
+    if (rc != ORACLE_OK) return rc;
+    if (total == 0) return ORACLE_OK;
+    int64_t padded_rows = round_up(rows, 128);
+    memset(out, 0, (size_t)total);
+
+    int64_t out_col = 0;
+    int64_t group_start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t width = offs[g] - group_start;
+        int64_t padded_width = round_up(width, 4);
+        uint8_t *group_out = out + padded_rows * out_col;
+        for (int64_t i = 0; i < padded_rows; ++i) {
+            for (int64_t j = 0; j < padded_width; ++j) {
+                uint8_t v = 0;
+                if (i < rows && j < width) v = scales[i * ld + group_start + j];
+                group_out[blocked_byte(padded_width, i, j)] = v;
+            }
+        }
+        out_col += padded_width;
+        group_start = offs[g];
+    }
+    return ORACLE_OK;
+}

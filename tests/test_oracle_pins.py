@@ -1,0 +1,222 @@
+"""Pins of the CPU oracle (no GPU).
+
+The oracle is checked against hand-worked positions, the inverse map derived
+from the tile geometry, brute force over every offset vector of tiny shapes, a
+reshape formulation of a single blocked matrix, the pages' printed bandwidth
+figures (which fix the K-groups output size), and whole-workload invariants.
+Deliberately broken copies of the oracle must fail these same pins.
+"""
+
+import itertools
+import os
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+import workloads
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build()
+    return oracle.Oracle(oracle.LIBRARY)
+
+
+def test_hand_worked_positions(orc):
+    assert pins.check_positions(orc) == []
+
+
+def test_hand_worked_zero_counts(orc):
+    # with every input byte non-zero, the zeros are exactly the padding
+    for case in pins.load_positions():
+        rows, cols = case["rows"], case["cols"]
+        A = np.full((rows, cols), 200, dtype=np.uint8)
+        out = orc.rearrange(case["kind"], A, case["offs"])
+        assert int((out == 0).sum()) == case["out_bytes"] - case["copied"], case["name"]
+        assert int((out == 200).sum()) == case["copied"], case["name"]
+
+
+def test_pad_in_tile_bytes_exact(orc):
+    A = np.array([[11, 12, 13], [21, 22, 23]], dtype=np.uint8)
+    out = orc.rearrange("M", A, [2])
+    want = np.zeros(520, np.uint8)
+    want[0:3] = [11, 12, 13]
+    want[16:19] = [21, 22, 23]
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("kind", ["M", "K"])
+def test_inverse_map_random(orc, kind):
+    rng = np.random.default_rng(100 if kind == "M" else 200)
+    fails = []
+    for _ in range(60):
+        rows, cols, ld, offs = pins.random_case(rng, kind)
+        fails += pins.check_inverse(orc, kind, rows, cols, ld, offs)
+    assert fails == []
+
+
+def _nondecreasing(total, G):
+    return [list(c) for c in itertools.combinations_with_replacement(range(total + 1), G)]
+
+
+def test_brute_force_M_tiny(orc):
+    fails = []
+    for rows in range(0, 7):
+        for cols in (1, 3, 4, 5):
+            for G in (1, 2, 3):
+                for offs in _nondecreasing(rows, G):
+                    fails += pins.check_inverse(orc, "M", rows, cols, cols + (rows % 2), offs)
+    assert fails == []
+
+
+def test_brute_force_M_crossing_blocks(orc):
+    # group boundaries on and around multiples of 128
+    fails = []
+    cuts = [0, 1, 127, 128, 129, 255, 256, 300]
+    for a, b in itertools.combinations_with_replacement(cuts, 2):
+        fails += pins.check_inverse(orc, "M", 300, 5, 7, [a, b, 300])
+    assert fails == []
+
+
+def test_brute_force_K_tiny(orc):
+    fails = []
+    for cols in range(0, 10):
+        for rows in (1, 5, 129):
+            for G in (1, 2, 3):
+                for offs in _nondecreasing(cols, G):
+                    fails += pins.check_inverse(orc, "K", rows, cols, cols + 2, offs)
+    assert fails == []
+
+
+def test_single_matrix_reductions(orc):
+    assert pins.check_single_matrix(orc, np.random.default_rng(7)) == []
+
+
+def test_M_and_K_single_group_agree(orc):
+    rng = np.random.default_rng(8)
+    for rows, cols in [(1, 1), (130, 6), (256, 8), (77, 13)]:
+        A = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+        m = orc.rearrange("M", A, [rows])
+        k = orc.rearrange("K", A, [cols])
+        used = pins.ru(rows, 128) * pins.ru(cols, 4)
+        assert np.array_equal(m[:used], k[:used])
+        assert not m[used:].any() and not k[used:].any()
+
+
+def test_K_output_size_reproduces_printed_bandwidth(orc):
+    assert pins.check_bandwidth_tables(orc) == []
+
+
+def test_bandwidth_pin_rejects_other_sizes():
+    # the printed figures single out the column term of the byte count: the
+    # obvious alternatives fail. (Every printed shape has a multiple of 128 rows,
+    # so the figures cannot tell row padding apart; the hand-worked cases do.)
+    rows_tab = pins.load_bandwidth_rows()
+    assert all(r % 128 == 0 for _, r, _, _, _, _ in rows_tab)
+    alternatives = {
+        "no padding": lambda r, c, G: r * c,
+        "no group padding": lambda r, c, G: pins.ru(r, 128) * c,
+        "padding of 3 per group": lambda r, c, G: pins.ru(r, 128) * (c + 3 * G),
+        "padding of 8 per group": lambda r, c, G: pins.ru(r, 128) * (c + 8 * G),
+    }
+    for name, fn in alternatives.items():
+        misses = sum(not pins.bandwidth_matches(r, c, G, us, gb, fn(r, c, G)) for _, r, c, G, us, gb in rows_tab)
+        assert misses > 0, name
+
+
+def test_rejects_invalid_input(orc):
+    A = np.ones((10, 4), np.uint8)
+    for kind, offs in [("M", [5, 3]), ("M", [11]), ("M", [-1, 10]), ("K", [5]), ("K", [2, 1])]:
+        with pytest.raises(ValueError):
+            orc.rearrange(kind, A, offs)
+    with pytest.raises(ValueError):
+        orc.rearrange("M", A, np.zeros(0, np.int32))
+
+
+def test_empty_shapes(orc):
+    # rows = 0 (M): all groups empty, 128*G*Cp zero bytes
+    out = orc.rearrange("M", np.zeros((0, 6), np.uint8), [0, 0])
+    assert out.size == 256 * 8 and not out.any()
+    # cols = 0: M writes nothing; K writes Rp*4G zeros
+    assert orc.rearrange("M", np.zeros((5, 0), np.uint8), [5]).size == 0
+    out = orc.rearrange("K", np.zeros((5, 0), np.uint8), [0, 0, 0])
+    assert out.size == 128 * 12 and not out.any()
+    assert orc.rearrange("K", np.zeros((0, 7), np.uint8), [7]).size == 0
+
+
+@pytest.mark.parametrize("name", ["m_groups_tiny", "m_groups_skinny", "m_groups_experts", "k_groups"])
+def test_workload_invariants(orc, name):
+    w = workloads.make(name)
+    out = orc.rearrange(w.kind, w.scales, w.offs)
+    assert out.size == orc.out_bytes(w.kind, w.rows, w.cols, w.num_groups)
+    # a permutation of the input plus zeros: histograms agree byte value by byte value
+    hist_in = np.bincount(w.scales.reshape(-1), minlength=256)
+    hist_out = np.bincount(out, minlength=256)
+    assert hist_in[0] == 0
+    assert np.array_equal(hist_out[1:], hist_in[1:])
+    assert hist_out[0] == out.size - w.rows * w.cols
+
+
+def test_workload_m_tiny_inverse(orc):
+    w = workloads.make("m_groups_tiny")
+    assert pins.check_inverse(orc, "M", w.rows, w.cols, w.cols, w.offs) == []
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each broken copy of the oracle must fail at least one pin
+# --------------------------------------------------------------------------
+
+MUTANTS = {
+    # each replacement keeps every write inside the output buffer
+    "swapped in-tile strides": ("return (r % 32) * 16 + (r / 32) * 4 + c;",
+                                "return (r / 32) * 16 + (r % 32) * 4 + c;"),
+    "tile index drops the column block": ("int64_t tile = (i / 128) * (ncols / 4) + (j / 4);",
+                                          "int64_t tile = (i / 128) * (ncols / 4);"),
+    "M groups not advanced": ("        out_row += padded_rows;\n", "\n"),
+    "M rows padded to 64": ("int64_t padded_rows = round_up(size, 128);",
+                            "int64_t padded_rows = round_up(size, 64);"),
+    "K one global matrix": ("group_out[blocked_byte(padded_width, i, j)] = v;",
+                            "out[blocked_byte((cols + 4 * (int64_t)num_groups) / 4 * 4, i, out_col + j)] = v;"),
+    "K source column off by one": ("v = scales[i * ld + group_start + j];",
+                                   "v = scales[i * ld + group_start + j + (j + 1 < width)];"),
+    "K output size without group padding": ("return round_up(rows, 128) * (cols + 4 * (int64_t)num_groups);",
+                                            "return round_up(rows, 128) * (cols + 3 * (int64_t)num_groups);"),
+    "M row stride taken as cols": ("v = scales[(group_start + i) * ld + j];",
+                                   "v = scales[(group_start + i) * cols + j];"),
+}
+
+
+def _build_mutant(tmp, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert old in src, name
+    path = os.path.join(tmp, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(tmp, "libmutant_%d.so" % abs(hash(name)))
+    oracle.compile_library(path, lib)
+    return oracle.Oracle(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTANTS[name]
+    tmp = tempfile.mkdtemp()
+    try:
+        mut = _build_mutant(tmp, name, old, new)
+        rng = np.random.default_rng(3)
+        fails = pins.check_positions(mut)
+        fails += pins.check_bandwidth_tables(mut)
+        for kind in ("M", "K"):
+            for _ in range(10):
+                rows, cols, ld, offs = pins.random_case(rng, kind)
+                try:
+                    fails += pins.check_inverse(mut, kind, rows, cols, ld, offs)
+                except (AssertionError, ValueError, IndexError) as e:
+                    fails.append(repr(e))
+        assert fails, "mutant '%s' passed every pin" % name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

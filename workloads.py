@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the grouped MXFP8 scale rearrangement.
+
+This module only draws inputs: E8M0 scale bytes and cumulative int32 group end
+offsets. It holds none of the rearrangement's arithmetic (no padding, no prefix
+sums of padded sizes, no layout), so both the CPU oracle and the HIP library can
+be fed from it without sharing any of the method.
+
+The five named workloads stand in for the shapes the pages benchmark:
+
+* "[mxfp8 moe training] fallback cuda kernel for when input doesn't meet 2d TMA
+  constraints", Benchmarks table: M-groups scales of shape (131072, 44), the
+  DeepSeek-V3-16B expert shape with 44-byte rows.
+* "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by reshaping to
+  2d", Benchmarks tables: activations A of shape (16640, 5120), whose block-32
+  scales are (16640, 160).
+* "Add CuTeDSL MXFP8 K-groups scale rearrange kernel", realistic-shapes table:
+  M x TotalK = 7168 x 131072 and 28672 x 262144 with 8 groups, group widths drawn
+  with a granularity of one scale column (the bench's multiple-of-1 option).
+
+No dataset is involved; every value is drawn from numpy's PCG64 generator with
+the workload's number as seed, offsets first, then values.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass
+class Workload:
+    name: str            # short identifier
+    kind: str            # "M" (groups of rows) or "K" (groups of scale columns)
+    rows: int
+    cols: int
+    offs: np.ndarray     # int32[G], cumulative group end offsets (rows for M, scale cols for K)
+    scales: np.ndarray   # uint8[rows, cols], C-contiguous (row stride == cols)
+    description: str
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.offs.shape[0])
+
+
+def _sorted_cuts(rng, total, n_cuts):
+    """n_cuts distinct interior cut points in [1, total), sorted."""
+    return np.sort(rng.choice(np.arange(1, total), n_cuts, replace=False))
+
+
+def _offsets_from_cuts(cuts, total):
+    return np.concatenate([cuts, [total]]).astype(np.int32)
+
+
+def _values(rng, rows, cols, lo, hi):
+    return rng.integers(lo, hi + 1, size=(rows, cols), dtype=np.uint8)
+
+
+def m_groups_tiny(seed=1):
+    """(1024, 16) scales, 4 groups whose sizes are not multiples of 128, values in [110, 140]."""
+    rng = np.random.default_rng(seed)
+    rows, cols = 1024, 16
+    while True:
+        offs = _offsets_from_cuts(_sorted_cuts(rng, rows, 3), rows)
+        sizes = np.diff(np.concatenate([[0], offs]))
+        if np.all(sizes % 128 != 0):
+            break
+    return Workload("m_groups_tiny", "M", rows, cols, offs, _values(rng, rows, cols, 110, 140),
+                    "M-groups tiny: uint8 scales (1024, 16), 4 groups")
+
+
+def m_groups_skinny(seed=2):
+    """(131072, 44) scales (44-byte rows), 8 multinomial groups, values in [100, 150]."""
+    rng = np.random.default_rng(seed)
+    rows, cols, G = 131072, 44, 8
+    sizes = rng.multinomial(rows, [1.0 / G] * G)
+    offs = np.cumsum(sizes).astype(np.int32)
+    return Workload("m_groups_skinny", "M", rows, cols, offs, _values(rng, rows, cols, 100, 150),
+                    "M-groups skinny: uint8 scales (131072, 44), 8 groups")
+
+
+def m_groups_experts(seed=3):
+    """(16640, 160) scales, 16 expert groups of which 3 are forced empty, values in [100, 150]."""
+    rng = np.random.default_rng(seed)
+    rows, cols, G = 16640, 160, 16
+    empty = rng.choice(G, 3, replace=False)
+    p = np.full(G, 1.0 / (G - 3))
+    p[empty] = 0.0
+    sizes = rng.multinomial(rows, p)
+    offs = np.cumsum(sizes).astype(np.int32)
+    return Workload("m_groups_experts", "M", rows, cols, offs, _values(rng, rows, cols, 100, 150),
+                    "M-groups: uint8 scales (16640, 160), 16 groups, some empty")
+
+
+def k_groups(seed=4):
+    """M = 7168, TotalK = 131072: (7168, 4096) scales, 8 groups of arbitrary scale-column width."""
+    rng = np.random.default_rng(seed)
+    rows, cols, G = 7168, 4096, 8
+    offs = _offsets_from_cuts(_sorted_cuts(rng, cols, G - 1), cols)
+    return Workload("k_groups", "K", rows, cols, offs, _values(rng, rows, cols, 100, 150),
+                    "K-groups: uint8 scales (7168, 4096), 8 groups")
+
+
+def k_groups_large(seed=5):
+    """M = 28672, TotalK = 262144: (28672, 8192) scales, 8 groups of arbitrary scale-column width."""
+    rng = np.random.default_rng(seed)
+    rows, cols, G = 28672, 8192, 8
+    offs = _offsets_from_cuts(_sorted_cuts(rng, cols, G - 1), cols)
+    return Workload("k_groups_large", "K", rows, cols, offs, _values(rng, rows, cols, 100, 150),
+                    "K-groups large: uint8 scales (28672, 8192), 8 groups")
+
+
+WORKLOADS = {
+    "m_groups_tiny": m_groups_tiny,
+    "m_groups_skinny": m_groups_skinny,
+    "m_groups_experts": m_groups_experts,
+    "k_groups": k_groups,
+    "k_groups_large": k_groups_large,
+}
+
+
+def make(name: str) -> Workload:
+    return WORKLOADS[name]()
+
+
+def random_offsets(rng, total, num_groups, p_empty=0.25, short_total=False):
+    """Cumulative end offsets for num_groups groups over [0, total].
+
+    Groups are made empty with probability p_empty; with short_total the last
+    end offset may stop before total (trailing rows or columns in no group).
+    """
+    end = total
+    if short_total and total > 0:
+        end = int(rng.integers(0, total + 1))
+    cuts = np.sort(rng.integers(0, end + 1, size=num_groups - 1)) if num_groups > 1 else np.zeros(0, np.int64)
+    offs = np.concatenate([cuts, [end]]).astype(np.int64)
+    # collapse some groups to empty by repeating the previous end
+    for g in range(num_groups):
+        if rng.random() < p_empty:
+            offs[g] = offs[g - 1] if g > 0 else 0
+    offs = np.maximum.accumulate(offs)
+    return offs.astype(np.int32)
+
+
+def random_scales(rng, rows, cols, ld=None, lo=1, hi=255):
+    """A (rows, cols) uint8 array with row stride ld >= cols (a strided view of a larger buffer)."""
+    ld = cols if ld is None else ld
+    base = rng.integers(lo, hi + 1, size=max(rows * ld, 1), dtype=np.uint8)
+    return np.lib.stride_tricks.as_strided(base[: rows * ld] if rows * ld else base[:0],
+                                           shape=(rows, cols), strides=(ld, 1))

@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped MXFP8 scale rearrangement on one MI355X.
+
+A step is one rearrangement launch over one batch of synthetic scales (group
+scan, lookup, strip load, in-tile interleave, zero padding, stores and tail
+fill all happen inside that launch). The default workload is the M-groups
+skinny case: scales (131072, 44) with 44-byte rows, 8 groups. `--workload`
+selects any of the other named workloads.
+
+Timing: inputs are resident in HBM before the timed region. Steps rotate over
+enough copies of input and output (1 GiB by default, four times the 256 MB
+Infinity Cache) that each step reads its input from HBM rather than from a
+cache. The K timed steps are captured once in a HIP graph (the pages' own
+K-groups benchmark timed CUDA graphs of 1000 launches) and replayed once
+between two synchronisations; `--eager` launches them one by one instead.
+
+Bytes per step follow the pages' convention: every input scale byte read once
+plus the whole output allocation written once.
+
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (read+write) and µs per scale rearrange, M- and K-groups"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "m_groups_skinny"
+# The pages' own figure for the same scale shape and operation, M groups at (131072, 44):
+# 19.46 us for the fallback CUDA kernel ("[mxfp8 moe training] fallback cuda kernel for when
+# input doesn't meet 2d TMA constraints", Benchmarks table). GPU not named on the page.
+PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
+KERNEL_NAMES = {"M": "rearrange_kernel<false>", "K": "rearrange_kernel<true>"}
+KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def align_up(x, a):
+    return (x + a - 1) // a * a
+
+
+class Job:
+    """Device buffers and launches for one workload, rotating over `copies` input/output copies."""
+
+    def __init__(self, name, rotate_bytes=1 << 30, max_copies=4096):
+        import numpy as np
+        import torch
+
+        import group_scale_factor_amd as gsf
+        import workloads
+
+        self.torch = torch
+        self.w = w = workloads.make(name)
+        self.kind = w.kind
+        lib = gsf.library()
+        size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+        self.out_bytes = int(size_fn(w.rows, w.cols, w.num_groups))
+        self.in_bytes = w.rows * w.cols
+        self.bytes_per_step = self.in_bytes + self.out_bytes
+        self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
+        in_pitch = align_up(self.in_bytes, 256)
+        out_pitch = align_up(self.out_bytes, 256)
+        dev = torch.device("cuda")
+        src = torch.from_numpy(np.ascontiguousarray(w.scales).reshape(-1)).to(dev)
+        self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
+        self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
+        for k in range(self.copies):
+            self.inp[k * in_pitch: k * in_pitch + self.in_bytes].copy_(src)
+        self.offs = torch.from_numpy(w.offs).to(dev)
+        self.outs = [self.outbuf[k * out_pitch: k * out_pitch + self.out_bytes] for k in range(self.copies)]
+        self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
+        self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
+        self.fn = lib.mx_block_rearrange_M_groups if w.kind == "M" else lib.mx_block_rearrange_K_groups
+        self.error = gsf.RearrangeError
+        torch.cuda.synchronize()
+
+    def step(self, i, stream=None):
+        """One launch on `stream` (default: torch's current stream), input/output copy i mod copies."""
+        k = i % self.copies
+        if stream is None:
+            stream = self.torch.cuda.current_stream().cuda_stream
+        rc = self.fn(self.in_ptrs[k], self.w.rows, self.w.cols, self.w.cols, self.offs.data_ptr(),
+                     self.w.num_groups, self.out_ptrs[k], stream or None)
+        if rc != 0:
+            raise self.error(rc)
+
+
+def capture(job, first, count):
+    """A HIP graph of `count` launches starting at step `first`."""
+    torch = job.torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + count):
+                job.step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def cpu_baseline(name, seconds):
+    """The CPU oracle, as it is, on the same workload, repeated for about `seconds` of CPU time."""
+    import oracle
+    import workloads
+
+    w = workloads.make(name)
+    out = None
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.rearrange(w.kind, w.scales, w.offs, out)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    bytes_step = w.rows * w.cols + out.size
+    return {
+        "value": round(bytes_step * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d full runs of the %s workload (%dx%d scales, %d groups) in %.1f s, single-threaded C oracle"
+                  % (reps, name, w.rows, w.cols, w.num_groups, el),
+        "us_per_call": round(el / reps * 1e6, 1),
+    }
+
+
+def hbm_traffic(name, kind):
+    """Measured HBM bytes per launch from the committed counter profile, if it matches this kernel."""
+    path = os.path.join(PROFILES, "pmc_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate-mib", type=int, default=1024, help="bytes of input+output rotated over")
+    ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the rearrangement has no multi-GPU path in this build "
+              "(each GPU converts its own groups independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from group_scale_factor_amd import _build
+
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    import group_scale_factor_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+
+    torch.cuda.set_device(0)
+    job = Job(args.workload, rotate_bytes=args.rotate_mib << 20)
+    K, W = args.steps, args.warmup
+
+    if args.eager:
+        for i in range(W):
+            job.step(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(W, W + K):
+            job.step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        gw = capture(job, 0, W) if W > 0 else None
+        gk = capture(job, W, K)
+        if gw is not None:
+            gw.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        gk.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    us_per_launch = gpu_s / K * 1e6
+    value = job.bytes_per_step * K / wall / 1e9
+    achieved = job.bytes_per_step / (gpu_s / K) / 1e9
+    pages_us = PAGES_US.get(args.workload)
+    w = job.w
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 6),
+        "us_per_launch": round(us_per_launch, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(pages_us / (wall / K * 1e6), 3) if pages_us else None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "kind": "%s-groups" % w.kind,
+            "scales_shape": [w.rows, w.cols],
+            "num_groups": w.num_groups,
+            "bytes_per_step": job.bytes_per_step,
+            "rotating_copies": job.copies,
+            "launch": "eager" if args.eager else "hip_graph",
+            "parallelism": "single_gpu",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": hbm_traffic(args.workload, w.kind),
+            "kernel": KERNEL_NAMES[w.kind],
+            "avg_launch_us": round(us_per_launch, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu and args.cpu_seconds > 0 and int(os.environ.get("RANK", "0")) == 0:
+        res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+"""Grouped MXFP8 scale-factor rearrangement for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/mx_rearrange.h``. It only
+marshals arguments: it checks dtypes and devices, reads sizes and strides,
+allocates the output with torch when none is given, and calls the HIP library
+on the current torch stream. Every byte of the result is produced by the HIP
+kernels; there is no CPU or PyTorch fallback, and importing the binding
+fails loudly when the library has not been built.
+
+    out = mx_block_rearrange_M_groups(scales, group_end_offsets)
+    out = mx_block_rearrange_K_groups(scales, group_end_offsets)
+
+``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
+row stride >= cols, any base alignment); ``group_end_offsets`` an int32 CUDA
+tensor of cumulative group ends (rows for M, scale columns for K). The result is
+a flat uint8 tensor of ``*_out_bytes(rows, cols, G)`` bytes holding the blocked
+128x4-tile layout of every group, padding zeroed.
+"""
+
+import ctypes
+import os
+
+from . import _build
+
+LIBRARY = _build.LIBRARY
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            "HIP library %s is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)" % LIBRARY)
+    lib = ctypes.CDLL(LIBRARY)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    for name in ("mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, i32]
+        fn.restype = i64
+    for name in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp]
+        fn.restype = ctypes.c_int
+    lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
+    lib.mx_rearrange_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes handle of libmxrearrange.so."""
+    return _load()
+
+
+def mx_rearrange_M_groups_out_bytes(rows, cols, num_groups):
+    return int(_load().mx_rearrange_M_groups_out_bytes(rows, cols, num_groups))
+
+
+def mx_rearrange_K_groups_out_bytes(rows, cols, num_groups):
+    return int(_load().mx_rearrange_K_groups_out_bytes(rows, cols, num_groups))
+
+
+class RearrangeError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__("mx_block_rearrange failed (%d): %s"
+                         % (status, _load().mx_rearrange_strerror(status).decode()))
+
+
+def _call(kind, scales, group_end_offsets, out, stream):
+    import torch
+
+    lib = _load()
+    if scales.dtype != torch.uint8 or scales.dim() != 2:
+        raise TypeError("scales must be a 2-D torch.uint8 tensor")
+    if group_end_offsets.dtype != torch.int32 or group_end_offsets.dim() != 1:
+        raise TypeError("group_end_offsets must be a 1-D torch.int32 tensor")
+    if not (scales.is_cuda and group_end_offsets.is_cuda):
+        raise ValueError("scales and group_end_offsets must be GPU tensors")
+    if scales.device != group_end_offsets.device:
+        raise ValueError("scales and group_end_offsets must be on the same device")
+    if not group_end_offsets.is_contiguous():
+        raise ValueError("group_end_offsets must be contiguous")
+    rows, cols = scales.shape
+    if rows > 1 and cols > 1 and scales.stride(1) != 1:
+        raise ValueError("scales must have unit column stride (row-major rows)")
+    row_stride = scales.stride(0) if rows > 1 else cols
+    G = group_end_offsets.numel()
+    size_fn = lib.mx_rearrange_M_groups_out_bytes if kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+    n = int(size_fn(rows, cols, G))
+    if n < 0:
+        raise ValueError("invalid sizes rows=%d cols=%d num_groups=%d" % (rows, cols, G))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=scales.device)
+    else:
+        if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < n:
+            raise ValueError("out must be a contiguous uint8 tensor of at least %d bytes" % n)
+        if out.device != scales.device:
+            raise ValueError("out must be on the scales' device")
+    if stream is None:
+        stream = torch.cuda.current_stream(scales.device).cuda_stream
+    fn = lib.mx_block_rearrange_M_groups if kind == "M" else lib.mx_block_rearrange_K_groups
+    rc = fn(scales.data_ptr() or None, rows, cols, row_stride, group_end_offsets.data_ptr() or None,
+            G, out.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return out
+
+
+def mx_block_rearrange_M_groups(scales, group_end_offsets, out=None, stream=None):
+    """Groups along M: each group's rows padded to 128, columns to 4, blocked 128x4 tiles.
+
+    Returns the flat uint8 output (rows + 128*G) * round_up(cols, 4) bytes long.
+    ``stream`` is a raw hipStream_t handle (int); default: torch's current stream.
+    """
+    return _call("M", scales, group_end_offsets, out, stream)
+
+
+def mx_block_rearrange_K_groups(scales, group_end_offsets, out=None, stream=None):
+    """Groups along K: each group's scale columns padded to 4, rows to 128, one blocked matrix per group.
+
+    Returns the flat uint8 output round_up(rows, 128) * (cols + 4*G) bytes long.
+    ``stream`` is a raw hipStream_t handle (int); default: torch's current stream.
+    """
+    return _call("K", scales, group_end_offsets, out, stream)
+
+
+__all__ = [
+    "mx_block_rearrange_M_groups",
+    "mx_block_rearrange_K_groups",
+    "mx_rearrange_M_groups_out_bytes",
+    "mx_rearrange_K_groups_out_bytes",
+    "RearrangeError",
+    "library",
+]

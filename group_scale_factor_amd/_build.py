@@ -1,0 +1,48 @@
+"""Compiles the gfx950 HIP library in-tree with hipcc (no JIT cache, no torch extension)."""
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = [os.path.join(PKG, "csrc", "mx_rearrange.hip")]
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libmxrearrange.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    "--offload-arch=" + ARCH,
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # no packed fp32 instructions in any generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else "hipcc"
+
+
+def build(verbose=False):
+    """Compile libmxrearrange.so next to this file. Always recompiles."""
+    tmp = LIBRARY + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msgs)
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,139 @@
+/*
+ * mx_rearrange.h — C ABI of the gfx950 grouped MXFP8 scale-factor rearrangement.
+ *
+ * Converts a row-major matrix of E8M0 scale bytes (one byte per 32 data
+ * elements) into the blocked, swizzled scale-factor layout built from 128x4
+ * tiles, one group at a time. Groups run along M (token groups, rows) or along
+ * K (weight-gradient groups, scale columns). Each group's padded output start
+ * is a prefix sum of the padded sizes of the groups before it, and it is
+ * computed inside the kernel from the cumulative end offsets: no host
+ * synchronisation, no device-to-host read, no extra launch.
+ *
+ * Sources (pytorch/ao pull-request pages):
+ *   "[mxfp8 moe training] compute prefix sum of group sizes inside kernel intead
+ *    of precomputing" — Context and Changes: the blocked swizzled target format,
+ *    per-group padded starts, the prefix sum moved into the kernel.
+ *   "[mxfp8 moe training] fallback cuda kernel for when input doesn't meet 2d
+ *    TMA constraints" — Context: groups along M, rows of any byte width (44-byte
+ *    rows), no 16-byte row-stride requirement.
+ *   "[mxfp8 moe training] add bench script for scale conversion to blocked
+ *    format kernels for groups along K" — the 128x4 scale-factor tiles of each
+ *    group along K.
+ *   "Add CuTeDSL MXFP8 K-groups scale rearrange kernel" — review notes: group
+ *    widths padded to multiples of 4 scale columns, empty groups contribute
+ *    nothing, padding is zero.
+ *
+ * Layout written (the pages name it but do not print the byte map; this is
+ * the reading implemented):
+ *   - A tile holds a 128-row x 4-column block; its element (r, c) is byte
+ *     (r mod 32)*16 + (r div 32)*4 + c of the tile's 512 bytes.
+ *   - The tiles of a matrix follow one another row-major over (row block,
+ *     column block).
+ *   - M groups: group g = input rows [offs[g-1], offs[g]) (offs[-1] = 0) is
+ *     padded to round_up(size,128) rows and round_up(cols,4) columns; padded
+ *     groups are stacked, so group g's tiles start at byte
+ *     round_up(cols,4) * (sum over h < g of round_up(size_h,128)).
+ *   - K groups: group g = input columns [offs[g-1], offs[g]) is its own blocked
+ *     matrix of round_up(rows,128) rows and round_up(width,4) columns, stored
+ *     contiguously from byte round_up(rows,128) * (sum over h < g of
+ *     round_up(width_h,4)).
+ *   - Every padding byte, and every byte after the last group's data up to the
+ *     end of the output (the sizes below), is written as 0x00.
+ *
+ * Common arguments of both entry points:
+ *   scales             device pointer to the uint8 scale matrix, `rows` rows of
+ *                      `cols` bytes, row r starting at scales + r*row_stride.
+ *                      Any byte alignment. May be NULL when rows*cols == 0.
+ *                      Read only.
+ *   rows, cols         matrix shape in bytes (scale elements); >= 0, and
+ *                      rows, cols + 4*num_groups < 2^31.
+ *   row_stride         bytes between consecutive rows; cols <= row_stride <= 2^24.
+ *                      No alignment requirement.
+ *   group_end_offsets  device pointer to int32[num_groups], cumulative
+ *                      exclusive group ends, non-decreasing, in rows (M) or
+ *                      scale columns (K); the last may be below rows (M) or
+ *                      cols (K), leaving trailing rows or columns in no group.
+ *                      Never NULL. Read only.
+ *   num_groups         G >= 1.
+ *   out                device pointer, 16-byte aligned, at least
+ *                      mx_rearrange_M_groups_out_bytes(...) or
+ *                      mx_rearrange_K_groups_out_bytes(...) bytes. Every byte of
+ *                      that range is written (no pre-zeroing needed); no byte
+ *                      past it is touched. Must not overlap the inputs. May be
+ *                      NULL when the output size is 0.
+ *   stream             HIP stream the single kernel is enqueued on (NULL: the
+ *                      default stream).
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing,
+ * keeps no state and holds no pointer after returning. Calls are thread-safe.
+ *
+ * Errors: a negative status is returned and nothing is enqueued when an
+ * argument is invalid (see MX_REARRANGE_E*); the checks read no device memory.
+ * Offsets that break the preconditions above cannot be checked without a
+ * synchronisation: the kernel then clamps each end offset into
+ * [previous end, rows or cols], so it still reads only inside the scale
+ * matrix and writes only inside out[0, out_bytes); the bytes written are then
+ * those of the clamped offsets.
+ */
+#ifndef MX_REARRANGE_H
+#define MX_REARRANGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+#define MX_REARRANGE_OK 0
+#define MX_REARRANGE_ENULL (-1)        /* a required pointer is NULL */
+#define MX_REARRANGE_ESHAPE (-2)       /* rows/cols negative or too large, or row_stride outside [cols, 2^24] */
+#define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 */
+#define MX_REARRANGE_EALIGN (-4)       /* out is not 16-byte aligned */
+#define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
+
+/*
+ * Output size in bytes for groups along M: (rows + 128*num_groups) *
+ * round_up(cols, 4). This bounds the padded total for any group sizes, since
+ * the sum of round_up(size_g, 128) is below rows + 128*num_groups. Returns -1
+ * for invalid sizes.
+ */
+int64_t mx_rearrange_M_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups);
+
+/*
+ * Output size in bytes for groups along K: round_up(rows, 128) *
+ * (cols + 4*num_groups) — the byte count behind every bandwidth figure printed
+ * on the K-groups pages. Returns -1 for invalid sizes.
+ */
+int64_t mx_rearrange_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups);
+
+/*
+ * Groups along M (token groups): rows [offs[g-1], offs[g]) of `scales` become
+ * group g's blocked matrix, rows padded to a multiple of 128 and columns to a
+ * multiple of 4, stacked after the previous groups' padded rows. One kernel
+ * launch on `stream`; returns after enqueueing.
+ */
+int mx_block_rearrange_M_groups(const uint8_t *scales, int64_t rows, int64_t cols,
+                                int64_t row_stride, const int32_t *group_end_offsets,
+                                int32_t num_groups, uint8_t *out, hipStream_t stream);
+
+/*
+ * Groups along K (weight-gradient groups): columns [offs[g-1], offs[g]) of
+ * `scales` become group g's blocked matrix, columns padded to a multiple of 4
+ * and rows to a multiple of 128, stored contiguously after the previous
+ * groups' matrices. One kernel launch on `stream`; returns after enqueueing.
+ */
+int mx_block_rearrange_K_groups(const uint8_t *scales, int64_t rows, int64_t cols,
+                                int64_t row_stride, const int32_t *group_end_offsets,
+                                int32_t num_groups, uint8_t *out, hipStream_t stream);
+
+/* Static text for a status code returned above. */
+const char *mx_rearrange_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_REARRANGE_H */

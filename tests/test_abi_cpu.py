@@ -1,0 +1,121 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+declared entry point, sizes its outputs like the oracle, and rejects invalid
+arguments before any HIP call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from group_scale_factor_amd import _build
+
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    import group_scale_factor_amd as gsf
+
+    return gsf.library()
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fname in sorted(os.listdir(inc)):
+        if not fname.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fname)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for want in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups",
+                 "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_out_bytes_match_oracle(lib):
+    import oracle
+
+    rng = np.random.default_rng(5)
+    shapes = [(0, 0, 1), (1, 1, 1), (1024, 16, 4), (131072, 44, 8), (16640, 160, 16), (7168, 4096, 8),
+              (28672, 8192, 8), (130, 10, 3), (5, 4097, 200)]
+    shapes += [(int(rng.integers(0, 5000)), int(rng.integers(0, 5000)), int(rng.integers(1, 300))) for _ in range(50)]
+    for rows, cols, G in shapes:
+        assert lib.mx_rearrange_M_groups_out_bytes(rows, cols, G) == oracle.out_bytes("M", rows, cols, G)
+        assert lib.mx_rearrange_K_groups_out_bytes(rows, cols, G) == oracle.out_bytes("K", rows, cols, G)
+    assert lib.mx_rearrange_M_groups_out_bytes(-1, 4, 1) == -1
+    assert lib.mx_rearrange_K_groups_out_bytes(4, 4, 0) == -1
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("fn", ["mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups"])
+def test_argument_validation(lib, fn):
+    f = getattr(lib, fn)
+    # (scales, rows, cols, ld, offs, G, out) -> expected status
+    cases = [
+        ((FAKE, 4, 4, 4, None, 1, FAKE), -1),       # offsets NULL
+        ((None, 4, 4, 4, FAKE, 1, FAKE), -1),       # scales NULL with data
+        ((FAKE, 4, 4, 4, FAKE, 1, None), -1),       # out NULL with output bytes
+        ((FAKE, -1, 4, 4, FAKE, 1, FAKE), -2),      # negative rows
+        ((FAKE, 4, -4, 4, FAKE, 1, FAKE), -2),      # negative cols
+        ((FAKE, 4, 8, 7, FAKE, 1, FAKE), -2),       # row stride below cols
+        ((FAKE, 4, 8, (1 << 24) + 1, FAKE, 1, FAKE), -2),  # row stride too large
+        ((FAKE, 1 << 31, 8, 8, FAKE, 1, FAKE), -2),  # rows past the int32 range
+        ((FAKE, 4, 4, 4, FAKE, 0, FAKE), -3),       # no groups
+        ((FAKE, 4, 4, 4, FAKE, -2, FAKE), -3),
+        ((FAKE, 4, 4, 4, FAKE, 1, FAKE + 8), -4),   # out not 16-byte aligned
+    ]
+    for args, want in cases:
+        assert f(*args, None) == want, (fn, args)
+    # nothing to write: success without a launch
+    if fn.endswith("M_groups"):
+        assert f(None, 5, 0, 0, FAKE, 2, None, None) == 0
+    else:
+        assert f(None, 0, 9, 9, FAKE, 2, None, None) == 0
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        s = lib.mx_rearrange_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_binding_has_no_cpu_path():
+    # the binding refuses CPU tensors instead of computing anything itself
+    import torch
+
+    import group_scale_factor_amd as gsf
+
+    with pytest.raises(ValueError):
+        gsf.mx_block_rearrange_M_groups(torch.zeros((4, 4), dtype=torch.uint8), torch.tensor([4], dtype=torch.int32))
+    with pytest.raises(TypeError):
+        gsf.mx_block_rearrange_K_groups(torch.zeros((4, 4), dtype=torch.int8), torch.tensor([4], dtype=torch.int32))
+
+
+def test_product_code_never_touches_the_oracle():
+    # the HIP source and the binding neither include nor import the oracle
+    pkg = os.path.join(ROOT, "group_scale_factor_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)
+    src = open(os.path.join(ROOT, "oracle", "mx_rearrange_oracle.c")).read()
+    assert "#include" not in src.replace("#include <stdint.h>", "").replace("#include <string.h>", "")

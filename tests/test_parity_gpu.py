@@ -1,0 +1,252 @@
+"""Parity of the HIP library with the CPU oracle, byte for byte (GPU).
+
+Every case prints its name before touching the GPU. The output buffer is
+prefilled with 0xAB and followed by guard bytes, so a test also shows that the
+kernel writes every byte of its output and nothing past it.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+POISON = 0xAB
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    from group_scale_factor_amd import _build
+    import oracle
+
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    if not os.path.exists(oracle.LIBRARY):
+        oracle.build()
+    import group_scale_factor_amd as gsf
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return gsf, oracle, torch
+
+
+def _device_scales(torch, scales_np, misalign=0):
+    """Upload a (rows, cols) host view (any row stride) to a device view whose base is misaligned by `misalign`."""
+    rows, cols = scales_np.shape
+    ld = scales_np.strides[0] if rows > 1 else cols
+    ld = max(ld, cols)
+    flat = np.zeros(misalign + rows * ld + 64, np.uint8)
+    if rows and cols:
+        dst = np.lib.stride_tricks.as_strided(flat[misalign:], shape=(rows, cols), strides=(ld, 1))
+        dst[...] = scales_np
+    buf = torch.from_numpy(flat).cuda()
+    if rows == 0:
+        return buf[misalign:misalign].view(0, cols) if cols else buf[:0].view(0, 0)
+    return torch.as_strided(buf, (rows, cols), (ld, 1), misalign)
+
+
+def run_case(env, kind, scales_np, offs_np, misalign=0, label=""):
+    gsf, oracle, torch = env
+    rows, cols = scales_np.shape
+    G = len(offs_np)
+    print("case", label, kind, "rows", rows, "cols", cols, "ld", scales_np.strides[0] if rows > 1 else cols,
+          "G", G, "misalign", misalign, flush=True)
+    want = oracle.rearrange(kind, scales_np, offs_np)
+    n = want.size
+    dev = _device_scales(torch, scales_np, misalign)
+    offs = torch.from_numpy(np.asarray(offs_np, np.int32)).cuda()
+    buf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    fn = gsf.mx_block_rearrange_M_groups if kind == "M" else gsf.mx_block_rearrange_K_groups
+    out = fn(dev, offs, out=buf[:n])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert n == 0 or out.data_ptr() == buf.data_ptr()
+    assert (got[n:] == POISON).all(), "%s: bytes past the output were written" % label
+    if not np.array_equal(got[:n], want):
+        bad = np.nonzero(got[:n] != want)[0]
+        raise AssertionError("%s: %d of %d bytes differ, first at %d (got %d want %d)"
+                             % (label, bad.size, n, bad[0], got[bad[0]], want[bad[0]]))
+    return got[:n]
+
+
+# --------------------------------------------------------------------------
+# the five workloads, full size
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["m_groups_tiny", "m_groups_skinny", "m_groups_experts", "k_groups", "k_groups_large"])
+def test_workload_bit_exact(env, name):
+    import workloads
+
+    w = workloads.make(name)
+    run_case(env, w.kind, w.scales, w.offs, label=name)
+
+
+# --------------------------------------------------------------------------
+# hand-worked cases and tiny brute force
+# --------------------------------------------------------------------------
+
+def test_hand_worked_cases(env):
+    import pins
+
+    rng = np.random.default_rng(21)
+    for case in pins.load_positions():
+        A = rng.integers(1, 256, size=(case["rows"], case["cols"]), dtype=np.uint8)
+        run_case(env, case["kind"], A, np.array(case["offs"], np.int32), label=case["name"])
+
+
+def test_brute_force_tiny(env):
+    import itertools
+
+    rng = np.random.default_rng(22)
+    for kind, total_dim in (("M", 0), ("K", 1)):
+        for rows, cols in [(5, 3), (6, 9), (129, 7), (1, 9)]:
+            total = (rows, cols)[total_dim]
+            A = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+            for G in (1, 2, 3):
+                for offs in itertools.combinations_with_replacement(range(total + 1), G):
+                    run_case(env, kind, A, np.array(offs, np.int32), label="brute")
+
+
+# --------------------------------------------------------------------------
+# seeded fuzz: shapes, strides, misaligned bases, empty groups, many groups
+# --------------------------------------------------------------------------
+
+def _fuzz(env, kind, seed, n):
+    import workloads
+
+    rng = np.random.default_rng(seed)
+    row_choices = [0, 1, 2, 31, 127, 128, 129, 255, 300, 513, 1000, 2049]
+    col_choices = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 44, 45, 63, 64, 129, 160, 255, 256, 257, 300, 513, 1031]
+    for i in range(n):
+        rows = int(rng.choice(row_choices))
+        cols = int(rng.choice(col_choices))
+        extra = int(rng.choice([0, 0, 1, 3, 12, 13, 64]))
+        ld = cols + extra
+        G = int(rng.choice([1, 2, 3, 8, 16, 63, 64, 65, 130]))
+        total = rows if kind == "M" else cols
+        offs = workloads.random_offsets(rng, total, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        A = workloads.random_scales(rng, rows, cols, ld)
+        run_case(env, kind, A, offs, misalign=int(rng.integers(0, 16)), label="fuzz%s-%d" % (kind, i))
+
+
+def test_fuzz_M(env):
+    _fuzz(env, "M", 31, 120)
+
+
+def test_fuzz_K(env):
+    _fuzz(env, "K", 32, 120)
+
+
+@pytest.mark.parametrize("kind", ["M", "K"])
+def test_wide_and_odd_shapes(env, kind):
+    rng = np.random.default_rng(33)
+    for rows, cols, offs in [(300, 4097, [1000, 1000, 4097]), (130, 129, [64, 129]), (257, 4097, [4097]),
+                             (1, 1, [1]), (128, 1025, [3, 700, 1025]), (1000, 600, [1, 2, 3, 599])]:
+        offs = np.array(offs, np.int32)
+        if kind == "M":
+            offs = np.minimum(offs * rows // max(cols, 1), rows).astype(np.int32)
+        A = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+        run_case(env, kind, A, offs, misalign=int(rng.integers(0, 16)), label="wide")
+
+
+def test_empty_inputs(env):
+    gsf, oracle, torch = env
+    # M with no rows: all groups empty, output all zero
+    run_case(env, "M", np.zeros((0, 6), np.uint8), np.array([0, 0, 0], np.int32), label="M rows=0")
+    # K with no columns: output all zero
+    run_case(env, "K", np.zeros((5, 0), np.uint8), np.array([0, 0], np.int32), label="K cols=0")
+    # nothing to write
+    out = gsf.mx_block_rearrange_M_groups(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
+                                          torch.tensor([5], dtype=torch.int32, device="cuda"))
+    assert out.numel() == 0
+
+
+# --------------------------------------------------------------------------
+# offsets that break the preconditions: clamped, never out of bounds
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["M", "K"])
+def test_invalid_offsets_are_clamped(env, kind):
+    rng = np.random.default_rng(34)
+    for raw in ([50, 20, 400], [-5, 10, 10**6], [300, 0, 0], [2**31 - 1] * 3, [-(2**31)] * 2):
+        rows, cols = 300, 45
+        A = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+        limit = rows if kind == "M" else cols
+        clamped = np.minimum(np.maximum.accumulate(np.maximum(np.array(raw, np.int64), 0)), limit).astype(np.int32)
+        gsf, oracle, torch = env
+        want = oracle.rearrange(kind, A, clamped)
+        n = want.size
+        buf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+        fn = gsf.mx_block_rearrange_M_groups if kind == "M" else gsf.mx_block_rearrange_K_groups
+        print("case invalid offsets", kind, raw, flush=True)
+        fn(torch.from_numpy(A).cuda(), torch.tensor(raw, dtype=torch.int32, device="cuda"), out=buf[:n])
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        assert (got[n:] == POISON).all()
+        assert np.array_equal(got[:n], want)
+
+
+# --------------------------------------------------------------------------
+# determinism, streams, errors
+# --------------------------------------------------------------------------
+
+def test_repeat_is_deterministic(env):
+    import workloads
+
+    gsf, oracle, torch = env
+    for name in ("m_groups_experts", "k_groups"):
+        w = workloads.make(name)
+        print("case repeat", name, flush=True)
+        s = torch.from_numpy(w.scales).cuda()
+        o = torch.from_numpy(w.offs).cuda()
+        fn = gsf.mx_block_rearrange_M_groups if w.kind == "M" else gsf.mx_block_rearrange_K_groups
+        outs = [fn(s, o) for _ in range(3)]
+        torch.cuda.synchronize()
+        for x in outs[1:]:
+            assert torch.equal(x, outs[0])
+
+
+def test_side_stream(env):
+    import workloads
+
+    gsf, oracle, torch = env
+    w = workloads.make("m_groups_tiny")
+    print("case side stream", flush=True)
+    s = torch.from_numpy(w.scales).cuda()
+    o = torch.from_numpy(w.offs).cuda()
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        out = gsf.mx_block_rearrange_M_groups(s, o)
+    st.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.rearrange("M", w.scales, w.offs))
+
+
+def test_misaligned_out_is_rejected(env):
+    gsf, oracle, torch = env
+    s = torch.ones((4, 4), dtype=torch.uint8, device="cuda")
+    o = torch.tensor([4], dtype=torch.int32, device="cuda")
+    buf = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gsf.RearrangeError) as e:
+        gsf.mx_block_rearrange_M_groups(s, o, out=buf[8:])
+    assert e.value.status == -4
+
+
+def test_bench_launch_configuration(env):
+    """The exact launches bench.py times (rotating buffers, its stream) give the oracle's bytes."""
+    import bench
+
+    gsf, oracle, torch = env
+    for name in ("m_groups_skinny", "k_groups_large"):
+        print("case bench config", name, flush=True)
+        job = bench.Job(name, rotate_bytes=0)  # one copy: both launches write the same output
+        job.step(0)
+        job.step(1)
+        torch.cuda.synchronize()
+        want = oracle.rearrange(job.w.kind, job.w.scales, job.w.offs)
+        for k in range(min(2, job.copies)):
+            assert np.array_equal(job.outs[k].cpu().numpy(), want)

@@ -15,20 +15,19 @@
 //
 // The work is pure data movement, bound by HBM bandwidth; there is no
 // arithmetic on the scale values. Design:
-//   * One workgroup (4 wave64s) handles one work unit: 128 rows x up to 256
-//     padded scale columns of one group, i.e. up to 64 output tiles, which are
-//     contiguous in the output (up to 32 KiB written with 16-byte stores).
+//   * One workgroup handles one work unit: 128 rows x a column chunk of one
+//     group, i.e. a run of whole output tiles that are contiguous in the output.
 //   * Group lookup: every wave loads the end offsets, one group per lane,
 //     clamps them into a non-decreasing sequence, and forms the padded sizes
-//     and their prefix sums with wave shuffles; a ballot over the cumulative
-//     unit counts names the group of the unit. G > 64 is handled in 64-lane
-//     slices with a carry.
+//     and their prefix sums with DPP scans; a ballot over the cumulative unit
+//     counts names the group of the unit. G > 64 is handled in 64-lane slices
+//     with a carry.
 //   * Load: the unit's source bytes are fetched as 16-byte aligned pieces
-//     (global_load_dwordx4) covering each row segment (or, for contiguous
-//     skinny rows, the whole strip as one range) and staged in LDS. A 16-byte
-//     aligned piece that contains at least one byte of the matrix lies inside
-//     the same memory page as that byte, so the cover never touches a page
-//     the matrix does not; the extra bytes are never emitted.
+//     (buffer_load_dwordx4) covering each row segment (or, for packed narrow
+//     rows, the whole strip as one range) and staged in LDS. A 16-byte aligned
+//     piece that contains at least one byte of the matrix lies inside the same
+//     memory page as that byte, so the cover never touches a page the matrix
+//     does not; the extra bytes are never emitted.
 //   * Interleave: after one barrier each lane assembles one 16-byte output
 //     unit — the same 4-byte column word of rows i, i+32, i+64, i+96 of the
 //     tile — from LDS. When the source is not 4-byte aligned each word is
@@ -51,22 +50,36 @@
 
 namespace {
 
-constexpr int kThreads = 256;                 // 4 wave64s
 constexpr int kWave = 64;
 constexpr int kTileRows = 128;
-constexpr int kUnitCols = 256;                // padded scale columns per work unit
-constexpr int kMaxPieces = (kUnitCols + 30) / 16;            // 16-byte pieces covering one row segment
-constexpr int kMaxPitch = 16 * kMaxPieces + 4;               // LDS row pitch: 4*pieces+1 words, odd
+constexpr int kMaxUnitCols = 256;             // widest column chunk of a unit
+constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits M row blocks into
+constexpr int kTargetUnits = 1024;            // M: split row blocks into chunks until this many units
+constexpr int kFlatMaxCols = 64;              // M: widest packed row staged as one flat range
+constexpr int kMaxPieces = (kMaxUnitCols + 30) / 16;   // 16-byte pieces covering one row segment
+constexpr int kMaxPitch = 16 * kMaxPieces + 4;         // LDS row pitch: 4*pieces+1 words, odd
+constexpr int kMaxFlatPieces = (kTileRows * kFlatMaxCols + 30) / 16;
 constexpr int kLdsSlack = 16;                 // room for the second word of an unaligned read
-constexpr int kMaxLdsBytes = kTileRows * kMaxPitch + kLdsSlack;
-constexpr int kMaxLoadIters = (kTileRows * kMaxPieces + kThreads - 1) / kThreads;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // keeps a unit's byte span inside 32-bit buffer offsets
 constexpr uint32_t kOutOfRange = 0xfffffff0u;          // buffer offset past any range: the load returns 0
 constexpr int kRawBufferFlags = 0x00020000;            // buffer descriptor word 3: 32-bit raw data
 
-static_assert(kUnitCols % 16 == 0, "unit width must be a multiple of 16 columns");
-static_assert(kMaxLdsBytes <= 64 * 1024, "LDS per workgroup");
+// Staging modes; each is its own kernel instantiation.
+enum Mode : int {
+  kModeMFlat = 0,   // M groups, packed rows of <= 64 bytes, one contiguous range per 128-row strip
+  kModeMRows = 1,   // M groups, one row segment at a time
+  kModeKRows = 2,   // K groups, one row segment at a time
+};
+
+constexpr int threads_for(int mode) { return mode == kModeMFlat ? 128 : 256; }
+constexpr int load_iters_for(int mode) {
+  return mode == kModeMFlat ? (kMaxFlatPieces + threads_for(mode) - 1) / threads_for(mode)
+                            : (kTileRows * kMaxPieces + threads_for(mode) - 1) / threads_for(mode);
+}
+
+static_assert(kMaxUnitCols % 16 == 0 && kMinUnitCols % 16 == 0, "unit widths must be multiples of 16 columns");
+static_assert(kTileRows * kMaxPitch + kLdsSlack <= 64 * 1024, "LDS per workgroup");
 
 struct Params {
   const uint8_t *src;
@@ -80,33 +93,45 @@ struct Params {
   int cols;
   int groups;
   int padded_cols;     // M: round_up(cols, 4)
-  int unit_cols;       // M: columns per unit in a row block; K: kUnitCols
+  int unit_cols;       // columns per unit chunk (multiple of 4)
   int per_row;         // M: units per output row block; K: units per 128-row block
   int pitch;           // LDS row pitch (bytes) in per-row staging
   int pieces;          // 16-byte pieces per LDS row in per-row staging
-  int flat;            // M only: stage each 128-row strip as one contiguous range
 };
 
 // ---------------------------------------------------------------------------
-// wave64 helpers
+// wave64 scans with DPP (row shifts within 16-lane rows, then row broadcasts)
 // ---------------------------------------------------------------------------
 
-__device__ inline int wave_inclusive_sum(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+template <int CTRL>
+__device__ inline int dpp_shr(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);  // lanes without a source read 0
+}
+
+__device__ inline int wave_inclusive_sum(int x) {
+  x += dpp_shr<0x111>(x);                                      // row_shr:1
+  x += dpp_shr<0x112>(x);                                      // row_shr:2
+  x += dpp_shr<0x114>(x);                                      // row_shr:4
+  x += dpp_shr<0x118>(x);                                      // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
-__device__ inline int wave_inclusive_max(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x = max(x, y);
-  }
+// Inclusive running maximum of non-negative values.
+__device__ inline int wave_inclusive_max(int x) {
+  x = max(x, dpp_shr<0x111>(x));
+  x = max(x, dpp_shr<0x112>(x));
+  x = max(x, dpp_shr<0x114>(x));
+  x = max(x, dpp_shr<0x118>(x));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
   return x;
+}
+
+// Value of the previous lane (wave_shr:1); lane 0 gets `first`.
+__device__ inline int wave_shift_up(int x, int first) {
+  return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
 }
 
 __device__ inline int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
@@ -116,16 +141,14 @@ __device__ inline int lane_value(int x, int l) { return __builtin_amdgcn_readlan
 // ---------------------------------------------------------------------------
 
 // Where a work unit sits among the groups. Group sizes are counted in rows (M)
-// or scale columns (K); "units" are 128-row blocks (M) or kUnitCols-column
+// or scale columns (K); "units" are 128-row blocks (M) or unit_cols-column
 // chunks of one 128-row block (K).
 struct GroupHit {
   int group;        // index of the group holding the unit; == groups for the tail
   int start;        // first input row (M) / column (K) of the group
   int size;         // rows (M) / columns (K) of the group
-  int first_unit;   // units of all earlier groups
-  int padded_start; // K: padded columns of all earlier groups
-  int total_units;  // tail only: units of all groups
-  int total_padded; // tail only (K): padded columns of all groups
+  int first_unit;   // units of all earlier groups (all groups, for the tail)
+  int padded_start; // K: padded columns of all earlier groups (all groups, for the tail)
 };
 
 // Scans the cumulative end offsets in 64-lane slices and finds the group that
@@ -133,34 +156,31 @@ struct GroupHit {
 // into [previous end, limit], which leaves valid offsets unchanged and keeps
 // every access in bounds for invalid ones.
 template <bool KGROUPS>
-__device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int limit,
-                               int target, int lane) {
+__device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int limit, int unit_cols,
+                               int target) {
+  const int lane = threadIdx.x & (kWave - 1);
   int carry_end = 0, carry_units = 0, carry_padded = 0;
   for (int base = 0; base < groups; base += kWave) {
     const int g = base + lane;
     const bool active = g < groups;
     int end = active ? offs[g] : 0;
     end = min(max(end, 0), limit);
-    end = max(wave_inclusive_max(end, lane), carry_end);
-    int prev = __shfl_up(end, 1, kWave);
-    if (lane == 0) prev = carry_end;
+    end = max(wave_inclusive_max(end), carry_end);
+    const int prev = wave_shift_up(end, carry_end);
     const int size = end - prev;                       // 0 for lanes past the last group
     const int padded = KGROUPS ? (size + 3) & ~3 : 0;  // K: width padded to 4 columns
-    const int units = KGROUPS ? (padded + kUnitCols - 1) / kUnitCols : (size + kTileRows - 1) / kTileRows;
-    const int cum_units = wave_inclusive_sum(units, lane) + carry_units;
-    const int cum_padded = KGROUPS ? wave_inclusive_sum(padded, lane) + carry_padded : 0;
+    const int units = KGROUPS ? (padded + unit_cols - 1) / unit_cols : (size + kTileRows - 1) / kTileRows;
+    const int cum_units = wave_inclusive_sum(units) + carry_units;
+    const int cum_padded = KGROUPS ? wave_inclusive_sum(padded) + carry_padded : 0;
     const unsigned long long before = __ballot(active && cum_units <= target);
     const int n = __popcll(before);
-    const int in_slice = min(kWave, groups - base);
-    if (n < in_slice) {
+    if (n < min(kWave, groups - base)) {
       GroupHit h;
       h.group = base + n;
       h.start = lane_value(prev, n);
       h.size = lane_value(size, n);
       h.first_unit = lane_value(cum_units, n) - lane_value(units, n);
       h.padded_start = KGROUPS ? lane_value(cum_padded, n) - lane_value(padded, n) : 0;
-      h.total_units = 0;
-      h.total_padded = 0;
       return h;
     }
     carry_end = lane_value(end, kWave - 1);
@@ -173,8 +193,6 @@ __device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int
   h.size = 0;
   h.first_unit = carry_units;
   h.padded_start = carry_padded;
-  h.total_units = carry_units;
-  h.total_padded = carry_padded;
   return h;
 }
 
@@ -183,18 +201,20 @@ __device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int
 // aligned and hi a multiple of 4
 // ---------------------------------------------------------------------------
 
+template <int NT>
 __device__ inline void zero_part(uint8_t *__restrict__ out, int64_t lo, int64_t hi, int64_t part,
                                  int64_t parts) {
+  if (lo >= hi || parts <= 0) return;
   const int64_t len16 = (hi - lo + 15) >> 4;
   const int64_t per = (len16 + parts - 1) / parts;
   const int64_t b = lo + 16 * min(per * part, len16);
   const int64_t e = min(lo + 16 * min(per * (part + 1), len16), hi);
   const int64_t full = b + ((e - b) & ~int64_t(15));
   const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int64_t p = b + 16 * threadIdx.x; p < full; p += 16 * kThreads)
-    *reinterpret_cast<uint4 *>(out + p) = z;
-  for (int64_t p = full + 4 * threadIdx.x; p < e; p += 4 * kThreads)
-    *reinterpret_cast<uint32_t *>(out + p) = 0u;
+  for (int64_t q = b + 16 * threadIdx.x; q < full; q += 16 * NT)
+    *reinterpret_cast<uint4 *>(out + q) = z;
+  for (int64_t q = full + 4 * threadIdx.x; q < e; q += 4 * NT)
+    *reinterpret_cast<uint32_t *>(out + q) = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -216,29 +236,34 @@ __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t offset) {
 // Per-row staging: row r's segment [a, a + seg) with a = row_base + r*ld is
 // fetched as the 16-byte pieces covering it and stored at LDS r*pitch; its
 // first byte then sits at r*pitch + (a mod 16).
+template <int NT, int ITERS>
 __device__ inline void stage_rows(uint8_t *__restrict__ lds, const uint8_t *row_base, int64_t ld,
                                   int nrows, int seg, int pitch, int pieces) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(row_base) & 15);
   const uint8_t *base = row_base - lead;  // 16-byte aligned
   const uint32_t span = uint32_t((lead + int64_t(nrows - 1) * ld + seg + 15) & ~int64_t(15));
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(base, span);
-  const int step_r = kThreads / pieces, step_k = kThreads % pieces;
+  const int slots = nrows * pieces;
+  const int step_r = NT / pieces, step_k = NT % pieces;
   int r = threadIdx.x / pieces, k = threadIdx.x % pieces;
-  uint4 v[kMaxLoadIters];
-  uint32_t lds_off[kMaxLoadIters];
+  uint4 v[ITERS];
+  uint32_t lds_off[ITERS];
 #pragma unroll
-  for (int it = 0; it < kMaxLoadIters; ++it) {
-    const uint32_t row_off = lead + uint32_t(r) * uint32_t(ld);  // in range whenever r < nrows
-    const int need = int(((row_off & 15) + seg + 15) >> 4);
-    const bool valid = r < nrows && k < need;
-    v[it] = load16(rsrc, valid ? (row_off & ~15u) + 16 * k : kOutOfRange);
-    lds_off[it] = valid ? uint32_t(r * pitch + 16 * k) : kOutOfRange;
+  for (int it = 0; it < ITERS; ++it) {
+    lds_off[it] = kOutOfRange;
+    if (it * NT < slots) {                                         // uniform
+      const uint32_t row_off = lead + uint32_t(r) * uint32_t(ld);  // in range whenever r < nrows
+      const int need = int(((row_off & 15) + seg + 15) >> 4);
+      const bool valid = r < nrows && k < need;
+      v[it] = load16(rsrc, valid ? (row_off & ~15u) + 16 * k : kOutOfRange);
+      lds_off[it] = valid ? uint32_t(r * pitch + 16 * k) : kOutOfRange;
+    }
     r += step_r;
     k += step_k;
     if (k >= pieces) { k -= pieces; ++r; }
   }
 #pragma unroll
-  for (int it = 0; it < kMaxLoadIters; ++it) {
+  for (int it = 0; it < ITERS; ++it) {
     if (lds_off[it] != kOutOfRange) {
       uint32_t *d = reinterpret_cast<uint32_t *>(lds + lds_off[it]);
       d[0] = v[it].x;
@@ -251,19 +276,20 @@ __device__ inline void stage_rows(uint8_t *__restrict__ lds, const uint8_t *row_
 
 // Flat staging: the strip is one contiguous range [a, a + len); its 16-byte
 // cover is copied to LDS from offset 0, so byte a sits at LDS (a mod 16).
+template <int NT, int ITERS>
 __device__ inline void stage_flat(uint8_t *__restrict__ lds, const uint8_t *start, int len) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(start) & 15);
   const int n = int((lead + len + 15) >> 4);
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(start - lead, uint32_t(16 * n));
-  uint4 v[kMaxLoadIters];
+  uint4 v[ITERS];
 #pragma unroll
-  for (int it = 0; it < kMaxLoadIters; ++it) {
-    const int k = threadIdx.x + it * kThreads;
-    v[it] = load16(rsrc, k < n ? uint32_t(16 * k) : kOutOfRange);
+  for (int it = 0; it < ITERS; ++it) {
+    const int k = threadIdx.x + it * NT;
+    if (it * NT < n) v[it] = load16(rsrc, k < n ? uint32_t(16 * k) : kOutOfRange);  // uniform test
   }
 #pragma unroll
-  for (int it = 0; it < kMaxLoadIters; ++it) {
-    const int k = threadIdx.x + it * kThreads;
+  for (int it = 0; it < ITERS; ++it) {
+    const int k = threadIdx.x + it * NT;
     if (k < n) *reinterpret_cast<uint4 *>(lds + 16 * k) = v[it];
   }
 }
@@ -274,15 +300,14 @@ __device__ inline void stage_flat(uint8_t *__restrict__ lds, const uint8_t *star
 
 // Writes `tile_cols` tiles (128 rows x 4 columns each) contiguously at dst.
 // Row r, column c of the unit is LDS byte row_off(r) + c with
-// row_off(r) = first + r*row_step + (per_row_shift ? (addr + r*ld) mod 16 : 0).
+// row_off(r) = first + r*row_step (FLAT) or r*row_step + (addr + r*ld) mod 16.
 // Rows >= nrows and columns >= ncols are written as zero.
-template <bool ALIGNED>
+template <int NT, bool FLAT, bool ALIGNED>
 __device__ inline void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__restrict__ dst, int tile_cols,
-                                  int nrows, int ncols, int first, int row_step, bool per_row_shift,
-                                  uintptr_t addr, int64_t ld) {
+                                  int nrows, int ncols, int first, int row_step, uintptr_t addr, int64_t ld) {
   const uint32_t *w32 = reinterpret_cast<const uint32_t *>(lds);
   const int n16 = tile_cols * 32;
-  for (int v = threadIdx.x; v < n16; v += kThreads) {
+  for (int v = threadIdx.x; v < n16; v += NT) {
     const int tc = v >> 5;
     const int i = v & 31;
     const int nvalid = ncols - 4 * tc;
@@ -293,8 +318,11 @@ __device__ inline void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__re
       const int r = i + 32 * q;
       uint32_t x = 0;
       if (r < nrows) {
-        int b = first + r * row_step + 4 * tc;
-        if (per_row_shift) b += int((addr + uintptr_t(int64_t(r) * ld)) & 15);
+        int b = r * row_step + 4 * tc;
+        if (FLAT)
+          b += first;
+        else
+          b += int((addr + uintptr_t(int64_t(r) * ld)) & 15);
         if (ALIGNED) {
           x = w32[b >> 2];
         } else {
@@ -310,34 +338,39 @@ __device__ inline void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__re
 
 // Stages one unit of `nrows` rows x `ncols` source columns starting at
 // row_base (row stride ld) and writes its tile_cols tiles at dst.
+template <int MODE>
 __device__ inline void copy_unit(uint8_t *__restrict__ lds, const Params &p, const uint8_t *row_base,
-                                 int nrows, int ncols, int tile_cols, uint8_t *dst, bool flat) {
+                                 int nrows, int ncols, int tile_cols, uint8_t *dst) {
+  constexpr int NT = threads_for(MODE);
+  constexpr int ITERS = load_iters_for(MODE);
+  constexpr bool FLAT = MODE == kModeMFlat;
   const uintptr_t a = reinterpret_cast<uintptr_t>(row_base);
   bool aligned;
-  if (flat) {
-    stage_flat(lds, row_base, nrows * ncols);
+  if (FLAT) {
+    stage_flat<NT, ITERS>(lds, row_base, nrows * ncols);
     aligned = ((a & 3) == 0) && ((ncols & 3) == 0);
   } else {
-    stage_rows(lds, row_base, p.ld, nrows, ncols, p.pitch, p.pieces);
+    stage_rows<NT, ITERS>(lds, row_base, p.ld, nrows, ncols, p.pitch, p.pieces);
     aligned = ((a & 3) == 0) && ((p.ld & 3) == 0);
   }
   __syncthreads();
-  const int first = flat ? int(a & 15) : 0;
-  const int step = flat ? ncols : p.pitch;
+  const int first = FLAT ? int(a & 15) : 0;
+  const int step = FLAT ? ncols : p.pitch;
   if (aligned)
-    emit_tiles<true>(lds, dst, tile_cols, nrows, ncols, first, step, !flat, a, p.ld);
+    emit_tiles<NT, FLAT, true>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
   else
-    emit_tiles<false>(lds, dst, tile_cols, nrows, ncols, first, step, !flat, a, p.ld);
+    emit_tiles<NT, FLAT, false>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 
-template <bool KGROUPS>
-__global__ __launch_bounds__(kThreads) void rearrange_kernel(Params p) {
+template <int MODE>
+__global__ __launch_bounds__(threads_for(MODE)) void rearrange_kernel(Params p) {
+  constexpr int NT = threads_for(MODE);
+  constexpr bool KGROUPS = MODE == kModeKRows;
   extern __shared__ __align__(16) uint8_t lds[];
-  const int lane = threadIdx.x & (kWave - 1);
   bool first_iter = true;
   for (int64_t vb = blockIdx.x; vb < p.vunits; vb += gridDim.x) {
     // consecutive units on one XCD: workgroup b runs on XCD b mod 8
@@ -350,41 +383,48 @@ __global__ __launch_bounds__(kThreads) void rearrange_kernel(Params p) {
     const int slot = int(unit - block * p.per_row);     // column chunk (M) / unit within the row block (K)
 
     if (!KGROUPS) {
-      const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, int(block), lane);
+      const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, p.unit_cols, int(block));
       const int64_t row_block_bytes = int64_t(kTileRows) * p.padded_cols;
       if (h.group < p.groups) {
         const int k = int(block) - h.first_unit;
         const int row0 = h.start + kTileRows * k;
-        const int nrows = min(kTileRows, h.size - kTileRows * k);
+        // the min() with rows - row0 only restates what a correct scan guarantees
+        const int nrows = min(min(kTileRows, h.size - kTileRows * k), p.rows - row0);
         const int c0 = slot * p.unit_cols;
         const int ncols = min(p.unit_cols, p.cols - c0);
         const int tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
         uint8_t *dst = p.out + block * row_block_bytes + int64_t(c0) * kTileRows;
-        copy_unit(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst, p.flat != 0);
+        // the last condition, too, holds for every unit of a correct scan
+        if (nrows > 0 && ncols > 0 && (block + 1) * row_block_bytes <= p.out_bytes)
+          copy_unit<MODE>(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst);
       } else {
-        const int64_t tail_units = (int64_t(p.per_row) * ((p.units / p.per_row) - h.total_units));
-        const int64_t tail_index = (block - h.total_units) * p.per_row + slot;
-        zero_part(p.out, int64_t(h.total_units) * row_block_bytes, p.out_bytes, tail_index, tail_units);
+        const int64_t nblocks = p.units / p.per_row;
+        const int64_t tail_units = int64_t(p.per_row) * (nblocks - h.first_unit);
+        const int64_t tail_index = (block - h.first_unit) * p.per_row + slot;
+        zero_part<NT>(p.out, int64_t(h.first_unit) * row_block_bytes, p.out_bytes, tail_index, tail_units);
       }
     } else {
-      const GroupHit h = find_group<true>(p.offs, p.groups, p.cols, slot, lane);
+      const GroupHit h = find_group<true>(p.offs, p.groups, p.cols, p.unit_cols, slot);
       const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
       if (h.group < p.groups) {
         const int chunk = slot - h.first_unit;
         const int padded_width = (h.size + 3) & ~3;
-        const int c0 = h.start + chunk * kUnitCols;
+        const int c0 = h.start + chunk * p.unit_cols;
         const int nrows = min(kTileRows, p.rows - kTileRows * int(block));
-        const int ncols = min(kUnitCols, h.size - chunk * kUnitCols);
-        const int tile_cols = min(kUnitCols, padded_width - chunk * kUnitCols) >> 2;
+        // the min() with cols - c0 only restates what a correct scan guarantees
+        const int ncols = min(min(p.unit_cols, h.size - chunk * p.unit_cols), p.cols - c0);
+        const int tile_cols = min(p.unit_cols, padded_width - chunk * p.unit_cols) >> 2;
         uint8_t *dst = p.out + padded_rows * h.padded_start + block * kTileRows * padded_width +
-                       int64_t(chunk) * kUnitCols * kTileRows;
-        copy_unit(lds, p, p.src + block * kTileRows * p.ld + c0, nrows, ncols, tile_cols, dst, false);
+                       int64_t(chunk) * p.unit_cols * kTileRows;
+        // the last condition, too, holds for every unit of a correct scan
+        if (nrows > 0 && ncols > 0 && padded_rows * (h.padded_start + padded_width) <= p.out_bytes)
+          copy_unit<MODE>(lds, p, p.src + block * kTileRows * p.ld + c0, nrows, ncols, tile_cols, dst);
       } else {
         // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
         // 128 * (cols + 4G - padded total) slice per 128-row block
-        const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - h.total_padded;
-        const int64_t lo = padded_rows * h.total_padded + block * kTileRows * tail_cols;
-        zero_part(p.out, lo, lo + kTileRows * tail_cols, slot - h.total_units, p.per_row - h.total_units);
+        const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - h.padded_start;
+        const int64_t lo = padded_rows * h.padded_start + block * kTileRows * tail_cols;
+        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, slot - h.first_unit, p.per_row - h.first_unit);
       }
     }
   }
@@ -421,36 +461,47 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   p.cols = int(cols);
   p.groups = groups;
   p.padded_cols = int(round_up(cols, 4));
-  const int64_t seg = std::min<int64_t>(cols, kUnitCols);   // widest row segment of a unit
-  p.pieces = int((seg + 30) / 16);
-  if (p.pieces < 1) p.pieces = 1;
-  p.pitch = 16 * p.pieces + 4;
+  int mode;
   int64_t units;
   if (!kgroups) {
-    p.unit_cols = kUnitCols;
-    p.per_row = int((p.padded_cols + kUnitCols - 1) / kUnitCols);
     // row blocks: every group's data plus at least one block of tail
-    units = ((rows + kTileRows - 1) / kTileRows + groups) * p.per_row;
-    // one contiguous range per strip when rows are packed, narrow and not 16-byte multiples
-    p.flat = (ld == cols && p.per_row == 1 && (cols % 16) != 0) ? 1 : 0;
+    const int64_t blocks = (rows + kTileRows - 1) / kTileRows + groups;
+    if (ld == cols && cols <= kFlatMaxCols && (cols % 16) != 0) {
+      // packed narrow rows that are not whole 16-byte pieces: one flat range per strip
+      mode = kModeMFlat;
+      p.unit_cols = p.padded_cols;
+    } else {
+      // split row blocks into column chunks while there are too few units to fill the chip
+      mode = kModeMRows;
+      int uc = kMaxUnitCols;
+      while (uc > kMinUnitCols && blocks * ((p.padded_cols + uc - 1) / uc) < kTargetUnits) uc >>= 1;
+      p.unit_cols = uc;
+    }
+    p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
+    units = blocks * p.per_row;
   } else {
-    p.unit_cols = kUnitCols;
+    mode = kModeKRows;
+    p.unit_cols = kMaxUnitCols;
     // units per 128-row block: every group's chunks plus at least one of tail
-    p.per_row = int((cols + 4 * int64_t(groups) + kUnitCols - 1) / kUnitCols + groups);
+    p.per_row = int((cols + 4 * int64_t(groups) + p.unit_cols - 1) / p.unit_cols + groups);
     units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
-    p.flat = 0;
   }
+  const int64_t seg = std::min<int64_t>(cols, p.unit_cols);   // widest row segment of a unit
+  p.pieces = std::max<int>(1, int((seg + 30) / 16));
+  p.pitch = 16 * p.pieces + 4;
   p.units = units;
   p.vunits = round_up(units, 8);
   const int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);
-  size_t lds_bytes = p.flat ? size_t(kTileRows) * size_t(cols) + 32 + kLdsSlack
-                            : size_t(kTileRows) * size_t(p.pitch) + kLdsSlack;
+  size_t lds_bytes = mode == kModeMFlat ? size_t(kTileRows) * size_t(cols) + 32 + kLdsSlack
+                                        : size_t(kTileRows) * size_t(p.pitch) + kLdsSlack;
   lds_bytes = (lds_bytes + 15) & ~size_t(15);
 
   void *args[] = {&p};
-  const void *fn = kgroups ? reinterpret_cast<const void *>(&rearrange_kernel<true>)
-                           : reinterpret_cast<const void *>(&rearrange_kernel<false>);
-  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kThreads), args, lds_bytes, stream);
+  const void *fn = mode == kModeMFlat   ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMFlat>)
+                   : mode == kModeMRows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRows>)
+                                        : reinterpret_cast<const void *>(&rearrange_kernel<kModeKRows>);
+  const int threads = mode == kModeMFlat ? threads_for(kModeMFlat) : threads_for(kModeMRows);
+  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(threads), args, lds_bytes, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 
@@ -484,7 +535,7 @@ const char *mx_rearrange_strerror(int status) {
   switch (status) {
     case MX_REARRANGE_OK: return "success";
     case MX_REARRANGE_ENULL: return "a required pointer is NULL";
-    case MX_REARRANGE_ESHAPE: return "invalid shape: rows/cols negative or too large, or row_stride < cols";
+    case MX_REARRANGE_ESHAPE: return "invalid shape: rows/cols negative or too large, or row_stride outside [cols, 2^24]";
     case MX_REARRANGE_EGROUPS: return "num_groups must be >= 1";
     case MX_REARRANGE_EALIGN: return "out must be 16-byte aligned";
     case MX_REARRANGE_ELAUNCH: return "HIP kernel launch failed";

@@ -114,6 +114,29 @@ def capture(job, first, count):
     return g
 
 
+def copy_calibration(args):
+    """K plain device-to-device copies of the workload's input size (reads N, writes N bytes each)."""
+    import torch
+
+    import workloads
+
+    w = workloads.make(args.workload)
+    n = w.rows * w.cols
+    copies = max(2, min(4096, math.ceil((args.rotate_mib << 20) / (2 * n))))
+    src = torch.randint(0, 255, (copies, n), dtype=torch.uint8, device="cuda")
+    dst = torch.empty((copies, n), dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        dst[i % copies].copy_(src[i % copies])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dst[i % copies].copy_(src[i % copies])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(json.dumps({"copy_calibration": True, "bytes_read": n, "bytes_written": n, "steps": args.steps,
+                      "us_per_copy": round(wall / args.steps * 1e6, 3)}), flush=True)
+
+
 def cpu_baseline(name, seconds):
     """The CPU oracle, as it is, on the same workload, repeated for about `seconds` of CPU time."""
     import oracle
@@ -162,6 +185,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time torch's plain device copy of the workload's input size instead "
+                         "(reference kernel of known traffic for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -178,6 +204,9 @@ def main():
     import group_scale_factor_amd  # noqa: F401  (fails loudly if the HIP library is missing)
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     job = Job(args.workload, rotate_bytes=args.rotate_mib << 20)
     K, W = args.steps, args.warmup
 

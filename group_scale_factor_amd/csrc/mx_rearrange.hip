@@ -52,10 +52,11 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kTileRows = 128;
-// Widest column chunk of a unit: 240 columns are covered by at most 16 aligned
-// 16-byte pieces per row at any alignment, so a 128-row unit is 2048 pieces,
-// exactly 8 per producer lane.
-constexpr int kMaxUnitCols = 240;
+// Widest column chunk of a unit: 112 columns are covered by at most 8 aligned
+// 16-byte pieces per row at any alignment, so a 128-row unit is at most 1024
+// pieces, 4 per lane of a 256-thread workgroup. Narrow units keep registers and
+// LDS small (7 workgroups per CU), which measured faster than wider ones.
+constexpr int kMaxUnitCols = 112;
 constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits M row blocks into
 constexpr int kTargetUnits = 1024;            // M: split row blocks into chunks until this many units
 constexpr int kFlatMaxCols = 60;              // M: widest packed row staged as one flat range
@@ -68,46 +69,40 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // keeps a unit's byte spa
 constexpr uint32_t kOutOfRange = 0xfffffff0u;          // buffer offset past any range: the load returns 0
 constexpr int kRawBufferFlags = 0x00020000;            // buffer descriptor word 3: 32-bit raw data
 // Cache policy of the staging loads (buffer instruction bit 1: non-temporal).
-// Flat strips share at most one line with their neighbour, so they stream;
-// row segments of neighbouring units share lines, which must stay in L2.
+// M strips share at most one line with their neighbour, so they stream; the
+// row segments of neighbouring K units share lines, which stay in L2.
 constexpr int kFlatLoadPolicy = 2;
-constexpr int kRowsLoadPolicy = 0;
+constexpr int kMRowsLoadPolicy = 2;
+constexpr int kKRowsLoadPolicy = 0;
 
 // Staging modes; each is its own kernel instantiation.
 enum Mode : int {
-  kModeMFlat = 0,   // M groups, packed rows of <= 64 bytes, one contiguous range per 128-row strip
+  kModeMFlat = 0,   // M groups, packed rows of <= 60 bytes, one contiguous range per 128-row strip
   kModeMRows = 1,   // M groups, one row segment at a time
+  kModeMRowsNarrow = 3,  // M groups, one row segment of at most kNarrowUnitCols at a time
   kModeKRows = 2,   // K groups, one row segment at a time
 };
 
-// Each workgroup is split into producer waves, which only load (global ->
-// registers -> LDS), and consumer waves, which only store (LDS -> global).
-// On gfx9 one counter tracks both loads and stores of a wave, so a wave that
-// did both would wait for its own stores to be acknowledged whenever it waited
-// for a load; split roles keep the stores fire-and-forget.
-constexpr int producers_for(int mode) { return mode == kModeMFlat ? 64 : 256; }
-constexpr int consumers_for(int mode) { return mode == kModeMFlat ? 128 : 256; }
-constexpr int threads_for(int mode) { return producers_for(mode) + consumers_for(mode); }
+// Narrow M units (small problems split into many column chunks) get their own
+// instantiation sized for them: fewer loads per lane, fewer registers.
+constexpr int kNarrowUnitCols = 48;
+constexpr int threads_for(int mode) { return mode == kModeMFlat ? 128 : 256; }
+constexpr int max_pieces_for(int mode) {
+  return ((mode == kModeMRowsNarrow ? kNarrowUnitCols : kMaxUnitCols) + 30) / 16;
+}
 constexpr int load_iters_for(int mode) {
-  return ((mode == kModeMFlat ? kMaxFlatPieces : kTileRows * kMaxPieces) + producers_for(mode) - 1) /
-         producers_for(mode);
+  return ((mode == kModeMFlat ? kMaxFlatPieces : kTileRows * max_pieces_for(mode)) + threads_for(mode) - 1) /
+         threads_for(mode);
 }
-constexpr int store_iters_for(int mode) {
-  return (kTileRows * (mode == kModeMFlat ? kFlatMaxCols : kMaxUnitCols) / 16 + consumers_for(mode) - 1) /
-         consumers_for(mode);
-}
-// Persistent launch: as many workgroups as fit at once, each looping over its
-// units with two LDS buffers (loads of the next unit overlap the stores of
-// the current one). Otherwise one workgroup per unit.
-constexpr bool kPersistent = true;
-// Register budget: at least 4 waves per SIMD (<= 128 VGPRs), so that two
-// 8-wave workgroups share a CU, as their LDS buffers allow.
-constexpr int kMinWavesPerEu = 4;
+
+// Register budget hint (waves per SIMD); 1 leaves it to the compiler, which
+// needs about 72 VGPRs, i.e. 7 waves per SIMD.
+constexpr int kMinWavesPerEu = 1;
 
 static_assert(kMaxUnitCols % 4 == 0 && kMinUnitCols % 4 == 0, "units are whole tile columns");
-static_assert(kTileRows * kMaxPitch + kLdsSlack <= 32 * 1024 + 4096, "LDS per buffer");
-static_assert(producers_for(kModeMFlat) % kWave == 0 && producers_for(kModeKRows) % kWave == 0,
-              "roles are whole waves");
+static_assert(kTileRows * kMaxPitch + kLdsSlack <= 64 * 1024, "LDS per workgroup");
+static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8, "staging unrolled to 8");
+static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narrow units");
 
 struct Params {
   const uint8_t *src;
@@ -125,7 +120,7 @@ struct Params {
   int per_row;         // M: units per output row block; K: units per 128-row block
   int pitch;           // LDS row pitch (bytes) in per-row staging
   int pieces;          // 16-byte pieces per LDS row in per-row staging
-  int lds_stride;      // bytes per LDS buffer
+  int trash;           // LDS offset of 16 bytes that staging pieces without data are written to
 };
 
 // ---------------------------------------------------------------------------
@@ -185,8 +180,8 @@ struct GroupHit {
 // into [previous end, limit], which leaves valid offsets unchanged and keeps
 // every access in bounds for invalid ones. Every lane of the wave must call it.
 template <bool KGROUPS>
-__device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int limit, int unit_cols,
-                               int target) {
+__device__ __forceinline__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int limit,
+                                               int unit_cols, int target) {
   const int lane = threadIdx.x & (kWave - 1);
   int carry_end = 0, carry_units = 0, carry_padded = 0;
   for (int base = 0; base < groups; base += kWave) {
@@ -226,104 +221,33 @@ __device__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int
 }
 
 // ---------------------------------------------------------------------------
-// work units
+// stores
 // ---------------------------------------------------------------------------
 
-enum UnitKind : int { kNone = 0, kData = 1, kTail = 2 };
+// 16-byte store, streamed past the caches: the output is never read back here.
+__device__ __forceinline__ void store16(uint8_t *dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = {a, b, c, d};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst));
+}
 
-struct Unit {
-  int kind;
-  // data: nrows x ncols source bytes from row_base (row stride ld) -> tile_cols tiles at dst
-  const uint8_t *row_base;
-  uint8_t *dst;
-  int nrows, ncols, tile_cols;
-  // tail: part `part` of `parts` of the zero range [lo, hi)
-  int64_t lo, hi, part, parts;
-};
-
-// What consumers need of a unit, written into the head of its LDS buffer by
-// the producers (consumers then issue no global load at all).
-struct UnitDesc {
-  int kind, nrows, ncols, tile_cols;
-  uint32_t src_lo;  // low 32 bits of the unit's source address (row alignment)
-  uint32_t unused;
-  uint64_t dst;
-  int64_t lo, hi, part, parts;
-};
-constexpr int kHeaderBytes = 64;  // LDS bytes before a buffer's data
-static_assert(sizeof(UnitDesc) <= kHeaderBytes && kHeaderBytes % 16 == 0, "descriptor header");
-
-// Maps virtual block vb to its unit and resolves it against the groups. Every
-// lane of the wave must call it (it runs wave-wide scans).
-template <bool KGROUPS>
-__device__ Unit resolve(const Params &p, int64_t vb) {
-  Unit u;
-  u.kind = kNone;
-  u.row_base = p.src;
-  u.dst = p.out;
-  u.nrows = u.ncols = u.tile_cols = 0;
-  u.lo = u.hi = u.part = 0;
-  u.parts = 1;
-  if (vb >= p.vunits) return u;
-  // consecutive units on one XCD: workgroup b runs on XCD b mod 8, and vb = b (mod 8)
-  const int64_t unit = (vb & 7) * (p.vunits >> 3) + (vb >> 3);
-  if (unit >= p.units) return u;
-  const int64_t block = unit / p.per_row;           // output row block (M) / 128-row block (K)
-  const int slot = int(unit - block * p.per_row);   // column chunk (M) / unit within the row block (K)
-  if (!KGROUPS) {
-    const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, p.unit_cols, int(block));
-    const int64_t row_block_bytes = int64_t(kTileRows) * p.padded_cols;
-    if (h.group < p.groups) {
-      const int k = int(block) - h.first_unit;
-      const int row0 = h.start + kTileRows * k;
-      const int c0 = slot * p.unit_cols;
-      // the min() with rows - row0 and the output bound restate what a correct scan guarantees
-      u.nrows = min(min(kTileRows, h.size - kTileRows * k), p.rows - row0);
-      u.ncols = min(p.unit_cols, p.cols - c0);
-      u.tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
-      u.row_base = p.src + int64_t(row0) * p.ld + c0;
-      u.dst = p.out + block * row_block_bytes + int64_t(c0) * kTileRows;
-      if (u.nrows > 0 && u.ncols > 0 && (block + 1) * row_block_bytes <= p.out_bytes) u.kind = kData;
-    } else {
-      const int64_t nblocks = p.units / p.per_row;
-      u.kind = kTail;
-      u.lo = int64_t(h.first_unit) * row_block_bytes;
-      u.hi = p.out_bytes;
-      u.part = (block - h.first_unit) * p.per_row + slot;
-      u.parts = int64_t(p.per_row) * (nblocks - h.first_unit);
-    }
-  } else {
-    const GroupHit h = find_group<true>(p.offs, p.groups, p.cols, p.unit_cols, slot);
-    const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
-    if (h.group < p.groups) {
-      const int chunk = slot - h.first_unit;
-      const int padded_width = (h.size + 3) & ~3;
-      const int c0 = h.start + chunk * p.unit_cols;
-      u.nrows = min(kTileRows, p.rows - kTileRows * int(block));
-      // the min() with cols - c0 and the output bound restate what a correct scan guarantees
-      u.ncols = min(min(p.unit_cols, h.size - chunk * p.unit_cols), p.cols - c0);
-      u.tile_cols = min(p.unit_cols, padded_width - chunk * p.unit_cols) >> 2;
-      u.row_base = p.src + block * kTileRows * p.ld + c0;
-      u.dst = p.out + padded_rows * h.padded_start + block * kTileRows * padded_width +
-              int64_t(chunk) * p.unit_cols * kTileRows;
-      if (u.nrows > 0 && u.ncols > 0 && padded_rows * (h.padded_start + padded_width) <= p.out_bytes)
-        u.kind = kData;
-    } else {
-      // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
-      // 128 * (cols + 4G - padded total) slice per 128-row block
-      const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - h.padded_start;
-      u.kind = kTail;
-      u.lo = padded_rows * h.padded_start + block * kTileRows * tail_cols;
-      u.hi = u.lo + kTileRows * tail_cols;
-      u.part = slot - h.first_unit;
-      u.parts = p.per_row - h.first_unit;
-    }
-  }
-  return u;
+// Zero-fill of part `part` of `parts` of the byte range [lo, hi); lo is
+// 16-byte aligned and hi a multiple of 4.
+template <int NT>
+__device__ __forceinline__ void zero_part(uint8_t *__restrict__ out, int64_t lo, int64_t hi, int64_t part,
+                                          int64_t parts) {
+  if (lo >= hi || parts <= 0) return;
+  const int64_t len16 = (hi - lo + 15) >> 4;
+  const int64_t per = (len16 + parts - 1) / parts;
+  const int64_t b = lo + 16 * min(per * part, len16);
+  const int64_t e = min(lo + 16 * min(per * (part + 1), len16), hi);
+  const int64_t full = b + ((e - b) & ~int64_t(15));
+  for (int64_t q = b + 16 * threadIdx.x; q < full; q += 16 * NT) store16(out + q, 0, 0, 0, 0);
+  for (int64_t q = full + 4 * threadIdx.x; q < e; q += 4 * NT) *reinterpret_cast<uint32_t *>(out + q) = 0u;
 }
 
 // ---------------------------------------------------------------------------
-// producers: global -> registers -> LDS
+// staging a 128-row strip in LDS
 // ---------------------------------------------------------------------------
 
 // Buffer resource over [base, base + bytes) for raw (unswizzled) buffer loads.
@@ -349,263 +273,249 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t of
 // Per-row staging: row r's segment [a, a + seg) with a = row_base + r*ld is
 // fetched as the 16-byte pieces covering it into LDS row r (pitch bytes); its
 // first byte then sits at r*pitch + (a mod 16). Piece slot s = r*pieces + k
-// goes to producer lane s mod NP; each lane issues exactly N loads back to back
-// (N = slots per lane of this unit) before it waits for any of them.
-template <int NP, int N, int POLICY>
-__device__ __forceinline__ void stage_rows_n(uint8_t *__restrict__ buf, int t, __amdgpu_buffer_rsrc_t rsrc, uint32_t lead,
-                                    int64_t ld, int nrows, int seg, int pitch, int pieces) {
-  const int step_r = NP / pieces, step_k = NP % pieces;
-  int r = t / pieces, k = t % pieces;
+// goes to lane s mod NT; each lane issues exactly N loads back to back (N =
+// slots per lane of this unit) before it waits for any of them.
+template <int NT, int N, int POLICY>
+__device__ __forceinline__ void stage_rows_n(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
+                                             uint32_t lead, int64_t ld, int nrows, int seg, int pitch, int pieces) {
+  const int step_r = NT / pieces, step_k = NT % pieces;
+  const int r0 = threadIdx.x / pieces, k0 = threadIdx.x % pieces;
   uint4 v[N];
-  uint32_t off[N];
+  int r = r0, k = k0;
 #pragma unroll
   for (int it = 0; it < N; ++it) {
     const uint32_t row_off = lead + uint32_t(r) * uint32_t(ld);  // in range whenever r < nrows
     const int need = int(((row_off & 15) + seg + 15) >> 4);
     const bool valid = r < nrows && k < need;
     v[it] = load16<POLICY>(rsrc, valid ? (row_off & ~15u) + 16 * k : kOutOfRange);
-    off[it] = valid ? uint32_t(r * pitch + 16 * k) : kOutOfRange;
     r += step_r;
     k += step_k;
     if (k >= pieces) { k -= pieces; ++r; }
   }
+  // The same walk again (cheaper than keeping N offsets live across the
+  // loads). Every piece is written, slots without data to the trash bytes at
+  // the end of LDS: a write under a condition would let the compiler move its
+  // load under that condition too, one load after another.
+  r = r0;
+  k = k0;
 #pragma unroll
   for (int it = 0; it < N; ++it) {
-    if (off[it] != kOutOfRange) {
-      uint32_t *d = reinterpret_cast<uint32_t *>(buf + off[it]);  // 4-byte aligned rows
-      d[0] = v[it].x;
-      d[1] = v[it].y;
-      d[2] = v[it].z;
-      d[3] = v[it].w;
-    }
+    const uint32_t row_off = lead + uint32_t(r) * uint32_t(ld);
+    const int need = int(((row_off & 15) + seg + 15) >> 4);
+    const int off = (r < nrows && k < need) ? r * pitch + 16 * k : trash;
+    uint32_t *d = reinterpret_cast<uint32_t *>(lds + off);  // 4-byte aligned rows
+    d[0] = v[it].x;
+    d[1] = v[it].y;
+    d[2] = v[it].z;
+    d[3] = v[it].w;
+    r += step_r;
+    k += step_k;
+    if (k >= pieces) { k -= pieces; ++r; }
   }
 }
 
-template <int NP, int ITERS, int POLICY>
-__device__ __forceinline__ void stage_rows(uint8_t *__restrict__ buf, int t, const uint8_t *row_base, int64_t ld, int nrows,
-                                  int seg, int pitch, int pieces) {
-  static_assert(ITERS <= 8, "staging is unrolled for at most 8 pieces per lane");
+// Runs stage_rows_n with the smallest N >= n (n uniform, 1 <= n <= N).
+template <int NT, int N, int POLICY>
+__device__ __forceinline__ void stage_rows_upto(int n, uint8_t *__restrict__ lds, int trash,
+                                                __amdgpu_buffer_rsrc_t rsrc, uint32_t lead, int64_t ld, int nrows,
+                                                int seg, int pitch, int pieces) {
+  if constexpr (N > 1) {
+    if (n < N) {
+      stage_rows_upto<NT, N - 1, POLICY>(n, lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces);
+      return;
+    }
+  }
+  stage_rows_n<NT, N, POLICY>(lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces);
+}
+
+template <int NT, int ITERS, int POLICY>
+__device__ __forceinline__ void stage_rows(uint8_t *__restrict__ lds, int trash, const uint8_t *row_base, int64_t ld,
+                                           int nrows, int seg, int pitch, int pieces) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(row_base) & 15);
   const uint8_t *base = row_base - lead;  // 16-byte aligned
   const uint32_t span = uint32_t((lead + int64_t(nrows - 1) * ld + seg + 15) & ~int64_t(15));
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(base, span);
-  const int n = (nrows * pieces + NP - 1) / NP;  // uniform
-  switch (n) {
-    case 1: stage_rows_n<NP, 1, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 2: stage_rows_n<NP, 2, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 3: stage_rows_n<NP, 3, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 4: stage_rows_n<NP, 4, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 5: stage_rows_n<NP, 5, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 6: stage_rows_n<NP, 6, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    case 7: stage_rows_n<NP, 7, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-    default: stage_rows_n<NP, ITERS, POLICY>(buf, t, rsrc, lead, ld, nrows, seg, pitch, pieces); break;
-  }
+  stage_rows_upto<NT, ITERS, POLICY>((nrows * pieces + NT - 1) / NT, lds, trash, rsrc, lead, ld, nrows, seg, pitch,
+                                     pieces);
 }
 
 // Flat staging: the strip is one contiguous range [a, a + len); its 16-byte
 // cover goes to LDS from offset 0, so byte a sits at LDS (a mod 16).
-template <int NP, int N, int POLICY>
-__device__ __forceinline__ void stage_flat_n(uint8_t *__restrict__ buf, int t, __amdgpu_buffer_rsrc_t rsrc, int n) {
+template <int NT, int N, int POLICY>
+__device__ __forceinline__ void stage_flat_n(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
+                                             int n) {
+  const int t = threadIdx.x;
   uint4 v[N];
 #pragma unroll
-  for (int it = 0; it < N; ++it) v[it] = load16<POLICY>(rsrc, t + it * NP < n ? uint32_t(16 * (t + it * NP)) : kOutOfRange);
+  for (int it = 0; it < N; ++it) v[it] = load16<POLICY>(rsrc, t + it * NT < n ? uint32_t(16 * (t + it * NT)) : kOutOfRange);
+  // every piece is written (past the strip: to the trash bytes), see stage_rows_n
 #pragma unroll
   for (int it = 0; it < N; ++it)
-    if (t + it * NP < n) *reinterpret_cast<uint4 *>(buf + 16 * (t + it * NP)) = v[it];
+    *reinterpret_cast<uint4 *>(lds + (t + it * NT < n ? 16 * (t + it * NT) : trash)) = v[it];
 }
 
-template <int NP, int ITERS, int POLICY>
-__device__ __forceinline__ void stage_flat(uint8_t *__restrict__ buf, int t, const uint8_t *start, int len) {
-  static_assert(ITERS <= 8, "staging is unrolled for at most 8 pieces per lane");
+// Runs stage_flat_n with the smallest N >= m (m uniform, 1 <= m <= N).
+template <int NT, int N, int POLICY>
+__device__ __forceinline__ void stage_flat_upto(int m, uint8_t *__restrict__ lds, int trash,
+                                                __amdgpu_buffer_rsrc_t rsrc, int n) {
+  if constexpr (N > 1) {
+    if (m < N) {
+      stage_flat_upto<NT, N - 1, POLICY>(m, lds, trash, rsrc, n);
+      return;
+    }
+  }
+  stage_flat_n<NT, N, POLICY>(lds, trash, rsrc, n);
+}
+
+template <int NT, int ITERS, int POLICY>
+__device__ __forceinline__ void stage_flat(uint8_t *__restrict__ lds, int trash, const uint8_t *start, int len) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(start) & 15);
   const int n = int((lead + len + 15) >> 4);
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(start - lead, uint32_t(16 * n));
-  switch ((n + NP - 1) / NP) {  // uniform
-    case 1: stage_flat_n<NP, 1, POLICY>(buf, t, rsrc, n); break;
-    case 2: stage_flat_n<NP, 2, POLICY>(buf, t, rsrc, n); break;
-    case 3: stage_flat_n<NP, 3, POLICY>(buf, t, rsrc, n); break;
-    case 4: stage_flat_n<NP, 4, POLICY>(buf, t, rsrc, n); break;
-    case 5: stage_flat_n<NP, 5, POLICY>(buf, t, rsrc, n); break;
-    case 6: stage_flat_n<NP, 6, POLICY>(buf, t, rsrc, n); break;
-    case 7: stage_flat_n<NP, 7, POLICY>(buf, t, rsrc, n); break;
-    default: stage_flat_n<NP, ITERS, POLICY>(buf, t, rsrc, n); break;
-  }
-}
-
-// Resolves unit vb, publishes its descriptor and stages its bytes in buf.
-template <int MODE>
-__device__ __forceinline__ void produce(uint8_t *__restrict__ buf, const Params &p, int64_t vb) {
-  constexpr int NP = producers_for(MODE);
-  constexpr int ITERS = load_iters_for(MODE);
-  const Unit u = resolve<MODE == kModeKRows>(p, vb);
-  const int t = threadIdx.x;
-  if (t == 0) {
-    UnitDesc d;
-    d.kind = u.kind;
-    d.nrows = u.nrows;
-    d.ncols = u.ncols;
-    d.tile_cols = u.tile_cols;
-    d.src_lo = uint32_t(reinterpret_cast<uintptr_t>(u.row_base));
-    d.unused = 0;
-    d.dst = reinterpret_cast<uint64_t>(u.dst);
-    d.lo = u.lo;
-    d.hi = u.hi;
-    d.part = u.part;
-    d.parts = u.parts;
-    *reinterpret_cast<UnitDesc *>(buf) = d;
-  }
-  if (u.kind != kData) return;
-  uint8_t *data = buf + kHeaderBytes;
-  if (MODE == kModeMFlat)
-    stage_flat<NP, ITERS, kFlatLoadPolicy>(data, t, u.row_base, u.nrows * u.ncols);
-  else
-    stage_rows<NP, ITERS, kRowsLoadPolicy>(data, t, u.row_base, p.ld, u.nrows, u.ncols, p.pitch, p.pieces);
+  stage_flat_upto<NT, ITERS, POLICY>((n + NT - 1) / NT, lds, trash, rsrc, n);
 }
 
 // ---------------------------------------------------------------------------
-// consumers: LDS -> global
+// emitting tiles from LDS
 // ---------------------------------------------------------------------------
-
-// 16-byte store, streamed past the caches: the output is never read back here.
-__device__ __forceinline__ void store16(uint8_t *dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 t = {a, b, c, d};
-  __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst));
-}
-
-// Zero-fill of part `part` of `parts` of the byte range [lo, hi); lo is
-// 16-byte aligned and hi a multiple of 4. t: consumer thread index.
-template <int NC>
-__device__ __forceinline__ void zero_part(uint8_t *__restrict__ out, int t, int64_t lo, int64_t hi, int64_t part,
-                                 int64_t parts) {
-  if (lo >= hi || parts <= 0) return;
-  const int64_t len16 = (hi - lo + 15) >> 4;
-  const int64_t per = (len16 + parts - 1) / parts;
-  const int64_t b = lo + 16 * min(per * part, len16);
-  const int64_t e = min(lo + 16 * min(per * (part + 1), len16), hi);
-  const int64_t full = b + ((e - b) & ~int64_t(15));
-  for (int64_t q = b + 16 * t; q < full; q += 16 * NC) store16(out + q, 0, 0, 0, 0);
-  for (int64_t q = full + 4 * t; q < e; q += 4 * NC) *reinterpret_cast<uint32_t *>(out + q) = 0u;
-}
 
 // Writes `tile_cols` tiles (128 rows x 4 columns each) contiguously at dst.
 // Row r, column c of the unit is LDS byte row_off(r) + c with
 // row_off(r) = first + r*row_step (FLAT) or r*row_step + (addr + r*ld) mod 16.
-// Rows >= nrows and columns >= ncols are written as zero. Consumer thread t
-// writes 16-byte units t, t + NC, ...
-template <int NC, int ITERS, bool FLAT, bool ALIGNED>
-__device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ buf, int t, uint8_t *__restrict__ dst,
-                                  int tile_cols, int nrows, int ncols, int first, int row_step, uintptr_t addr,
-                                  int64_t ld) {
-  const uint32_t *w32 = reinterpret_cast<const uint32_t *>(buf);
+// Rows >= nrows and columns >= ncols are written as zero.
+template <int NT, bool FLAT, bool ALIGNED>
+__device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__restrict__ dst,
+                                           int tile_cols, int nrows, int ncols, int first, int row_step,
+                                           uintptr_t addr, int64_t ld) {
+  const uint32_t *w32 = reinterpret_cast<const uint32_t *>(lds);
   const int n16 = tile_cols * 32;
-#pragma unroll 2
-  for (int it = 0; it < ITERS; ++it) {
-    const int v = t + it * NC;
-    if (it * NC < n16 && v < n16) {
-      const int tc = v >> 5;
-      const int i = v & 31;
-      const int nvalid = ncols - 4 * tc;
-      const uint32_t mask = nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : (1u << (8 * nvalid)) - 1u);
-      uint32_t w[4];
+  for (int v = threadIdx.x; v < n16; v += NT) {
+    const int tc = v >> 5;
+    const int i = v & 31;
+    const int nvalid = ncols - 4 * tc;
+    const uint32_t mask = nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : (1u << (8 * nvalid)) - 1u);
+    uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = i + 32 * q;
-        uint32_t x = 0;
-        if (r < nrows) {
-          int b = r * row_step + 4 * tc;
-          if (FLAT)
-            b += first;
-          else
-            b += int((addr + uintptr_t(int64_t(r) * ld)) & 15);
-          if (ALIGNED) {
-            x = w32[b >> 2];
-          } else {
-            x = __builtin_amdgcn_alignbyte(w32[(b >> 2) + 1], w32[b >> 2], b & 3);
-          }
-          x &= mask;
+    for (int q = 0; q < 4; ++q) {
+      const int r = i + 32 * q;
+      uint32_t x = 0;
+      if (r < nrows) {
+        int b = r * row_step + 4 * tc;
+        if (FLAT)
+          b += first;
+        else
+          b += int((uint32_t(addr) + uint32_t(r) * uint32_t(ld)) & 15u);  // (addr + r*ld) mod 16
+        if (ALIGNED) {
+          x = w32[b >> 2];
+        } else {
+          x = __builtin_amdgcn_alignbyte(w32[(b >> 2) + 1], w32[b >> 2], b & 3);
         }
-        w[q] = x;
+        x &= mask;
       }
-      store16(dst + 16 * int64_t(v), w[0], w[1], w[2], w[3]);
+      w[q] = x;
     }
+    store16(dst + 16 * int64_t(v), w[0], w[1], w[2], w[3]);
   }
 }
 
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(x)))));
-  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(x) >> 32))));
-  return int64_t((hi << 32) | lo);
-}
-
-// Writes out the unit whose descriptor heads buf.
+// Stages one unit of `nrows` rows x `ncols` source columns starting at
+// row_base (row stride ld) and writes its tile_cols tiles at dst.
 template <int MODE>
-__device__ __forceinline__ void consume(const uint8_t *__restrict__ buf, const Params &p) {
-  constexpr int NC = consumers_for(MODE);
-  constexpr int ITERS = store_iters_for(MODE);
+__device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Params &p, const uint8_t *row_base,
+                                          int nrows, int ncols, int tile_cols, uint8_t *dst) {
+  constexpr int NT = threads_for(MODE);
   constexpr bool FLAT = MODE == kModeMFlat;
-  const int t = threadIdx.x - producers_for(MODE);
-  const UnitDesc &d = *reinterpret_cast<const UnitDesc *>(buf);
-  const int kind = uniform(d.kind);
-  if (kind == kTail) {
-    zero_part<NC>(p.out, t, uniform64(d.lo), uniform64(d.hi), uniform64(d.part), uniform64(d.parts));
-    return;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row_base);
+  bool aligned;
+  if (FLAT) {
+    stage_flat<NT, load_iters_for(MODE), kFlatLoadPolicy>(lds, p.trash, row_base, nrows * ncols);
+    aligned = ((a & 3) == 0) && ((ncols & 3) == 0);
+  } else {
+    stage_rows<NT, load_iters_for(MODE), MODE == kModeKRows ? kKRowsLoadPolicy : kMRowsLoadPolicy>(
+        lds, p.trash, row_base, p.ld, nrows, ncols, p.pitch, p.pieces);
+    aligned = ((a & 3) == 0) && ((p.ld & 3) == 0);
   }
-  if (kind != kData) return;
-  const int nrows = uniform(d.nrows), ncols = uniform(d.ncols), tile_cols = uniform(d.tile_cols);
-  const uint32_t a = uint32_t(uniform(int(d.src_lo)));
-  uint8_t *dst = reinterpret_cast<uint8_t *>(uniform64(int64_t(d.dst)));
-  const uint8_t *data = buf + kHeaderBytes;
-  const bool aligned = FLAT ? ((a & 3) == 0 && (ncols & 3) == 0) : ((a & 3) == 0 && (p.ld & 3) == 0);
+  __syncthreads();
   const int first = FLAT ? int(a & 15) : 0;
   const int step = FLAT ? ncols : p.pitch;
   if (aligned)
-    emit_tiles<NC, ITERS, FLAT, true>(data, t, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
+    emit_tiles<NT, FLAT, true>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
   else
-    emit_tiles<NC, ITERS, FLAT, false>(data, t, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
+    emit_tiles<NT, FLAT, false>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
 }
 
 // ---------------------------------------------------------------------------
-// the kernel
+// the kernel: one work unit per workgroup (a grid-stride loop only when the
+// grid is capped). A workgroup ends as soon as its stores are issued, so the
+// next one on the CU loads while those stores drain.
 // ---------------------------------------------------------------------------
 
-// Workgroup b handles virtual blocks b, b + grid, b + 2*grid, ... Producers
-// stage unit n+1 into one LDS buffer while consumers write unit n out of the
-// other; one barrier per unit hands the buffers over. Both roles resolve the
-// same units, so they run the same number of iterations and barriers.
 template <int MODE>
 __global__ __launch_bounds__(threads_for(MODE)) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu)))
 void rearrange_kernel(Params p) {
+  constexpr int NT = threads_for(MODE);
+  constexpr bool KGROUPS = MODE == kModeKRows;
   extern __shared__ __align__(16) uint8_t lds[];
-  const bool producer = threadIdx.x < producers_for(MODE);  // whole waves
-  int64_t vb = blockIdx.x;
-  int b = 0;
-  if (producer) produce<MODE>(lds, p, vb);
-  for (;;) {
-    __syncthreads();  // buffer b holds unit vb; nothing reads buffer b ^ 1 any more
-    const int64_t vb_next = vb + gridDim.x;
-    if (producer) {
-      if (vb_next < p.vunits) produce<MODE>(lds + (b ^ 1) * p.lds_stride, p, vb_next);
+  bool first_iter = true;
+  for (int64_t vb = blockIdx.x; vb < p.vunits; vb += gridDim.x) {
+    // consecutive units on one XCD: workgroup b runs on XCD b mod 8
+    const int64_t unit = (vb & 7) * (p.vunits >> 3) + (vb >> 3);
+    if (unit >= p.units) continue;
+    if (!first_iter) __syncthreads();  // LDS of the previous unit is no longer read
+    first_iter = false;
+
+    const int64_t block = unit / p.per_row;             // output row block (M) / 128-row block (K)
+    const int slot = int(unit - block * p.per_row);     // column chunk (M) / unit within the row block (K)
+
+    if (!KGROUPS) {
+      const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, p.unit_cols, int(block));
+      const int64_t row_block_bytes = int64_t(kTileRows) * p.padded_cols;
+      if (h.group < p.groups) {
+        const int k = int(block) - h.first_unit;
+        const int row0 = h.start + kTileRows * k;
+        // the min() with rows - row0 only restates what a correct scan guarantees
+        const int nrows = min(min(kTileRows, h.size - kTileRows * k), p.rows - row0);
+        const int c0 = slot * p.unit_cols;
+        const int ncols = min(p.unit_cols, p.cols - c0);
+        const int tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
+        uint8_t *dst = p.out + block * row_block_bytes + int64_t(c0) * kTileRows;
+        // the last condition, too, holds for every unit of a correct scan
+        if (nrows > 0 && ncols > 0 && (block + 1) * row_block_bytes <= p.out_bytes)
+          copy_unit<MODE>(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst);
+      } else {
+        const int64_t nblocks = p.units / p.per_row;
+        const int64_t tail_units = int64_t(p.per_row) * (nblocks - h.first_unit);
+        const int64_t tail_index = (block - h.first_unit) * p.per_row + slot;
+        zero_part<NT>(p.out, int64_t(h.first_unit) * row_block_bytes, p.out_bytes, tail_index, tail_units);
+      }
     } else {
-      consume<MODE>(lds + b * p.lds_stride, p);
+      const GroupHit h = find_group<true>(p.offs, p.groups, p.cols, p.unit_cols, slot);
+      const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
+      if (h.group < p.groups) {
+        const int chunk = slot - h.first_unit;
+        const int padded_width = (h.size + 3) & ~3;
+        const int c0 = h.start + chunk * p.unit_cols;
+        const int nrows = min(kTileRows, p.rows - kTileRows * int(block));
+        // the min() with cols - c0 only restates what a correct scan guarantees
+        const int ncols = min(min(p.unit_cols, h.size - chunk * p.unit_cols), p.cols - c0);
+        const int tile_cols = min(p.unit_cols, padded_width - chunk * p.unit_cols) >> 2;
+        uint8_t *dst = p.out + padded_rows * h.padded_start + block * kTileRows * padded_width +
+                       int64_t(chunk) * p.unit_cols * kTileRows;
+        // the last condition, too, holds for every unit of a correct scan
+        if (nrows > 0 && ncols > 0 && padded_rows * (h.padded_start + padded_width) <= p.out_bytes)
+          copy_unit<MODE>(lds, p, p.src + block * kTileRows * p.ld + c0, nrows, ncols, tile_cols, dst);
+      } else {
+        // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
+        // 128 * (cols + 4G - padded total) slice per 128-row block
+        const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - h.padded_start;
+        const int64_t lo = padded_rows * h.padded_start + block * kTileRows * tail_cols;
+        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, slot - h.first_unit, p.per_row - h.first_unit);
+      }
     }
-    if (vb_next >= p.vunits) break;
-    vb = vb_next;
-    b ^= 1;
   }
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// Workgroups of `fn` that fit on the current device at once (0 if unknown).
-int64_t resident_workgroups(const void *fn, int threads, size_t lds_bytes) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds_bytes) != hipSuccess) return 0;
-  return int64_t(cus) * per_cu;
-}
 
 bool sizes_ok(int64_t rows, int64_t cols, int64_t ld, int32_t groups) {
   if (rows < 0 || cols < 0 || ld < cols || ld > kMaxRowStride) return false;
@@ -647,11 +557,11 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
       p.unit_cols = p.padded_cols;
     } else {
       // split row blocks into column chunks while there are too few units to fill the chip
-      mode = kModeMRows;
       int uc = std::min<int>(kMaxUnitCols, p.padded_cols);
       while (uc > kMinUnitCols && blocks * ((p.padded_cols + uc - 1) / uc) < kTargetUnits)
         uc = std::max<int>(kMinUnitCols, int(round_up(uc / 2, 4)));
       p.unit_cols = uc;
+      mode = uc <= kNarrowUnitCols ? kModeMRowsNarrow : kModeMRows;
     }
     p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
     units = blocks * p.per_row;
@@ -667,25 +577,21 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   p.pitch = 16 * p.pieces + 4;
   p.units = units;
   p.vunits = round_up(units, 8);
-  size_t stride = kHeaderBytes + (mode == kModeMFlat ? size_t(kTileRows) * size_t(cols) + 32 + kLdsSlack
-                                                    : size_t(kTileRows) * size_t(p.pitch) + kLdsSlack);
-  stride = (stride + 15) & ~size_t(15);
-  p.lds_stride = int(stride);
-  size_t lds_bytes = 2 * stride;
+  // staged strip, then kLdsSlack bytes read past it by unaligned reads, then 16 trash bytes
+  size_t lds_bytes = mode == kModeMFlat ? size_t(kTileRows) * size_t(cols) + 32 + kLdsSlack
+                                        : size_t(kTileRows) * size_t(p.pitch) + kLdsSlack;
+  lds_bytes = (lds_bytes + 15) & ~size_t(15);
+  p.trash = int(lds_bytes);
+  lds_bytes += 16;
 
   const void *fn = mode == kModeMFlat   ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMFlat>)
                    : mode == kModeMRows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRows>)
+                   : mode == kModeMRowsNarrow ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow>)
                                         : reinterpret_cast<const void *>(&rearrange_kernel<kModeKRows>);
   const int threads = mode == kModeMFlat ? threads_for(kModeMFlat) : threads_for(kModeMRows);
-  // as many workgroups as can be resident at once (a multiple of 8, so that a
-  // workgroup's units all map to its own XCD), each looping over its units;
-  // when every workgroup gets a single unit, one LDS buffer is enough
-  int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);
-  if (kPersistent) {
-    const int64_t resident = resident_workgroups(fn, threads, lds_bytes);
-    if (resident >= 8) grid = std::min<int64_t>(grid, resident / 8 * 8);
-  }
-  if (grid >= p.vunits) lds_bytes = stride;
+  // one workgroup per unit; the grid is a multiple of 8, so a workgroup that
+  // loops (only past kMaxGrid units) stays on its XCD
+  const int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);
 
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(threads), args, lds_bytes, stream);

@@ -39,7 +39,11 @@ DEFAULT_WORKLOAD = "m_groups_skinny"
 # 19.46 us for the fallback CUDA kernel ("[mxfp8 moe training] fallback cuda kernel for when
 # input doesn't meet 2d TMA constraints", Benchmarks table). GPU not named on the page.
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
-KERNEL_NAMES = {"M": "rearrange_kernel<false>", "K": "rearrange_kernel<true>"}
+# kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
+# 3 = M narrow row segments, 2 = K row segments
+KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
+                "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
+                "k_groups_large": "rearrange_kernel<2>"}
 KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -163,6 +167,69 @@ def cpu_baseline(name, seconds):
     }
 
 
+def _counter_means(csv_path, counter, kernel_substring):
+    """Mean per-dispatch value of `counter` over the dispatches whose name contains kernel_substring."""
+    import csv
+
+    vals = []
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and kernel_substring in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise ValueError("no %s values for %s in %s" % (counter, kernel_substring, csv_path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, commands):
+    """HBM bytes per launch of the rearrange kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
+
+    Each counter (KiB per dispatch) is scaled by what it reads for a plain
+    device copy of known size (the --copy-calibration run), so the result is in
+    bytes whatever the counter's unit or coverage on this GPU.
+    """
+    import workloads
+
+    w = workloads.make(name)
+    copy_bytes = w.rows * w.cols
+    kfetch, nk = _counter_means(fetch_csv, "FETCH_SIZE", "rearrange_kernel")
+    kwrite, _ = _counter_means(write_csv, "WRITE_SIZE", "rearrange_kernel")
+    cfetch, nc = _counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _counter_means(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    fetch_scale = copy_bytes / cfetch      # bytes per counter unit
+    write_scale = copy_bytes / cwrite
+    read = kfetch * fetch_scale
+    written = kwrite * write_scale
+    import group_scale_factor_amd as gsf
+
+    lib = gsf.library()
+    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+    out_bytes = int(size_fn(w.rows, w.cols, w.num_groups))
+    d = {
+        "workload": name,
+        "kernel": KERNEL_NAMES.get(name),
+        "kernel_source_sha256_16": kernel_source_digest(),
+        "dispatches_averaged": nk,
+        "FETCH_SIZE_kib_per_dispatch": round(kfetch, 1),
+        "WRITE_SIZE_kib_per_dispatch": round(kwrite, 1),
+        "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "dispatches": nc,
+                             "FETCH_SIZE_kib": round(cfetch, 1), "WRITE_SIZE_kib": round(cwrite, 1),
+                             "fetch_bytes_per_unit": round(fetch_scale, 2),
+                             "write_bytes_per_unit": round(write_scale, 2)},
+        "hbm_read_bytes_per_launch": round(read),
+        "hbm_write_bytes_per_launch": round(written),
+        "hbm_bytes_per_launch": round(read + written),
+        "algorithmic_bytes_per_launch": w.rows * w.cols + out_bytes,
+        "traffic_over_algorithmic": round((read + written) / (w.rows * w.cols + out_bytes), 4),
+        "commands": commands,
+    }
+    path = os.path.join(PROFILES, "pmc_%s.json" % name)
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d))
+
+
 def hbm_traffic(name, kind):
     """Measured HBM bytes per launch from the committed counter profile, if it matches this kernel."""
     path = os.path.join(PROFILES, "pmc_%s.json" % name)
@@ -188,7 +255,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's plain device copy of the workload's input size instead "
                          "(reference kernel of known traffic for the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/pmc_<workload>.json from rocprofv3 counter_collection.csv files")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help="commands that produced the csv files")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc, commands=args.pmc_commands)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the rearrangement has no multi-GPU path in this build "
@@ -211,6 +284,7 @@ def main():
     K, W = args.steps, args.warmup
 
     if args.eager:
+        warm_launches = W
         for i in range(W):
             job.step(i)
         torch.cuda.synchronize()
@@ -223,19 +297,29 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     else:
-        gw = capture(job, 0, W) if W > 0 else None
-        gk = capture(job, W, K)
-        if gw is not None:
-            gw.replay()
+        # One graph covers one pass over the rotating copies (its first replay
+        # is part of the warm-up); the timed region replays it back to back.
+        chunk = min(job.copies, K)
+        g = capture(job, 0, chunk)
+        rem = K % chunk
+        g_rem = capture(job, 0, rem) if rem else None
+        warm_replays = max(1, math.ceil(W / chunk))
+        for _ in range(warm_replays):
+            g.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        warm_launches = warm_replays * chunk + rem
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record()
-        gk.replay()
+        for _ in range(K // chunk):
+            g.replay()
+        if g_rem is not None:
+            g_rem.replay()
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-
     gpu_s = ev0.elapsed_time(ev1) / 1e3
     us_per_launch = gpu_s / K * 1e6
     value = job.bytes_per_step * K / wall / 1e9
@@ -249,6 +333,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "warmup_launches_run": warm_launches,
         "ms_per_step": round(wall / K * 1e3, 6),
         "us_per_launch": round(us_per_launch, 3),
         "higher_is_better": True,
@@ -273,7 +358,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": hbm_traffic(args.workload, w.kind),
-            "kernel": KERNEL_NAMES[w.kind],
+            "kernel": KERNEL_NAMES.get(args.workload),
             "avg_launch_us": round(us_per_launch, 3),
         },
         "cpu_baseline": None,

@@ -30,7 +30,10 @@
  *     review: the notes on empty groups and on the zero-initialised output).
  *     Reading taken here: each group is its own blocked matrix of
  *     round_up(rows,128) x W_g bytes, stored contiguously from byte
- *     round_up(rows,128) * (sum of W_h for h < g).
+ *     round_up(rows,128) * (sum of W_h for h < g). No page prints a K-groups
+ *     byte position, so parity against the pages is unpinned for this
+ *     placement; the tests pin the code to the reading (hand-worked
+ *     positions that separate it from the other readings, the inverse map).
  *   - Padding bytes are zero (same review, the note on the output being
  *     allocated with zeros).
  *   - Output sizes: K groups, round_up(rows,128) * (cols + 4*G) bytes, which is

@@ -48,6 +48,10 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.oracle_3d_out_bytes.argtypes = [i64, i64, i64]
+        lib.oracle_3d_out_bytes.restype = i64
+        lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
+        lib.oracle_3d.restype = ctypes.c_int
         self.lib = lib
 
     def out_bytes(self, kind, rows, cols, num_groups):
@@ -83,6 +87,31 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return out[:n]
 
+    def out_bytes_3d(self, experts, rows, cols):
+        return int(self.lib.oracle_3d_out_bytes(experts, rows, cols))
+
+    def rearrange_3d(self, scales, out=None):
+        """Run the oracle on a host (experts, rows, cols) uint8 array with unit column stride.
+
+        Expert and row strides are taken from the array (any strided view).
+        Returns the flat uint8 output of out_bytes_3d(...) bytes.
+        """
+        if scales.dtype != np.uint8 or scales.ndim != 3:
+            raise ValueError("scales must be a 3-D uint8 array")
+        E, rows, cols = scales.shape
+        if E * rows * cols > 0 and cols > 1 and scales.strides[2] != 1:
+            raise ValueError("scales must have unit column stride")
+        ld = scales.strides[1] if rows > 1 else cols
+        es = scales.strides[0] if E > 1 else rows * ld
+        n = self.out_bytes_3d(E, rows, cols)
+        if out is None:
+            out = np.empty(max(n, 0), dtype=np.uint8)
+        sp = scales.__array_interface__["data"][0] if E * rows * cols > 0 else None
+        rc = self.lib.oracle_3d(sp, E, rows, cols, es, ld, out.ctypes.data if out.size > 0 else None)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return out[:n]
+
 
 _default = None
 
@@ -103,3 +132,11 @@ def out_bytes(kind, rows, cols, num_groups):
 
 def rearrange(kind, scales, offs, out=None):
     return default().rearrange(kind, scales, offs, out)
+
+
+def out_bytes_3d(experts, rows, cols):
+    return default().out_bytes_3d(experts, rows, cols)
+
+
+def rearrange_3d(scales, out=None):
+    return default().rearrange_3d(scales, out)

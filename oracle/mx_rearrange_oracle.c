@@ -159,3 +159,39 @@ int oracle_K_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t l
     }
     return ORACLE_OK;
 }
+
+/*
+ * Per-expert weight scales: `experts` matrices of rows x cols scale bytes,
+ * matrix e starting at scales + e * expert_stride, row stride ld. Each becomes
+ * its own blocked matrix of round_up(rows,128) x round_up(cols,4) bytes, the
+ * experts one after another. This is the weight operand of the grouped GEMM
+ * on "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by
+ * reshaping to 2d" (Benchmarks tables: B of shape (E, N, K)), whose scales
+ * are (E, N, K/32); every expert is one group of exactly N rows, so no
+ * offsets are needed. The layout of each matrix is the one read above.
+ */
+int64_t oracle_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols) {
+    return experts * round_up(rows, 128) * round_up(cols, 4);
+}
+
+int oracle_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols, int64_t expert_stride,
+              int64_t ld, uint8_t *out) {
+    if (experts < 0 || rows < 0 || cols < 0 || ld < cols || expert_stride < 0) return ORACLE_EBADSHAPE;
+    int64_t total = oracle_3d_out_bytes(experts, rows, cols);
+    if ((out == 0 && total > 0) || (scales == 0 && experts * rows * cols > 0)) return ORACLE_EBADPTR;
+    if (total == 0) return ORACLE_OK;
+    int64_t padded_rows = round_up(rows, 128);
+    int64_t padded_cols = round_up(cols, 4);
+    memset(out, 0, (size_t)total);
+    for (int64_t e = 0; e < experts; ++e) {
+        uint8_t *expert_out = out + e * padded_rows * padded_cols;
+        for (int64_t i = 0; i < padded_rows; ++i) {
+            for (int64_t j = 0; j < padded_cols; ++j) {
+                uint8_t v = 0;
+                if (i < rows && j < cols) v = scales[e * expert_stride + i * ld + j];
+                expert_out[blocked_byte(padded_cols, i, j)] = v;
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -269,3 +269,75 @@ def random_case(rng, kind, max_rows=700, max_cols=40, max_groups=6):
     total = rows if kind == "M" else cols
     offs = random_offsets(rng, total, G, p_empty=0.3, short_total=rng.random() < 0.3)
     return rows, cols, ld, offs
+
+
+# --------------------------------------------------------------------------
+# per-expert (3-D) weight scales: one blocked matrix per expert
+# --------------------------------------------------------------------------
+
+def strided_3d(buf, experts, rows, cols, es, ld):
+    return np.lib.stride_tricks.as_strided(buf, shape=(experts, rows, cols), strides=(es, ld, 1))
+
+
+def source_map_3d(orc, experts, rows, cols, es, ld):
+    """Linear input index (e*es + row*ld + col) held by each output byte, or -1."""
+    n = max(experts * es + rows * ld, 1)
+    assert n < (1 << 24)
+    idx = np.arange(n, dtype=np.int64)
+    outs = []
+    for k in range(3):
+        buf = ((idx >> (8 * k)) & 0xFF).astype(np.uint8)
+        outs.append(orc.rearrange_3d(strided_3d(buf, experts, rows, cols, es, ld)).astype(np.int64))
+    valid = orc.rearrange_3d(strided_3d(np.ones(n, np.uint8), experts, rows, cols, es, ld))
+    src = outs[0] | (outs[1] << 8) | (outs[2] << 16)
+    src[valid == 0] = -1
+    return src
+
+
+def decode_3d(experts, rows, cols, es, ld):
+    """Inverse map from the tile geometry: expert e owns bytes [e*Rp*Cp, (e+1)*Rp*Cp)."""
+    Rp, Cp = ru(rows, 128), ru(cols, 4)
+    n = experts * Rp * Cp
+    src = np.full(n, -1, dtype=np.int64)
+    if n == 0:
+        return src
+    b = np.arange(n, dtype=np.int64)
+    e, local = b // (Rp * Cp), b % (Rp * Cp)
+    t, r, c = _tile_coords(local)
+    row = (t // (Cp // 4)) * 128 + r
+    col = (t % (Cp // 4)) * 4 + c
+    hit = (row < rows) & (col < cols)
+    src[hit] = e[hit] * es + row[hit] * ld + col[hit]
+    return src
+
+
+def check_inverse_3d(orc, experts, rows, cols, es, ld):
+    n = orc.out_bytes_3d(experts, rows, cols)
+    src = source_map_3d(orc, experts, rows, cols, es, ld)
+    want = decode_3d(experts, rows, cols, es, ld)
+    if n != want.size or src.shape != want.shape or not np.array_equal(src, want):
+        return ["3d E=%d rows=%d cols=%d es=%d ld=%d: output differs from the decoded map"
+                % (experts, rows, cols, es, ld)]
+    return []
+
+
+def check_3d_reshape(orc, rng):
+    """Each expert's slice is the reshape layout of that expert's padded matrix."""
+    fails = []
+    for E, rows, cols in [(1, 1, 1), (1, 128, 4), (3, 200, 7), (2, 256, 12), (4, 77, 13), (5, 128, 160)]:
+        A = rng.integers(1, 256, size=(E, rows, cols), dtype=np.uint8)
+        out = orc.rearrange_3d(A)
+        Rp, Cp = ru(rows, 128), ru(cols, 4)
+        want = np.concatenate([to_blocked_reshape(pad_to(A[e], Rp, Cp)) for e in range(E)])
+        if not np.array_equal(out, want):
+            fails.append("3d E=%d %dx%d differs from the per-expert reshape layout" % (E, rows, cols))
+    return fails
+
+
+def random_case_3d(rng, max_experts=5, max_rows=300, max_cols=40):
+    E = int(rng.integers(0, max_experts + 1))
+    rows = int(rng.integers(0, max_rows + 1))
+    cols = int(rng.integers(0, max_cols + 1))
+    ld = cols + int(rng.choice([0, 0, 1, 3, 13]))
+    es = rows * ld + int(rng.choice([0, 0, 5, 64]))
+    return E, rows, cols, es, ld

@@ -166,6 +166,62 @@ def test_workload_m_tiny_inverse(orc):
     assert pins.check_inverse(orc, "M", w.rows, w.cols, w.cols, w.offs) == []
 
 
+def test_3d_inverse_map_random(orc):
+    rng = np.random.default_rng(300)
+    fails = []
+    for _ in range(60):
+        fails += pins.check_inverse_3d(orc, *pins.random_case_3d(rng))
+    assert fails == []
+
+
+def test_3d_brute_force_tiny(orc):
+    fails = []
+    for E in (0, 1, 2, 3):
+        for rows in (0, 1, 5, 127, 128, 129):
+            for cols in range(0, 7):
+                for ld_pad, es_pad in ((0, 0), (2, 0), (1, 9)):
+                    ld = cols + ld_pad
+                    fails += pins.check_inverse_3d(orc, E, rows, cols, rows * ld + es_pad, ld)
+    assert fails == []
+
+
+def test_3d_per_expert_reshape(orc):
+    assert pins.check_3d_reshape(orc, np.random.default_rng(9)) == []
+
+
+def test_3d_is_m_groups_of_equal_size(orc):
+    # experts of N rows each are M groups of N rows: same bytes over the 3-D output
+    rng = np.random.default_rng(10)
+    for E, N, C in [(1, 5, 3), (3, 128, 8), (4, 200, 13), (2, 1, 1)]:
+        A = rng.integers(1, 256, size=(E, N, C), dtype=np.uint8)
+        out = orc.rearrange_3d(A)
+        m = orc.rearrange("M", A.reshape(E * N, C), [N * (e + 1) for e in range(E)])
+        assert np.array_equal(out, m[: out.size])
+        assert not m[out.size:].any()
+
+
+def test_3d_sizes_and_errors(orc):
+    assert orc.out_bytes_3d(64, 8192, 160) == 64 * 8192 * 160
+    assert orc.out_bytes_3d(3, 129, 5) == 3 * 256 * 8
+    assert orc.out_bytes_3d(0, 100, 100) == 0
+    assert orc.rearrange_3d(np.zeros((2, 0, 5), np.uint8)).size == 0
+    out = orc.rearrange_3d(np.zeros((2, 3, 0), np.uint8))
+    assert out.size == 0
+    rc = orc.lib.oracle_3d(None, 1, 4, 4, 16, 3, None)  # ld < cols
+    assert rc != 0
+
+
+@pytest.mark.parametrize("name", ["experts_3d_small", "experts_3d_e16", "experts_3d_e64"])
+def test_3d_workload_invariants(orc, name):
+    w = workloads.make(name)
+    out = orc.rearrange_3d(w.scales)
+    hist_in = np.bincount(w.scales.reshape(-1), minlength=256)
+    hist_out = np.bincount(out, minlength=256)
+    assert hist_in[0] == 0
+    assert np.array_equal(hist_out[1:], hist_in[1:])
+    assert hist_out[0] == out.size - w.scales.size
+
+
 # --------------------------------------------------------------------------
 # planted mistakes: each broken copy of the oracle must fail at least one pin
 # --------------------------------------------------------------------------
@@ -187,6 +243,12 @@ MUTANTS = {
                                             "return round_up(rows, 128) * (cols + 3 * (int64_t)num_groups);"),
     "M row stride taken as cols": ("v = scales[(group_start + i) * ld + j];",
                                    "v = scales[(group_start + i) * cols + j];"),
+    "3-D expert stride ignored": ("v = scales[e * expert_stride + i * ld + j];",
+                                  "v = scales[e * rows * ld + i * ld + j];"),
+    "3-D experts packed without row padding": ("uint8_t *expert_out = out + e * padded_rows * padded_cols;",
+                                               "uint8_t *expert_out = out + e * rows * padded_cols;"),
+    "3-D columns not padded": ("expert_out[blocked_byte(padded_cols, i, j)] = v;",
+                               "expert_out[blocked_byte(cols, i, j)] = v;"),
 }
 
 
@@ -217,6 +279,9 @@ def test_planted_mistake_is_caught(name):
                     fails += pins.check_inverse(mut, kind, rows, cols, ld, offs)
                 except (AssertionError, ValueError, IndexError) as e:
                     fails.append(repr(e))
+        for _ in range(10):
+            fails += pins.check_inverse_3d(mut, *pins.random_case_3d(rng))
+        fails += pins.check_3d_reshape(mut, rng)
         assert fails, "mutant '%s' passed every pin" % name
     finally:
         shutil.rmtree(tmp, ignore_errors=True)

@@ -5,7 +5,7 @@ offsets. It holds none of the rearrangement's arithmetic (no padding, no prefix
 sums of padded sizes, no layout), so both the CPU oracle and the HIP library can
 be fed from it without sharing any of the method.
 
-The five named workloads stand in for the shapes the pages benchmark:
+The named workloads stand in for the shapes the pages benchmark:
 
 * "[mxfp8 moe training] fallback cuda kernel for when input doesn't meet 2d TMA
   constraints", Benchmarks table: M-groups scales of shape (131072, 44), the
@@ -13,6 +13,8 @@ The five named workloads stand in for the shapes the pages benchmark:
 * "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by reshaping to
   2d", Benchmarks tables: activations A of shape (16640, 5120), whose block-32
   scales are (16640, 160).
+* The same page's B operand of shape (E, 8192, 5120) for E = 16 and 64: per-expert
+  weight scales of shape (E, 8192, 160), one blocked matrix per expert.
 * "Add CuTeDSL MXFP8 K-groups scale rearrange kernel", realistic-shapes table:
   M x TotalK = 7168 x 131072 and 28672 x 262144 with 8 groups, group widths drawn
   with a granularity of one scale column (the bench's multiple-of-1 option).
@@ -108,6 +110,46 @@ def k_groups_large(seed=5):
                     "K-groups large: uint8 scales (28672, 8192), 8 groups")
 
 
+@dataclass
+class ExpertWorkload:
+    """Per-expert weight scales: E matrices of (rows, cols) scale bytes, no offsets."""
+    name: str
+    experts: int
+    rows: int
+    cols: int
+    scales: np.ndarray   # uint8[experts, rows, cols]; unit column stride, strides as drawn
+    description: str
+    kind: str = "3d"
+
+
+def _expert_values(rng, experts, rows, cols, expert_pad, lo, hi):
+    """(experts, rows, cols) bytes in [lo, hi]; expert_pad spare bytes between experts."""
+    es = rows * cols + expert_pad
+    base = rng.integers(lo, hi + 1, size=max(experts * es, 1), dtype=np.uint8)
+    return np.lib.stride_tricks.as_strided(base, shape=(experts, rows, cols), strides=(es, cols, 1))
+
+
+def experts_3d_small(seed=6):
+    """3 experts of (300, 45) scales, 64 spare bytes between experts, values in [1, 255]."""
+    rng = np.random.default_rng(seed)
+    return ExpertWorkload("experts_3d_small", 3, 300, 45, _expert_values(rng, 3, 300, 45, 64, 1, 255),
+                          "3-D expert scales: 3 x (300, 45), experts 64 bytes apart beyond their size")
+
+
+def experts_3d_e16(seed=7):
+    """Weights (16, 8192, 5120): block-32 scales (16, 8192, 160), values in [100, 150]."""
+    rng = np.random.default_rng(seed)
+    return ExpertWorkload("experts_3d_e16", 16, 8192, 160, _expert_values(rng, 16, 8192, 160, 0, 100, 150),
+                          "3-D expert scales: uint8 (16, 8192, 160)")
+
+
+def experts_3d_e64(seed=8):
+    """Weights (64, 8192, 5120): block-32 scales (64, 8192, 160), values in [100, 150]."""
+    rng = np.random.default_rng(seed)
+    return ExpertWorkload("experts_3d_e64", 64, 8192, 160, _expert_values(rng, 64, 8192, 160, 0, 100, 150),
+                          "3-D expert scales: uint8 (64, 8192, 160)")
+
+
 WORKLOADS = {
     "m_groups_tiny": m_groups_tiny,
     "m_groups_skinny": m_groups_skinny,
@@ -116,8 +158,16 @@ WORKLOADS = {
     "k_groups_large": k_groups_large,
 }
 
+WORKLOADS_3D = {
+    "experts_3d_small": experts_3d_small,
+    "experts_3d_e16": experts_3d_e16,
+    "experts_3d_e64": experts_3d_e64,
+}
 
-def make(name: str) -> Workload:
+
+def make(name: str):
+    if name in WORKLOADS_3D:
+        return WORKLOADS_3D[name]()
     return WORKLOADS[name]()
 
 

@@ -5,7 +5,8 @@ A step is one rearrangement launch over one batch of synthetic scales (group
 scan, lookup, strip load, in-tile interleave, zero padding, stores and tail
 fill all happen inside that launch). The default workload is the M-groups
 skinny case: scales (131072, 44) with 44-byte rows, 8 groups. `--workload`
-selects any of the other named workloads.
+selects any of the other named workloads, including the per-expert (3-D)
+weight scales, where a step is one launch over all experts.
 
 Timing: inputs are resident in HBM before the timed region. Steps rotate over
 enough copies of input and output (1 GiB by default, four times the 256 MB
@@ -41,9 +42,11 @@ DEFAULT_WORKLOAD = "m_groups_skinny"
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
 # kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
 # 3 = M narrow row segments, 2 = K row segments
+# 4 = per-expert row segments
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
                 "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
-                "k_groups_large": "rearrange_kernel<2>"}
+                "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
+                "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<4>"}
 KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -55,6 +58,17 @@ def kernel_source_digest():
 
 def align_up(x, a):
     return (x + a - 1) // a * a
+
+
+def in_bytes_of(w):
+    return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
+
+
+def out_bytes_of(lib, w):
+    if w.kind == "3d":
+        return int(lib.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
+    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+    return int(size_fn(w.rows, w.cols, w.num_groups))
 
 
 class Job:
@@ -71,9 +85,8 @@ class Job:
         self.w = w = workloads.make(name)
         self.kind = w.kind
         lib = gsf.library()
-        size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
-        self.out_bytes = int(size_fn(w.rows, w.cols, w.num_groups))
-        self.in_bytes = w.rows * w.cols
+        self.out_bytes = out_bytes_of(lib, w)
+        self.in_bytes = in_bytes_of(w)
         self.bytes_per_step = self.in_bytes + self.out_bytes
         self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
         in_pitch = align_up(self.in_bytes, 256)
@@ -84,11 +97,12 @@ class Job:
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
         for k in range(self.copies):
             self.inp[k * in_pitch: k * in_pitch + self.in_bytes].copy_(src)
-        self.offs = torch.from_numpy(w.offs).to(dev)
+        self.offs = torch.from_numpy(w.offs).to(dev) if w.kind != "3d" else None
         self.outs = [self.outbuf[k * out_pitch: k * out_pitch + self.out_bytes] for k in range(self.copies)]
         self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
-        self.fn = lib.mx_block_rearrange_M_groups if w.kind == "M" else lib.mx_block_rearrange_K_groups
+        self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
+                   "3d": lib.mx_block_rearrange_3d}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -97,8 +111,13 @@ class Job:
         k = i % self.copies
         if stream is None:
             stream = self.torch.cuda.current_stream().cuda_stream
-        rc = self.fn(self.in_ptrs[k], self.w.rows, self.w.cols, self.w.cols, self.offs.data_ptr(),
-                     self.w.num_groups, self.out_ptrs[k], stream or None)
+        w = self.w
+        if w.kind == "3d":   # experts packed: expert stride rows*cols, row stride cols
+            rc = self.fn(self.in_ptrs[k], w.experts, w.rows, w.cols, w.rows * w.cols, w.cols, self.out_ptrs[k],
+                         stream or None)
+        else:
+            rc = self.fn(self.in_ptrs[k], w.rows, w.cols, w.cols, self.offs.data_ptr(), w.num_groups,
+                         self.out_ptrs[k], stream or None)
         if rc != 0:
             raise self.error(rc)
 
@@ -125,7 +144,7 @@ def copy_calibration(args):
     import workloads
 
     w = workloads.make(args.workload)
-    n = w.rows * w.cols
+    n = in_bytes_of(w)
     copies = max(2, min(4096, math.ceil((args.rotate_mib << 20) / (2 * n))))
     src = torch.randint(0, 255, (copies, n), dtype=torch.uint8, device="cuda")
     dst = torch.empty((copies, n), dtype=torch.uint8, device="cuda")
@@ -150,19 +169,24 @@ def cpu_baseline(name, seconds):
     out = None
     reps, t0 = 0, time.perf_counter()
     while True:
-        out = oracle.rearrange(w.kind, w.scales, w.offs, out)
+        if w.kind == "3d":
+            out = oracle.rearrange_3d(w.scales, out)
+        else:
+            out = oracle.rearrange(w.kind, w.scales, w.offs, out)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    bytes_step = w.rows * w.cols + out.size
+    bytes_step = in_bytes_of(w) + out.size
+    shape = "x".join(str(x) for x in w.scales.shape)
+    groups = "%d experts" % w.experts if w.kind == "3d" else "%d groups" % w.num_groups
     return {
         "value": round(bytes_step * reps / el / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%d full runs of the %s workload (%dx%d scales, %d groups) in %.1f s, single-threaded C oracle"
-                  % (reps, name, w.rows, w.cols, w.num_groups, el),
+        "sample": "%d full runs of the %s workload (%s scales, %s) in %.1f s, single-threaded C oracle"
+                  % (reps, name, shape, groups, el),
         "us_per_call": round(el / reps * 1e6, 1),
     }
 
@@ -191,7 +215,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     import workloads
 
     w = workloads.make(name)
-    copy_bytes = w.rows * w.cols
+    copy_bytes = in_bytes_of(w)
     kfetch, nk = _counter_means(fetch_csv, "FETCH_SIZE", "rearrange_kernel")
     kwrite, _ = _counter_means(write_csv, "WRITE_SIZE", "rearrange_kernel")
     cfetch, nc = _counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
@@ -202,9 +226,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     written = kwrite * write_scale
     import group_scale_factor_amd as gsf
 
-    lib = gsf.library()
-    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
-    out_bytes = int(size_fn(w.rows, w.cols, w.num_groups))
+    out_bytes = out_bytes_of(gsf.library(), w)
     d = {
         "workload": name,
         "kernel": KERNEL_NAMES.get(name),
@@ -219,8 +241,8 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
         "hbm_read_bytes_per_launch": round(read),
         "hbm_write_bytes_per_launch": round(written),
         "hbm_bytes_per_launch": round(read + written),
-        "algorithmic_bytes_per_launch": w.rows * w.cols + out_bytes,
-        "traffic_over_algorithmic": round((read + written) / (w.rows * w.cols + out_bytes), 4),
+        "algorithmic_bytes_per_launch": copy_bytes + out_bytes,
+        "traffic_over_algorithmic": round((read + written) / (copy_bytes + out_bytes), 4),
         "commands": commands,
     }
     path = os.path.join(PROFILES, "pmc_%s.json" % name)
@@ -343,9 +365,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "kind": "%s-groups" % w.kind,
-            "scales_shape": [w.rows, w.cols],
-            "num_groups": w.num_groups,
+            "kind": "per-expert" if w.kind == "3d" else "%s-groups" % w.kind,
+            "scales_shape": list(w.scales.shape),
+            "num_groups": w.experts if w.kind == "3d" else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,
             "launch": "eager" if args.eager else "hip_graph",

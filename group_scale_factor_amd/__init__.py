@@ -9,12 +9,15 @@ fails loudly when the library has not been built.
 
     out = mx_block_rearrange_M_groups(scales, group_end_offsets)
     out = mx_block_rearrange_K_groups(scales, group_end_offsets)
+    out = mx_block_rearrange_3d(expert_scales)
 
 ``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
 row stride >= cols, any base alignment); ``group_end_offsets`` an int32 CUDA
 tensor of cumulative group ends (rows for M, scale columns for K). The result is
 a flat uint8 tensor of ``*_out_bytes(rows, cols, G)`` bytes holding the blocked
-128x4-tile layout of every group, padding zeroed.
+128x4-tile layout of every group, padding zeroed. ``expert_scales`` is an
+(E, rows, cols) uint8 CUDA tensor with unit column stride (per-expert weight
+scales); every expert becomes its own blocked matrix.
 """
 
 import ctypes
@@ -44,6 +47,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp]
         fn.restype = ctypes.c_int
+    lib.mx_rearrange_3d_out_bytes.argtypes = [i64, i64, i64]
+    lib.mx_rearrange_3d_out_bytes.restype = i64
+    lib.mx_block_rearrange_3d.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp]
+    lib.mx_block_rearrange_3d.restype = ctypes.c_int
     lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
     lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -61,6 +68,10 @@ def mx_rearrange_M_groups_out_bytes(rows, cols, num_groups):
 
 def mx_rearrange_K_groups_out_bytes(rows, cols, num_groups):
     return int(_load().mx_rearrange_K_groups_out_bytes(rows, cols, num_groups))
+
+
+def mx_rearrange_3d_out_bytes(experts, rows, cols):
+    return int(_load().mx_rearrange_3d_out_bytes(experts, rows, cols))
 
 
 class RearrangeError(RuntimeError):
@@ -128,7 +139,49 @@ def mx_block_rearrange_K_groups(scales, group_end_offsets, out=None, stream=None
     return _call("K", scales, group_end_offsets, out, stream)
 
 
+def mx_block_rearrange_3d(scales, out=None, stream=None):
+    """Per-expert weight scales (E, rows, cols): one blocked matrix per expert.
+
+    Expert e's rows are padded to a multiple of 128 and its columns to a
+    multiple of 4; the experts follow one another. Returns the flat uint8 output
+    of E * round_up(rows, 128) * round_up(cols, 4) bytes. Any expert and row
+    strides (row stride >= cols) with unit column stride.
+    ``stream`` is a raw hipStream_t handle (int); default: torch's current stream.
+    """
+    import torch
+
+    lib = _load()
+    if scales.dtype != torch.uint8 or scales.dim() != 3:
+        raise TypeError("scales must be a 3-D torch.uint8 tensor")
+    if not scales.is_cuda:
+        raise ValueError("scales must be a GPU tensor")
+    E, rows, cols = scales.shape
+    if E * rows * cols > 0 and cols > 1 and scales.stride(2) != 1:
+        raise ValueError("scales must have unit column stride")
+    row_stride = scales.stride(1) if rows > 1 else cols
+    expert_stride = scales.stride(0) if E > 1 else rows * row_stride
+    n = int(lib.mx_rearrange_3d_out_bytes(E, rows, cols))
+    if n < 0:
+        raise ValueError("invalid sizes experts=%d rows=%d cols=%d" % (E, rows, cols))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=scales.device)
+    else:
+        if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < n:
+            raise ValueError("out must be a contiguous uint8 tensor of at least %d bytes" % n)
+        if out.device != scales.device:
+            raise ValueError("out must be on the scales' device")
+    if stream is None:
+        stream = torch.cuda.current_stream(scales.device).cuda_stream
+    rc = lib.mx_block_rearrange_3d(scales.data_ptr() or None, E, rows, cols, expert_stride, row_stride,
+                                   out.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return out
+
+
 __all__ = [
+    "mx_block_rearrange_3d",
+    "mx_rearrange_3d_out_bytes",
     "mx_block_rearrange_M_groups",
     "mx_block_rearrange_K_groups",
     "mx_rearrange_M_groups_out_bytes",

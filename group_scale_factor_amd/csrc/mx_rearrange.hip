@@ -11,7 +11,9 @@
 // blocked format kernels for groups along K" (128x4 tiles per group along K);
 // "Add CuTeDSL MXFP8 K-groups scale rearrange kernel" (review: widths padded to
 // 4 columns, empty groups, zero padding, 128-bit loads with a byte-exact
-// fallback).
+// fallback); "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by
+// reshaping to 2d" (Benchmarks tables: per-expert weights (E, N, K), whose
+// scales become one blocked matrix per expert).
 //
 // The work is pure data movement, bound by HBM bandwidth; there is no
 // arithmetic on the scale values. Design:
@@ -74,6 +76,7 @@ constexpr int kRawBufferFlags = 0x00020000;            // buffer descriptor word
 constexpr int kFlatLoadPolicy = 2;
 constexpr int kMRowsLoadPolicy = 2;
 constexpr int kKRowsLoadPolicy = 0;
+constexpr int k3dLoadPolicy = 2;
 
 // Staging modes; each is its own kernel instantiation.
 enum Mode : int {
@@ -81,14 +84,25 @@ enum Mode : int {
   kModeMRows = 1,   // M groups, one row segment at a time
   kModeMRowsNarrow = 3,  // M groups, one row segment of at most kNarrowUnitCols at a time
   kModeKRows = 2,   // K groups, one row segment at a time
+  kMode3d = 4,      // per-expert matrices, one row segment at a time, no group lookup
 };
 
 // Narrow M units (small problems split into many column chunks) get their own
 // instantiation sized for them: fewer loads per lane, fewer registers.
 constexpr int kNarrowUnitCols = 48;
+// Per-expert units span a whole 128-row block of up to 160 columns (the
+// block-32 scales of K = 5120): one contiguous output run per row block.
+constexpr int k3dMaxUnitCols = 160;
 constexpr int threads_for(int mode) { return mode == kModeMFlat ? 128 : 256; }
-constexpr int max_pieces_for(int mode) {
-  return ((mode == kModeMRowsNarrow ? kNarrowUnitCols : kMaxUnitCols) + 30) / 16;
+constexpr int max_unit_cols_for(int mode) {
+  return mode == kModeMRowsNarrow ? kNarrowUnitCols : mode == kMode3d ? k3dMaxUnitCols : kMaxUnitCols;
+}
+constexpr int max_pieces_for(int mode) { return (max_unit_cols_for(mode) + 30) / 16; }
+constexpr int load_policy_for(int mode) {
+  return mode == kModeMFlat ? kFlatLoadPolicy
+         : mode == kModeKRows ? kKRowsLoadPolicy
+         : mode == kMode3d    ? k3dLoadPolicy
+                              : kMRowsLoadPolicy;
 }
 constexpr int load_iters_for(int mode) {
   return ((mode == kModeMFlat ? kMaxFlatPieces : kTileRows * max_pieces_for(mode)) + threads_for(mode) - 1) /
@@ -101,7 +115,10 @@ constexpr int kMinWavesPerEu = 1;
 
 static_assert(kMaxUnitCols % 4 == 0 && kMinUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kTileRows * kMaxPitch + kLdsSlack <= 64 * 1024, "LDS per workgroup");
-static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8, "staging unrolled to 8");
+static_assert(kTileRows * (16 * max_pieces_for(kMode3d) + 4) + kLdsSlack <= 64 * 1024, "LDS per workgroup");
+static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8 && load_iters_for(kMode3d) <= 8,
+              "staging unrolled to 8");
+static_assert(k3dMaxUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narrow units");
 
 struct Params {
@@ -115,12 +132,14 @@ struct Params {
   int rows;
   int cols;
   int groups;
-  int padded_cols;     // M: round_up(cols, 4)
+  int padded_cols;     // M and per-expert: round_up(cols, 4)
   int unit_cols;       // columns per unit chunk (multiple of 4)
   int per_row;         // M: units per output row block; K: units per 128-row block
   int pitch;           // LDS row pitch (bytes) in per-row staging
   int pieces;          // 16-byte pieces per LDS row in per-row staging
   int trash;           // LDS offset of 16 bytes that staging pieces without data are written to
+  int64_t expert_stride;  // per-expert matrices: bytes between experts
+  int64_t row_blocks;     // per-expert matrices: 128-row blocks per expert
 };
 
 // ---------------------------------------------------------------------------
@@ -431,8 +450,8 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
     stage_flat<NT, load_iters_for(MODE), kFlatLoadPolicy>(lds, p.trash, row_base, nrows * ncols);
     aligned = ((a & 3) == 0) && ((ncols & 3) == 0);
   } else {
-    stage_rows<NT, load_iters_for(MODE), MODE == kModeKRows ? kKRowsLoadPolicy : kMRowsLoadPolicy>(
-        lds, p.trash, row_base, p.ld, nrows, ncols, p.pitch, p.pieces);
+    stage_rows<NT, load_iters_for(MODE), load_policy_for(MODE)>(lds, p.trash, row_base, p.ld, nrows, ncols,
+                                                                p.pitch, p.pieces);
     aligned = ((a & 3) == 0) && ((p.ld & 3) == 0);
   }
   __syncthreads();
@@ -467,7 +486,21 @@ void rearrange_kernel(Params p) {
     const int64_t block = unit / p.per_row;             // output row block (M) / 128-row block (K)
     const int slot = int(unit - block * p.per_row);     // column chunk (M) / unit within the row block (K)
 
-    if (!KGROUPS) {
+    if constexpr (MODE == kMode3d) {
+      // expert e's row block rb is output row block e*row_blocks + rb; every
+      // unit holds data (rows >= 1, and a chunk starts below round_up(cols,4)
+      // at a multiple of 4, hence below cols), so the units cover the output
+      const int64_t e = block / p.row_blocks;
+      const int rb = int(block - e * p.row_blocks);
+      const int nrows = min(kTileRows, p.rows - kTileRows * rb);
+      const int c0 = slot * p.unit_cols;
+      const int ncols = min(p.unit_cols, p.cols - c0);
+      const int tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
+      uint8_t *dst = p.out + block * int64_t(kTileRows) * p.padded_cols + int64_t(c0) * kTileRows;
+      if (nrows > 0 && ncols > 0)
+        copy_unit<MODE>(lds, p, p.src + e * p.expert_stride + int64_t(kTileRows) * rb * p.ld + c0, nrows, ncols,
+                        tile_cols, dst);
+    } else if constexpr (!KGROUPS) {
       const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, p.unit_cols, int(block));
       const int64_t row_block_bytes = int64_t(kTileRows) * p.padded_cols;
       if (h.group < p.groups) {
@@ -524,6 +557,8 @@ bool sizes_ok(int64_t rows, int64_t cols, int64_t ld, int32_t groups) {
   return rows <= lim - 128 * int64_t(groups) && cols <= lim - 4 * int64_t(groups);
 }
 
+int dispatch(Params &p, int mode, int64_t units, hipStream_t stream);
+
 int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
            const int32_t *offs, int32_t groups, uint8_t *out, hipStream_t stream) {
   if (!sizes_ok(rows, cols, ld, groups)) return MX_REARRANGE_ESHAPE;
@@ -536,7 +571,7 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   if (reinterpret_cast<uintptr_t>(out) & 15) return MX_REARRANGE_EALIGN;
   if (out_bytes == 0) return MX_REARRANGE_OK;
 
-  Params p;
+  Params p = {};
   p.src = scales;
   p.offs = offs;
   p.out = out;
@@ -572,13 +607,51 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
     p.per_row = int((cols + 4 * int64_t(groups) + p.unit_cols - 1) / p.unit_cols + groups);
     units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
-  const int64_t seg = std::min<int64_t>(cols, p.unit_cols);   // widest row segment of a unit
+  return dispatch(p, mode, units, stream);
+}
+
+// Per-expert matrices: one unit per (expert, 128-row block, column chunk).
+int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols, int64_t expert_stride,
+              int64_t ld, uint8_t *out, hipStream_t stream) {
+  const int64_t out_bytes = mx_rearrange_3d_out_bytes(experts, rows, cols);
+  if (out_bytes < 0 || ld < cols || ld > kMaxRowStride || expert_stride < 0) return MX_REARRANGE_ESHAPE;
+  if (experts > 1 && expert_stride > INT64_MAX / experts) return MX_REARRANGE_ESHAPE;
+  if (experts * rows * cols > 0 && scales == nullptr) return MX_REARRANGE_ENULL;
+  if (out_bytes > 0 && out == nullptr) return MX_REARRANGE_ENULL;
+  if (reinterpret_cast<uintptr_t>(out) & 15) return MX_REARRANGE_EALIGN;
+  if (out_bytes == 0) return MX_REARRANGE_OK;
+
+  Params p = {};
+  p.src = scales;
+  p.out = out;
+  p.ld = ld;
+  p.out_bytes = out_bytes;
+  p.rows = int(rows);
+  p.cols = int(cols);
+  p.groups = 0;
+  p.padded_cols = int(round_up(cols, 4));
+  p.expert_stride = expert_stride;
+  p.row_blocks = (rows + kTileRows - 1) / kTileRows;
+  const int64_t blocks = experts * p.row_blocks;
+  // balanced column chunks of at most k3dMaxUnitCols; more of them while the
+  // grid is too small to fill the chip
+  int per_row = (p.padded_cols + k3dMaxUnitCols - 1) / k3dMaxUnitCols;
+  auto chunk = [&](int n) { return int(round_up((p.padded_cols + n - 1) / n, 4)); };
+  while (blocks * per_row < kTargetUnits && chunk(per_row + 1) >= kMinUnitCols && chunk(per_row + 1) < chunk(per_row))
+    ++per_row;
+  p.unit_cols = chunk(per_row);
+  p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
+  return dispatch(p, kMode3d, blocks * p.per_row, stream);
+}
+
+int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
+  const int64_t seg = std::min<int64_t>(p.cols, p.unit_cols);   // widest row segment of a unit
   p.pieces = std::max<int>(1, int((seg + 30) / 16));
   p.pitch = 16 * p.pieces + 4;
   p.units = units;
   p.vunits = round_up(units, 8);
   // staged strip, then kLdsSlack bytes read past it by unaligned reads, then 16 trash bytes
-  size_t lds_bytes = mode == kModeMFlat ? size_t(kTileRows) * size_t(cols) + 32 + kLdsSlack
+  size_t lds_bytes = mode == kModeMFlat ? size_t(kTileRows) * size_t(p.cols) + 32 + kLdsSlack
                                         : size_t(kTileRows) * size_t(p.pitch) + kLdsSlack;
   lds_bytes = (lds_bytes + 15) & ~size_t(15);
   p.trash = int(lds_bytes);
@@ -587,6 +660,7 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   const void *fn = mode == kModeMFlat   ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMFlat>)
                    : mode == kModeMRows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRows>)
                    : mode == kModeMRowsNarrow ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow>)
+                   : mode == kMode3d    ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3d>)
                                         : reinterpret_cast<const void *>(&rearrange_kernel<kModeKRows>);
   const int threads = mode == kModeMFlat ? threads_for(kModeMFlat) : threads_for(kModeMRows);
   // one workgroup per unit; the grid is a multiple of 8, so a workgroup that
@@ -612,6 +686,14 @@ int64_t mx_rearrange_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_
   return round_up(rows, 128) * (cols + 4 * int64_t(num_groups));
 }
 
+int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols) {
+  const int64_t lim = (int64_t(1) << 31) - 128;
+  if (experts < 0 || rows < 0 || cols < 0 || rows >= lim || cols >= lim) return -1;
+  const int64_t per_expert = round_up(rows, 128) * round_up(cols, 4);
+  if (per_expert > 0 && experts > INT64_MAX / per_expert) return -1;
+  return experts * per_expert;
+}
+
 int mx_block_rearrange_M_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t row_stride,
                                 const int32_t *group_end_offsets, int32_t num_groups, uint8_t *out,
                                 hipStream_t stream) {
@@ -622,6 +704,11 @@ int mx_block_rearrange_K_groups(const uint8_t *scales, int64_t rows, int64_t col
                                 const int32_t *group_end_offsets, int32_t num_groups, uint8_t *out,
                                 hipStream_t stream) {
   return launch(true, scales, rows, cols, row_stride, group_end_offsets, num_groups, out, stream);
+}
+
+int mx_block_rearrange_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols,
+                          int64_t expert_stride, int64_t row_stride, uint8_t *out, hipStream_t stream) {
+  return launch_3d(scales, experts, rows, cols, expert_stride, row_stride, out, stream);
 }
 
 const char *mx_rearrange_strerror(int status) {

@@ -129,6 +129,47 @@ int mx_block_rearrange_K_groups(const uint8_t *scales, int64_t rows, int64_t col
                                 int64_t row_stride, const int32_t *group_end_offsets,
                                 int32_t num_groups, uint8_t *out, hipStream_t stream);
 
+/*
+ * Per-expert (3-D) weight scales. Source: "[mxfp8 moe training] use dim1 cast
+ * cuda kernel for 3d weights by reshaping to 2d" — the grouped GEMM's weight
+ * operand B of shape (E, N, K) (Benchmarks tables, B_shape), quantized in
+ * blocks of 32 along K, has scales of shape (E, N, K/32). Each expert is one
+ * group of exactly N rows, so no offsets and no scan are needed: expert e's
+ * (rows x cols) scale matrix becomes its own blocked matrix of
+ * round_up(rows,128) rows and round_up(cols,4) columns (the tile map above),
+ * stored from byte e * round_up(rows,128) * round_up(cols,4). This equals the
+ * M-groups layout of E equal groups of `rows` rows, without the M-groups tail.
+ *
+ * Output size in bytes: experts * round_up(rows,128) * round_up(cols,4);
+ * -1 for invalid sizes (negative, rows or cols >= 2^31 - 128, or a size that
+ * does not fit in int64).
+ */
+int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols);
+
+/*
+ * scales         device pointer; element (e, i, j) at
+ *                scales + e*expert_stride + i*row_stride + j. Any byte
+ *                alignment. May be NULL when experts*rows*cols == 0. Read only;
+ *                experts may overlap (expert_stride 0 repeats one matrix).
+ * experts        E >= 0.
+ * rows, cols     N and K/32 of each expert's scale matrix, >= 0, below 2^31 - 128.
+ * expert_stride  bytes between consecutive experts, >= 0.
+ * row_stride     bytes between consecutive rows; cols <= row_stride <= 2^24.
+ * out            device pointer, 16-byte aligned, at least
+ *                mx_rearrange_3d_out_bytes(experts, rows, cols) bytes; every
+ *                byte of that range is written, none past it. May be NULL when
+ *                that size is 0. Must not overlap the input.
+ * stream         HIP stream for the single kernel (NULL: the default stream).
+ *
+ * Ownership and errors as for the grouped entry points: nothing is
+ * allocated or kept; an invalid argument returns a negative status
+ * (MX_REARRANGE_ESHAPE for sizes and strides, MX_REARRANGE_ENULL,
+ * MX_REARRANGE_EALIGN) with nothing enqueued.
+ */
+int mx_block_rearrange_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols,
+                          int64_t expert_stride, int64_t row_stride, uint8_t *out,
+                          hipStream_t stream);
+
 /* Static text for a status code returned above. */
 const char *mx_rearrange_strerror(int status);
 

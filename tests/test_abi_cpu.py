@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for want in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups",
-                 "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror"):
+                 "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror",
+                 "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes"):
         assert want in names
 
 
@@ -91,6 +92,42 @@ def test_argument_validation(lib, fn):
         assert f(None, 0, 9, 9, FAKE, 2, None, None) == 0
 
 
+def test_3d_out_bytes_match_oracle(lib):
+    import oracle
+
+    rng = np.random.default_rng(6)
+    shapes = [(0, 0, 0), (1, 1, 1), (16, 8192, 160), (64, 8192, 160), (3, 300, 45), (7, 0, 5), (2, 5, 0)]
+    shapes += [tuple(int(x) for x in rng.integers(0, [70, 5000, 400])) for _ in range(50)]
+    for E, rows, cols in shapes:
+        assert lib.mx_rearrange_3d_out_bytes(E, rows, cols) == oracle.out_bytes_3d(E, rows, cols)
+    assert lib.mx_rearrange_3d_out_bytes(-1, 4, 4) == -1
+    assert lib.mx_rearrange_3d_out_bytes(1, (1 << 31) - 128, 4) == -1
+    assert lib.mx_rearrange_3d_out_bytes(1 << 40, 1 << 20, 1 << 10) == -1   # past int64
+
+
+def test_3d_argument_validation(lib):
+    f = lib.mx_block_rearrange_3d
+    # (scales, E, rows, cols, expert_stride, row_stride, out) -> expected status
+    cases = [
+        ((None, 2, 4, 4, 16, 4, FAKE), -1),          # scales NULL with data
+        ((FAKE, 2, 4, 4, 16, 4, None), -1),          # out NULL with output bytes
+        ((FAKE, -1, 4, 4, 16, 4, FAKE), -2),         # negative experts
+        ((FAKE, 2, -4, 4, 16, 4, FAKE), -2),         # negative rows
+        ((FAKE, 2, 4, -1, 16, 4, FAKE), -2),         # negative cols
+        ((FAKE, 2, 4, 8, 32, 7, FAKE), -2),          # row stride below cols
+        ((FAKE, 2, 4, 8, 32, (1 << 24) + 1, FAKE), -2),  # row stride too large
+        ((FAKE, 2, 4, 8, -32, 8, FAKE), -2),         # negative expert stride
+        ((FAKE, 4, 4, 8, 1 << 62, 8, FAKE), -2),     # expert offsets past int64
+        ((FAKE, 2, 4, 4, 16, 4, FAKE + 4), -4),      # out not 16-byte aligned
+    ]
+    for args, want in cases:
+        assert f(*args, None) == want, args
+    # nothing to write: success without a launch
+    assert f(None, 0, 5, 5, 25, 5, None, None) == 0
+    assert f(None, 3, 0, 5, 0, 5, None, None) == 0
+    assert f(None, 3, 5, 0, 0, 0, None, None) == 0
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5, 7):
         s = lib.mx_rearrange_strerror(code)
@@ -107,6 +144,10 @@ def test_binding_has_no_cpu_path():
         gsf.mx_block_rearrange_M_groups(torch.zeros((4, 4), dtype=torch.uint8), torch.tensor([4], dtype=torch.int32))
     with pytest.raises(TypeError):
         gsf.mx_block_rearrange_K_groups(torch.zeros((4, 4), dtype=torch.int8), torch.tensor([4], dtype=torch.int32))
+    with pytest.raises(ValueError):
+        gsf.mx_block_rearrange_3d(torch.zeros((2, 4, 4), dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        gsf.mx_block_rearrange_3d(torch.zeros((4, 4), dtype=torch.uint8))
 
 
 def test_product_code_never_touches_the_oracle():

@@ -42,11 +42,11 @@ DEFAULT_WORKLOAD = "m_groups_skinny"
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
 # kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
 # 3 = M narrow row segments, 2 = K row segments
-# 4 = per-expert row segments
+# 4 = per-expert row segments, 5 = the same with 512 threads (grids of more than 2048 units)
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
                 "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
-                "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<4>"}
+                "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>"}
 KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 

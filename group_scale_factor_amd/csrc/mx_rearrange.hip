@@ -85,7 +85,10 @@ enum Mode : int {
   kModeMRowsNarrow = 3,  // M groups, one row segment of at most kNarrowUnitCols at a time
   kModeKRows = 2,   // K groups, one row segment at a time
   kMode3d = 4,      // per-expert matrices, one row segment at a time, no group lookup
+  kMode3dWide = 5,  // the same with twice the threads, for grids of several units per CU slot
 };
+
+constexpr bool is_3d(int mode) { return mode == kMode3d || mode == kMode3dWide; }
 
 // Narrow M units (small problems split into many column chunks) get their own
 // instantiation sized for them: fewer loads per lane, fewer registers.
@@ -93,15 +96,21 @@ constexpr int kNarrowUnitCols = 48;
 // Per-expert units span a whole 128-row block of up to 160 columns (the
 // block-32 scales of K = 5120): one contiguous output run per row block.
 constexpr int k3dMaxUnitCols = 160;
-constexpr int threads_for(int mode) { return mode == kModeMFlat ? 128 : 256; }
+// Threads per workgroup, measured per mode: 128 for the small per-unit work of
+// flat strips and narrow chunks, 256 elsewhere; per-expert grids of more than
+// k3dWideUnits units run 512 threads (fewer loads per lane, more units in flight).
+constexpr int threads_for(int mode) {
+  return mode == kModeMFlat || mode == kModeMRowsNarrow ? 128 : mode == kMode3dWide ? 512 : 256;
+}
+constexpr int64_t k3dWideUnits = 2048;
 constexpr int max_unit_cols_for(int mode) {
-  return mode == kModeMRowsNarrow ? kNarrowUnitCols : mode == kMode3d ? k3dMaxUnitCols : kMaxUnitCols;
+  return mode == kModeMRowsNarrow ? kNarrowUnitCols : is_3d(mode) ? k3dMaxUnitCols : kMaxUnitCols;
 }
 constexpr int max_pieces_for(int mode) { return (max_unit_cols_for(mode) + 30) / 16; }
 constexpr int load_policy_for(int mode) {
   return mode == kModeMFlat ? kFlatLoadPolicy
          : mode == kModeKRows ? kKRowsLoadPolicy
-         : mode == kMode3d    ? k3dLoadPolicy
+         : is_3d(mode)        ? k3dLoadPolicy
                               : kMRowsLoadPolicy;
 }
 constexpr int load_iters_for(int mode) {
@@ -116,7 +125,8 @@ constexpr int kMinWavesPerEu = 1;
 static_assert(kMaxUnitCols % 4 == 0 && kMinUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kTileRows * kMaxPitch + kLdsSlack <= 64 * 1024, "LDS per workgroup");
 static_assert(kTileRows * (16 * max_pieces_for(kMode3d) + 4) + kLdsSlack <= 64 * 1024, "LDS per workgroup");
-static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8 && load_iters_for(kMode3d) <= 8,
+static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8 && load_iters_for(kMode3d) <= 8 &&
+                  load_iters_for(kModeMRowsNarrow) <= 8 && load_iters_for(kModeMRows) <= 8,
               "staging unrolled to 8");
 static_assert(k3dMaxUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narrow units");
@@ -486,7 +496,7 @@ void rearrange_kernel(Params p) {
     const int64_t block = unit / p.per_row;             // output row block (M) / 128-row block (K)
     const int slot = int(unit - block * p.per_row);     // column chunk (M) / unit within the row block (K)
 
-    if constexpr (MODE == kMode3d) {
+    if constexpr (is_3d(MODE)) {
       // expert e's row block rb is output row block e*row_blocks + rb; every
       // unit holds data (rows >= 1, and a chunk starts below round_up(cols,4)
       // at a multiple of 4, hence below cols), so the units cover the output
@@ -641,7 +651,8 @@ int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
     ++per_row;
   p.unit_cols = chunk(per_row);
   p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
-  return dispatch(p, kMode3d, blocks * p.per_row, stream);
+  const int64_t units = blocks * p.per_row;
+  return dispatch(p, units > k3dWideUnits ? kMode3dWide : kMode3d, units, stream);
 }
 
 int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
@@ -661,8 +672,9 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
                    : mode == kModeMRows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRows>)
                    : mode == kModeMRowsNarrow ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow>)
                    : mode == kMode3d    ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3d>)
+                   : mode == kMode3dWide ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3dWide>)
                                         : reinterpret_cast<const void *>(&rearrange_kernel<kModeKRows>);
-  const int threads = mode == kModeMFlat ? threads_for(kModeMFlat) : threads_for(kModeMRows);
+  const int threads = threads_for(mode);
   // one workgroup per unit; the grid is a multiple of 8, so a workgroup that
   // loops (only past kMaxGrid units) stays on its XCD
   const int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);

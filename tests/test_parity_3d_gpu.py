@@ -106,7 +106,9 @@ def test_fuzz_strides_and_alignment(env):
 
 def test_wide_rows_and_many_experts(env):
     rng = np.random.default_rng(33)
-    for E, rows, cols in [(1, 256, 1000), (2, 130, 4096), (128, 128, 160), (300, 3, 7), (1, 20000, 12)]:
+    # the last two run more than 2048 units (the 512-thread instantiation), with ragged rows in the last
+    for E, rows, cols in [(1, 256, 1000), (2, 130, 4096), (128, 128, 160), (300, 3, 7), (1, 20000, 12),
+                          (20, 16384, 8), (3, 100001, 45)]:
         run_3d(env, host_experts(rng, E, rows, cols), label="wide")
 
 

@@ -241,12 +241,15 @@ def test_bench_launch_configuration(env):
     import bench
 
     gsf, oracle, torch = env
-    for name in ("m_groups_skinny", "k_groups_large"):
+    for name in ("m_groups_skinny", "k_groups_large", "experts_3d_e64"):
         print("case bench config", name, flush=True)
         job = bench.Job(name, rotate_bytes=0)  # one copy: both launches write the same output
         job.step(0)
         job.step(1)
         torch.cuda.synchronize()
-        want = oracle.rearrange(job.w.kind, job.w.scales, job.w.offs)
+        if job.w.kind == "3d":
+            want = oracle.rearrange_3d(job.w.scales)
+        else:
+            want = oracle.rearrange(job.w.kind, job.w.scales, job.w.offs)
         for k in range(min(2, job.copies)):
             assert np.array_equal(job.outs[k].cpu().numpy(), want)

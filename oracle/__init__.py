@@ -1,12 +1,13 @@
-"""CPU oracle for the grouped MXFP8 scale-factor rearrangement (test infrastructure).
+"""CPU oracle for the grouped MXFP8 scale-factor rearrangement and the MXFP8 dim0 cast (test infrastructure).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package. The HIP library and its Python binding never do, and this package
 imports nothing from them.
 
 The arithmetic lives in ``mx_rearrange_oracle.c``: a plain C loop over groups and
-over every position of each group's padded matrix. This module only compiles it
-with gcc and calls it through ctypes with host numpy arrays.
+over every position of each group's padded matrix, and a plain per-block loop for
+the quantisation (nearest E4M3 code found by trying every code). This module only
+compiles it with gcc and calls it through ctypes with host numpy arrays.
 """
 
 import ctypes
@@ -22,7 +23,7 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 def compile_library(src, dst, verbose=False):
     """Compile one oracle source file into a shared library (plain gcc -O2, one thread)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", dst + ".tmp", src]
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", dst + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -48,6 +49,17 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e8m0_of_amax.argtypes = [ctypes.c_double]
+        lib.oracle_e8m0_of_amax.restype = ctypes.c_int
+        lib.oracle_quantize_dim0.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_quantize_dim0.restype = ctypes.c_int
+        lib.oracle_quantize_dim0_M_groups.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32,
+                                                      ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_quantize_dim0_M_groups.restype = ctypes.c_int
         lib.oracle_3d_out_bytes.argtypes = [i64, i64, i64]
         lib.oracle_3d_out_bytes.restype = i64
         lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
@@ -112,6 +124,50 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return out[:n]
 
+    def quantize_dim0(self, x_bits):
+        """MXFP8 dim0 cast of a host (rows, K) uint16 array of bf16 bit patterns (any row stride).
+
+        Returns (q, scales): q (rows, K) uint8 E4M3 codes, scales (rows, K/32) uint8 E8M0 bytes.
+        """
+        rows, K, ld = self._bf16_shape(x_bits)
+        q = np.empty((rows, K), np.uint8)
+        scales = np.empty((rows, K // 32), np.uint8)
+        rc = self.lib.oracle_quantize_dim0(self._ptr(x_bits), rows, K, ld, q.ctypes.data, scales.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return q, scales
+
+    def quantize_dim0_M_groups(self, x_bits, offs):
+        """dim0 cast whose scales go straight into the M-groups blocked layout.
+
+        Returns (q, blocked): blocked holds out_bytes("M", rows, K/32, G) bytes.
+        """
+        rows, K, ld = self._bf16_shape(x_bits)
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        G = int(offs.shape[0])
+        q = np.empty((rows, K), np.uint8)
+        blocked = np.empty(max(self.out_bytes("M", rows, K // 32, G), 1) if G > 0 else 1, np.uint8)
+        rc = self.lib.oracle_quantize_dim0_M_groups(self._ptr(x_bits), rows, K, ld,
+                                                    offs.ctypes.data if G > 0 else None, G,
+                                                    q.ctypes.data, blocked.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return q, blocked[: self.out_bytes("M", rows, K // 32, G)]
+
+    @staticmethod
+    def _bf16_shape(x_bits):
+        if x_bits.dtype != np.uint16 or x_bits.ndim != 2:
+            raise ValueError("x must be a 2-D uint16 array of bf16 bit patterns")
+        rows, K = x_bits.shape
+        if rows > 0 and K > 1 and x_bits.strides[1] != 2:
+            raise ValueError("x must have unit column stride")
+        ld = x_bits.strides[0] // 2 if rows > 1 else K
+        return rows, K, ld
+
+    @staticmethod
+    def _ptr(a):
+        return a.__array_interface__["data"][0] if a.size > 0 else None
+
 
 _default = None
 
@@ -140,3 +196,11 @@ def out_bytes_3d(experts, rows, cols):
 
 def rearrange_3d(scales, out=None):
     return default().rearrange_3d(scales, out)
+
+
+def quantize_dim0(x_bits):
+    return default().quantize_dim0(x_bits)
+
+
+def quantize_dim0_M_groups(x_bits, offs):
+    return default().quantize_dim0_M_groups(x_bits, offs)

@@ -47,6 +47,8 @@
  */
 
 #include <stdint.h>
+#include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_OK 0
@@ -194,4 +196,123 @@ int oracle_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
         }
     }
     return ORACLE_OK;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * MXFP8 quantisation along rows (dim0 cast) with the scales written straight
+ * into the grouped blocked layout.
+ *
+ * The pages name this step (the dim0 and dim1 casts that produce the scales;
+ * "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by reshaping
+ * to 2d", first notes and Benchmarks tables: activations A of shape
+ * (16640, 5120), blocks of 32) but never state its numerics. Reading taken
+ * here, the shared-scale rule of the OCP Microscaling (MX) v1.0 format for
+ * MXFP8 with E4M3 elements:
+ *   - a block is 32 consecutive elements of one row;
+ *   - its scale is the power of two 2^s with s = floor(log2(amax)) - 8, where
+ *     amax is the largest magnitude in the block and 8 is the exponent of the
+ *     largest E4M3 normal (448 = 1.75 * 2^8); s is clamped to [-127, 127] and
+ *     stored as the E8M0 byte s + 127. An all-zero block gets byte 0 (s = -127);
+ *   - each element becomes the E4M3 (finite, "fn" variant) code nearest to
+ *     x / 2^s, ties to the even code, magnitudes above 448 saturated to 448,
+ *     the sign kept (a negative value that rounds to zero gives -0, code 0x80);
+ *   - a block holding a NaN or an infinity gets the E8M0 NaN byte 0xFF and
+ *     every element of it the E4M3 NaN code 0x7F.
+ * Since a bf16 value has 8 significant bits and the factor is a power of two,
+ * x / 2^s is exact in binary64 and, wherever it is not far below the smallest
+ * E4M3 subnormal, in binary32 as well, so the code chosen does not depend on
+ * the precision the division is carried out in.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Value of a finite E4M3 code: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent field 0 holds the subnormals m/8 * 2^-6. */
+double oracle_e4m3_value(int code) {
+    int sign = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 code to y (finite), ties to the even code, saturating at 448:
+ * every non-negative finite code (0x00 .. 0x7E, increasing in value) is tried. */
+uint8_t oracle_e4m3_encode(double y) {
+    double a = fabs(y);
+    int best = 0;
+    double best_err = fabs(a - oracle_e4m3_value(0));
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(a - oracle_e4m3_value(c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* bf16 is the upper half of a binary32. */
+static double bf16_value(uint16_t bits) {
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* The E8M0 byte of one block's largest magnitude (finite, >= 0). */
+int oracle_e8m0_of_amax(double amax) {
+    if (amax == 0.0) return 0;
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e, 0.5 <= f < 1, so floor(log2(amax)) = e - 1 */
+    int s = (e - 1) - 8;
+    if (s < -127) s = -127;
+    if (s > 127) s = 127;
+    return s + 127;
+}
+
+/* Quantises x (rows x K bf16, row stride ld elements, K a multiple of 32) into
+ * q (rows x K codes, row stride K) and scales (rows x K/32 E8M0 bytes, row-major). */
+int oracle_quantize_dim0(const uint16_t *x, int64_t rows, int64_t K, int64_t ld, uint8_t *q, uint8_t *scales) {
+    if (rows < 0 || K < 0 || K % 32 != 0 || ld < K) return ORACLE_EBADSHAPE;
+    if (rows * K > 0 && (x == 0 || q == 0 || scales == 0)) return ORACLE_EBADPTR;
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const uint16_t *blk = x + i * ld + 32 * b;
+            double amax = 0.0;
+            int finite = 1;
+            for (int k = 0; k < 32; ++k) {
+                double v = bf16_value(blk[k]);
+                if (isnan(v) || isinf(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            uint8_t *qb = q + i * K + 32 * b;
+            if (!finite) {
+                scales[i * (K / 32) + b] = 0xFF;
+                for (int k = 0; k < 32; ++k) qb[k] = 0x7F;
+                continue;
+            }
+            int byte = oracle_e8m0_of_amax(amax);
+            scales[i * (K / 32) + b] = (uint8_t)byte;
+            for (int k = 0; k < 32; ++k) {
+                double y = ldexp(bf16_value(blk[k]), -(byte - 127));
+                if (y > 448.0) y = 448.0;
+                if (y < -448.0) y = -448.0;
+                qb[k] = oracle_e4m3_encode(y);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The dim0 cast followed by the M-groups rearrangement of its scales:
+ * blocked receives oracle_M_groups_out_bytes(rows, K/32, num_groups) bytes. */
+int oracle_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_t ld, const int32_t *offs,
+                                  int32_t num_groups, uint8_t *q, uint8_t *blocked) {
+    if (rows < 0 || K < 0 || K % 32 != 0 || ld < K) return ORACLE_EBADSHAPE;
+    int64_t n = rows * (K / 32);
+    uint8_t *scales = (uint8_t *)malloc(n > 0 ? (size_t)n : 1);
+    if (!scales) return ORACLE_EBADPTR;
+    int rc = oracle_quantize_dim0(x, rows, K, ld, q, scales);
+    if (rc == ORACLE_OK) rc = oracle_M_groups(scales, rows, K / 32, K / 32, offs, num_groups, blocked);
+    free(scales);
+    return rc;
 }

@@ -16,6 +16,8 @@ the same checks also run against deliberately broken copies of the oracle.
 """
 
 import os
+import shutil
+import tempfile
 
 import numpy as np
 
@@ -341,3 +343,218 @@ def random_case_3d(rng, max_experts=5, max_rows=300, max_cols=40):
     ld = cols + int(rng.choice([0, 0, 1, 3, 13]))
     es = rows * ld + int(rng.choice([0, 0, 5, 64]))
     return E, rows, cols, es, ld
+
+
+# --------------------------------------------------------------------------
+# deliberately broken copies of the oracle
+# --------------------------------------------------------------------------
+
+def with_mutant(old, new, fn):
+    """Build a copy of the oracle source with `old` replaced by `new`, call fn(oracle), clean up."""
+    import oracle
+
+    src = open(oracle.SOURCE).read()
+    assert old in src, old
+    tmp = tempfile.mkdtemp()
+    try:
+        path = os.path.join(tmp, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = os.path.join(tmp, "libmutant.so")
+        oracle.compile_library(path, lib)
+        return fn(oracle.Oracle(lib))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+# --------------------------------------------------------------------------
+# MXFP8 dim0 cast
+# --------------------------------------------------------------------------
+
+def load_mxfp8_blocks():
+    """Hand-worked blocks: list of (name, x bits uint16[32], scale byte, codes uint8[32])."""
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "mxfp8_dim0_blocks.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "block":
+                cur = {"name": tok[1], "x": np.zeros(32, np.uint16), "q": np.zeros(32, np.uint8), "scale": None}
+                blocks.append(cur)
+            elif tok[0] == "scale":
+                cur["scale"] = int(tok[1], 16)
+            elif tok[0] == "x":
+                i = int(tok[1])
+                cur["x"][i] = int(tok[2], 16)
+                cur["q"][i] = int(tok[3], 16)
+    for b in blocks:
+        if b["scale"] == 0xFF:   # a non-finite block: every code is NaN, listed or not
+            b["q"][:] = 0x7F
+    return blocks
+
+
+def bf16_bits(values):
+    """bf16 bit patterns of float values that are exactly representable in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    bits = f.view(np.uint32)
+    assert not (bits & 0xFFFF).any(), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def torch_e4m3_values():
+    """Value of every E4M3 code according to torch's float8_e4m3fn (a library routine)."""
+    import torch
+
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def torch_e4m3_encode(values_f32):
+    import torch
+
+    return torch.from_numpy(np.asarray(values_f32, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check_e4m3_table(orc):
+    want = torch_e4m3_values()
+    fails = []
+    for c in range(256):
+        got = orc.lib.oracle_e4m3_value(c)
+        if np.isnan(want[c]):
+            if c & 0x7F != 0x7F:
+                fails.append("torch says code %#x is NaN" % c)
+            continue
+        if got != want[c] or np.signbit(got) != np.signbit(want[c]):
+            fails.append("code %#x: oracle %r, torch %r" % (c, got, want[c]))
+    return fails
+
+
+def e4m3_test_values(rng):
+    """binary32 values in [-448, 448]: every code's value, every midpoint, one binary32 step either side
+    of each midpoint, and log-uniform random values."""
+    vals = torch_e4m3_values()
+    pos = np.unique(vals[(vals >= 0) & np.isfinite(vals)])
+    mids = (pos[1:] + pos[:-1]) / 2
+    mids32 = mids.astype(np.float32)
+    up = np.nextafter(mids32, np.float32(np.inf))
+    down = np.nextafter(mids32, np.float32(-np.inf))
+    rnd = (rng.choice([-1.0, 1.0], 4000) * 2.0 ** rng.uniform(-12, np.log2(448), 4000)).astype(np.float32)
+    v = np.concatenate([pos, mids32, up, down, rnd]).astype(np.float32)
+    v = np.concatenate([v, -v, np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 2.0 ** -11, 2.0 ** -30])])
+    return v[np.abs(v) <= 448]
+
+
+def check_e4m3_encode(orc, rng):
+    v = e4m3_test_values(rng)
+    want = torch_e4m3_encode(v)
+    got = np.array([orc.lib.oracle_e4m3_encode(float(x)) for x in v], np.uint8)
+    bad = np.nonzero(got != want)[0]
+    return ["encode(%r): oracle %#x, torch %#x" % (float(v[i]), got[i], want[i]) for i in bad[:5]]
+
+
+def check_scale_closed_form(orc):
+    """amax = m * 2^k with 1 <= m < 2 gives byte clamp(k - 8, -127, 127) + 127; amax 0 gives 0."""
+    fails = []
+    for k in range(-149, 128):
+        for m in (1.0, 1.5, 1.9921875):
+            amax = m * 2.0 ** k
+            want = min(max(k - 8, -127), 127) + 127
+            if orc.lib.oracle_e8m0_of_amax(amax) != want:
+                fails.append("amax %r: byte %d, want %d" % (amax, orc.lib.oracle_e8m0_of_amax(amax), want))
+    if orc.lib.oracle_e8m0_of_amax(0.0) != 0:
+        fails.append("amax 0 must give byte 0")
+    return fails
+
+
+def check_golden_blocks(orc):
+    fails = []
+    blocks = load_mxfp8_blocks()
+    x = np.stack([b["x"] for b in blocks])
+    q, s = orc.quantize_dim0(x.reshape(1, -1))
+    for i, b in enumerate(blocks):
+        if s[0, i] != b["scale"]:
+            fails.append("%s: scale %#x, want %#x" % (b["name"], s[0, i], b["scale"]))
+        got = q[0, 32 * i: 32 * i + 32]
+        for j in np.nonzero(got != b["q"])[0]:
+            fails.append("%s[%d]: code %#x, want %#x" % (b["name"], j, got[j], b["q"][j]))
+    return fails
+
+
+def random_bf16_rows(rng, rows, K, ld=None, zero_block_p=0.05):
+    """bf16 bit patterns: normal values times 2^U{-40..40} per block, some zero blocks, some -0."""
+    ld = K if ld is None else ld
+    v = rng.standard_normal((rows, ld)).astype(np.float32)
+    v *= (2.0 ** rng.integers(-40, 41, size=(rows, ld // 32 + 1))).repeat(32, axis=1)[:, :ld].astype(np.float32)
+    zb = rng.random((rows, ld // 32 + 1)) < zero_block_p
+    v[zb.repeat(32, axis=1)[:, :ld]] = 0.0
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)   # truncation to bf16
+    bits[rng.random((rows, ld)) < 0.01] = 0x8000
+    return bits[:, :K]
+
+
+def check_round_trip(orc, rng, rows=64, K=256):
+    """Properties of any correct result: the scale puts the block's largest |y| in [256, 512) (unless
+    clamped), every code is within half an E4M3 step of y = x / 2^s (saturated at 448), signs agree."""
+    fails = []
+    x = random_bf16_rows(rng, rows, K)
+    q, s = orc.quantize_dim0(x)
+    xv = bf16_to_f64(x).reshape(rows, K // 32, 32)
+    qv = torch_e4m3_values()[q].reshape(rows, K // 32, 32)
+    sexp = s.astype(np.int64) - 127
+    y = xv / (2.0 ** sexp)[:, :, None]
+    ymax = np.abs(y).max(axis=2)
+    nz = ymax > 0
+    clamped_low = sexp == -127
+    if not np.all(((ymax >= 256) & (ymax < 512)) | ~nz | (clamped_low & (ymax < 256))):
+        fails.append("a block's scale does not put its largest |y| in [256, 512)")
+    if np.any(s[~nz] != 0):
+        fails.append("zero block with non-zero scale")
+    yc = np.clip(y, -448, 448)
+    ay = np.abs(yc)
+    step = 2.0 ** (np.maximum(np.floor(np.log2(np.where(ay > 0, ay, 1.0))), -6) - 3)
+    err = np.abs(qv - yc)
+    if np.any(err > step / 2 + 0.0):
+        i = np.argmax(err - step / 2)
+        fails.append("a code is more than half a step from y (%r vs %r)" % (qv.flat[i], yc.flat[i]))
+    sign_bad = (np.signbit(qv) != np.signbit(y))
+    if np.any(sign_bad):
+        fails.append("%d codes with the wrong sign" % int(sign_bad.sum()))
+    return fails
+
+
+def check_nonfinite(orc):
+    x = np.zeros((1, 96), np.uint16)
+    x[0, :] = bf16_bits([1.0])[0]
+    x[0, 5] = 0x7F80        # +inf in block 0
+    x[0, 40] = 0x7FC1       # NaN in block 1
+    q, s = orc.quantize_dim0(x)
+    fails = []
+    if list(s[0]) != [0xFF, 0xFF, 119]:   # block 2: amax 1.0, s = -8
+        fails.append("scales of non-finite blocks: %s" % list(s[0]))
+    if not (q[0, :64] == 0x7F).all():
+        fails.append("codes of non-finite blocks are not all NaN")
+    if not (q[0, 64:] == 0x78).all():     # 1.0 / 2^-8 = 256 = 2^8: exponent field 15, mantissa 0
+        fails.append("a finite block next to non-finite ones is wrong")
+    return fails
+
+
+def check_blocked_scales(orc, rng):
+    """The blocked scales equal the M-groups layout of the row-major scales, decoded from the tile geometry."""
+    fails = []
+    for rows, K, offs in [(200, 96, [200]), (300, 128, [0, 77, 77, 300]), (5, 32, [2, 5]), (129, 160, [129]),
+                          (260, 64, [1, 130, 259])]:
+        x = random_bf16_rows(rng, rows, K)
+        q, s = orc.quantize_dim0(x)
+        q2, blocked = orc.quantize_dim0_M_groups(x, offs)
+        if not np.array_equal(q, q2):
+            fails.append("codes differ between the two entry points")
+        src = decode_M(rows, K // 32, K // 32, offs, blocked.size)
+        want = np.where(src >= 0, s.reshape(-1)[np.maximum(src, 0)], 0).astype(np.uint8)
+        if not np.array_equal(blocked, want):
+            fails.append("blocked scales rows=%d K=%d offs=%s differ from the decoded layout" % (rows, K, offs))
+    return fails

@@ -8,9 +8,6 @@ Deliberately broken copies of the oracle must fail these same pins.
 """
 
 import itertools
-import os
-import shutil
-import tempfile
 
 import numpy as np
 import pytest
@@ -252,23 +249,11 @@ MUTANTS = {
 }
 
 
-def _build_mutant(tmp, name, old, new):
-    src = open(oracle.SOURCE).read()
-    assert old in src, name
-    path = os.path.join(tmp, "mutant.c")
-    with open(path, "w") as f:
-        f.write(src.replace(old, new))
-    lib = os.path.join(tmp, "libmutant_%d.so" % abs(hash(name)))
-    oracle.compile_library(path, lib)
-    return oracle.Oracle(lib)
-
-
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name):
     old, new = MUTANTS[name]
-    tmp = tempfile.mkdtemp()
-    try:
-        mut = _build_mutant(tmp, name, old, new)
+
+    def all_pins(mut):
         rng = np.random.default_rng(3)
         fails = pins.check_positions(mut)
         fails += pins.check_bandwidth_tables(mut)
@@ -282,6 +267,6 @@ def test_planted_mistake_is_caught(name):
         for _ in range(10):
             fails += pins.check_inverse_3d(mut, *pins.random_case_3d(rng))
         fails += pins.check_3d_reshape(mut, rng)
-        assert fails, "mutant '%s' passed every pin" % name
-    finally:
-        shutil.rmtree(tmp, ignore_errors=True)
+        return fails
+
+    assert pins.with_mutant(old, new, all_pins), "mutant '%s' passed every pin" % name

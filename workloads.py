@@ -15,6 +15,8 @@ The named workloads stand in for the shapes the pages benchmark:
   scales are (16640, 160).
 * The same page's B operand of shape (E, 8192, 5120) for E = 16 and 64: per-expert
   weight scales of shape (E, 8192, 160), one blocked matrix per expert.
+* The same page's activations A of shape (16640, 5120) in bf16, as the input of the
+  MXFP8 dim0 cast whose scales go straight into the M-groups blocked layout.
 * "Add CuTeDSL MXFP8 K-groups scale rearrange kernel", realistic-shapes table:
   M x TotalK = 7168 x 131072 and 28672 x 262144 with 8 groups, group widths drawn
   with a granularity of one scale column (the bench's multiple-of-1 option).
@@ -150,6 +152,54 @@ def experts_3d_e64(seed=8):
                           "3-D expert scales: uint8 (64, 8192, 160)")
 
 
+@dataclass
+class QuantWorkload:
+    """bf16 activations (as uint16 bit patterns) and M-group offsets for the MXFP8 dim0 cast."""
+    name: str
+    rows: int
+    K: int
+    offs: np.ndarray     # int32[G], cumulative group end offsets in rows
+    x: np.ndarray        # uint16[rows, K], bf16 bit patterns, C-contiguous
+    description: str
+    kind: str = "quant"
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.offs.shape[0])
+
+
+def _bf16_activations(rng, rows, K, row_exp, zero_block_p):
+    """Standard normal values times 2^U{-row_exp..row_exp} per row, a fraction of all-zero
+    32-element blocks, truncated to bf16 (the upper 16 bits of each binary32)."""
+    v = rng.standard_normal((rows, K), dtype=np.float32)
+    v *= (2.0 ** rng.integers(-row_exp, row_exp + 1, size=(rows, 1))).astype(np.float32)
+    if zero_block_p > 0:
+        zb = rng.random((rows, K // 32)) < zero_block_p
+        v.reshape(rows, K // 32, 32)[zb] = 0.0
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def quant_m_groups_small(seed=9):
+    """(1000, 640) bf16 activations, 5 groups (one empty, sizes not multiples of 128)."""
+    rng = np.random.default_rng(seed)
+    rows, K = 1000, 640
+    offs = np.array([130, 130, 383, 700, 1000], np.int32)
+    return QuantWorkload("quant_m_groups_small", rows, K, offs, _bf16_activations(rng, rows, K, 20, 0.02),
+                         "MXFP8 dim0 cast: bf16 (1000, 640), 5 groups")
+
+
+def quant_m_groups(seed=10):
+    """(16640, 5120) bf16 activations, 16 expert groups of which 3 are forced empty."""
+    rng = np.random.default_rng(seed)
+    rows, K, G = 16640, 5120, 16
+    empty = rng.choice(G, 3, replace=False)
+    p = np.full(G, 1.0 / (G - 3))
+    p[empty] = 0.0
+    offs = np.cumsum(rng.multinomial(rows, p)).astype(np.int32)
+    return QuantWorkload("quant_m_groups", rows, K, offs, _bf16_activations(rng, rows, K, 8, 0.0),
+                         "MXFP8 dim0 cast: bf16 (16640, 5120), 16 groups, some empty")
+
+
 WORKLOADS = {
     "m_groups_tiny": m_groups_tiny,
     "m_groups_skinny": m_groups_skinny,
@@ -165,9 +215,17 @@ WORKLOADS_3D = {
 }
 
 
+WORKLOADS_QUANT = {
+    "quant_m_groups_small": quant_m_groups_small,
+    "quant_m_groups": quant_m_groups,
+}
+
+
 def make(name: str):
     if name in WORKLOADS_3D:
         return WORKLOADS_3D[name]()
+    if name in WORKLOADS_QUANT:
+        return WORKLOADS_QUANT[name]()
     return WORKLOADS[name]()
 
 

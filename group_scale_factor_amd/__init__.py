@@ -10,6 +10,7 @@ fails loudly when the library has not been built.
     out = mx_block_rearrange_M_groups(scales, group_end_offsets)
     out = mx_block_rearrange_K_groups(scales, group_end_offsets)
     out = mx_block_rearrange_3d(expert_scales)
+    q, blocked_scales = mx_quantize_dim0_M_groups(x_bf16, group_end_offsets)
 
 ``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
 row stride >= cols, any base alignment); ``group_end_offsets`` an int32 CUDA
@@ -17,7 +18,10 @@ tensor of cumulative group ends (rows for M, scale columns for K). The result is
 a flat uint8 tensor of ``*_out_bytes(rows, cols, G)`` bytes holding the blocked
 128x4-tile layout of every group, padding zeroed. ``expert_scales`` is an
 (E, rows, cols) uint8 CUDA tensor with unit column stride (per-expert weight
-scales); every expert becomes its own blocked matrix.
+scales); every expert becomes its own blocked matrix. ``x_bf16`` is a
+(rows, K) torch.bfloat16 CUDA tensor (K a multiple of 32, unit column stride);
+the MXFP8 cast returns its E4M3 codes as a (rows, K) uint8 tensor and its E8M0
+scales already in the M-groups blocked layout.
 """
 
 import ctypes
@@ -51,6 +55,10 @@ def _load():
     lib.mx_rearrange_3d_out_bytes.restype = i64
     lib.mx_block_rearrange_3d.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp]
     lib.mx_block_rearrange_3d.restype = ctypes.c_int
+    lib.mx_quantize_dim0_M_groups_scale_bytes.argtypes = [i64, i64, i32]
+    lib.mx_quantize_dim0_M_groups_scale_bytes.restype = i64
+    lib.mx_quantize_dim0_M_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
+    lib.mx_quantize_dim0_M_groups.restype = ctypes.c_int
     lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
     lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -179,7 +187,58 @@ def mx_block_rearrange_3d(scales, out=None, stream=None):
     return out
 
 
+def mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups):
+    return int(_load().mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups))
+
+
+def mx_quantize_dim0_M_groups(x, group_end_offsets, q=None, scales=None, stream=None):
+    """MXFP8 cast along rows (blocks of 32) with the scales placed in the M-groups blocked layout.
+
+    ``x``: (rows, K) torch.bfloat16 CUDA tensor, unit column stride, 16-byte aligned rows.
+    Returns (q, scales): q a (rows, K) uint8 tensor of E4M3 codes (``q.view(torch.float8_e4m3fn)``
+    reads them as floats), scales the flat uint8 blocked E8M0 output of
+    (rows + 128*G) * round_up(K/32, 4) bytes.
+    """
+    import torch
+
+    lib = _load()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D torch.bfloat16 tensor")
+    if group_end_offsets.dtype != torch.int32 or group_end_offsets.dim() != 1:
+        raise TypeError("group_end_offsets must be a 1-D torch.int32 tensor")
+    if not (x.is_cuda and group_end_offsets.is_cuda) or x.device != group_end_offsets.device:
+        raise ValueError("x and group_end_offsets must be GPU tensors on one device")
+    if not group_end_offsets.is_contiguous():
+        raise ValueError("group_end_offsets must be contiguous")
+    rows, K = x.shape
+    if rows > 0 and K > 1 and x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    row_stride = x.stride(0) if rows > 1 else K
+    G = group_end_offsets.numel()
+    n = int(lib.mx_quantize_dim0_M_groups_scale_bytes(rows, K, G))
+    if n < 0:
+        raise ValueError("invalid sizes rows=%d K=%d num_groups=%d" % (rows, K, G))
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    elif q.dtype != torch.uint8 or q.shape != (rows, K) or not q.is_contiguous() or q.device != x.device:
+        raise ValueError("q must be a contiguous (rows, K) uint8 tensor on x's device")
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.uint8, device=x.device)
+    elif scales.dtype != torch.uint8 or not scales.is_contiguous() or scales.numel() < n or scales.device != x.device:
+        raise ValueError("scales must be a contiguous uint8 tensor of at least %d bytes on x's device" % n)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib.mx_quantize_dim0_M_groups(x.data_ptr() or None, rows, K, row_stride,
+                                       group_end_offsets.data_ptr() or None, G, q.data_ptr() or None,
+                                       scales.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return q, scales
+
+
 __all__ = [
+    "mx_quantize_dim0_M_groups",
+    "mx_quantize_dim0_M_groups_scale_bytes",
     "mx_block_rearrange_3d",
     "mx_rearrange_3d_out_bytes",
     "mx_block_rearrange_M_groups",

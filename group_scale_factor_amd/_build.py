@@ -5,7 +5,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "mx_rearrange.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "mx_rearrange.hip"), os.path.join(PKG, "csrc", "mx_quantize.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmxrearrange.so")
 ARCH = "gfx950"

@@ -1,0 +1,86 @@
+/*
+ * mx_quantize.h — C ABI of the gfx950 MXFP8 dim0 cast whose E8M0 scales are
+ * written straight into the grouped (M groups) blocked scale layout.
+ *
+ * Sources (pytorch/ao pull-request pages):
+ *   "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by reshaping
+ *    to 2d" — first notes and Benchmarks tables: bf16 activations A of shape
+ *    (16640, 5120) are cast to MXFP8 (blocks of 32 elements) before the grouped
+ *    GEMM; the cast produces the E8M0 scales that the blocked layout holds.
+ *   "[mxfp8 moe training] compute prefix sum of group sizes inside kernel intead
+ *    of precomputing" — Context and Changes: the blocked layout of token-group
+ *    scales, groups padded to 128 rows, padded starts computed in the kernel.
+ *
+ * Numerics (the pages do not state them; the OCP Microscaling (MX) v1.0 rule
+ * for MXFP8 with E4M3 elements is the reading implemented):
+ *   - a block is 32 consecutive elements of one row of x;
+ *   - its scale is 2^s with s = floor(log2(max |x|)) - 8, clamped to
+ *     [-127, 127], stored as the E8M0 byte s + 127; an all-zero block gets 0;
+ *   - each element is stored as the E4M3 code (finite variant: 4 exponent bits
+ *     with bias 7, 3 mantissa bits, largest 448, NaN 0x7F) nearest to x / 2^s,
+ *     ties to the even code, saturated at +-448, sign kept;
+ *   - a block holding a NaN or an infinity gets the byte 0xFF and every element
+ *     of it the code 0x7F.
+ *
+ * Scale layout: exactly what mx_block_rearrange_M_groups (mx_rearrange.h)
+ * writes for the row-major (rows, K/32) scale matrix of this cast and the same
+ * group offsets: group g (rows [offs[g-1], offs[g])) padded to a multiple of
+ * 128 rows and K/32 to a multiple of 4 columns, groups stacked, 128x4 tiles,
+ * element (r, c) of a tile at byte (r mod 32)*16 + (r div 32)*4 + c, padding
+ * and the tail of the allocation zero.
+ */
+#ifndef MX_QUANTIZE_H
+#define MX_QUANTIZE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+/*
+ * Bytes of the blocked scale output: (rows + 128*num_groups) * round_up(K/32, 4),
+ * the M-groups output size for a (rows, K/32) scale matrix. -1 for invalid sizes
+ * (negative, K not a multiple of 32, num_groups < 1).
+ */
+int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t num_groups);
+
+/*
+ * x                  device pointer to bf16 values (raw 16-bit patterns), rows x K,
+ *                    row r at x + r*row_stride elements; 16-byte aligned. May be
+ *                    NULL when rows*K == 0. Read only.
+ * rows, K            shape; K a multiple of 32; rows + 128*num_groups < 2^31.
+ * row_stride         elements between rows: K <= row_stride <= 2^26, a multiple of 8
+ *                    (rows start on 16-byte boundaries).
+ * group_end_offsets  device int32[num_groups], cumulative group ends in rows,
+ *                    non-decreasing, the last <= rows (rows past it belong to no
+ *                    group: they are quantised into q, their scales are not
+ *                    placed). Never NULL. Offsets that break this are clamped into
+ *                    [previous end, rows] as in mx_block_rearrange_M_groups.
+ * num_groups         1 <= G <= 4096.
+ * q                  device pointer, 16-byte aligned, rows*K bytes: E4M3 codes,
+ *                    row-major with row stride K. May be NULL when rows*K == 0.
+ * blocked_scales     device pointer, 16-byte aligned, at least
+ *                    mx_quantize_dim0_M_groups_scale_bytes(rows, K, G) bytes; every
+ *                    byte of that range is written, none past it. May be NULL when
+ *                    that size is 0.
+ * stream             HIP stream for the single kernel (NULL: the default stream).
+ *
+ * Ownership: the caller owns every buffer; nothing is allocated or kept.
+ * Errors (negative status, nothing enqueued): MX_REARRANGE_ESHAPE for sizes and
+ * strides, MX_REARRANGE_EGROUPS for num_groups, MX_REARRANGE_ENULL for a missing
+ * pointer, MX_REARRANGE_EALIGN for alignment, MX_REARRANGE_ELAUNCH when the
+ * launch fails (status values and mx_rearrange_strerror in mx_rearrange.h).
+ */
+int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_t row_stride,
+                              const int32_t *group_end_offsets, int32_t num_groups, uint8_t *q,
+                              uint8_t *blocked_scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_QUANTIZE_H */

@@ -57,6 +57,8 @@ class Oracle:
         lib.oracle_e8m0_of_amax.restype = ctypes.c_int
         lib.oracle_quantize_dim0.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_quantize_dim0.restype = ctypes.c_int
+        lib.oracle_scales_dim0.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p]
+        lib.oracle_scales_dim0.restype = ctypes.c_int
         lib.oracle_quantize_dim0_M_groups.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32,
                                                       ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_quantize_dim0_M_groups.restype = ctypes.c_int
@@ -137,6 +139,15 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return q, scales
 
+    def scales_dim0(self, x_bits):
+        """Only the (rows, K/32) E8M0 scale bytes of the dim0 cast."""
+        rows, K, ld = self._bf16_shape(x_bits)
+        scales = np.empty((rows, K // 32), np.uint8)
+        rc = self.lib.oracle_scales_dim0(self._ptr(x_bits), rows, K, ld, scales.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return scales
+
     def quantize_dim0_M_groups(self, x_bits, offs):
         """dim0 cast whose scales go straight into the M-groups blocked layout.
 
@@ -204,3 +215,7 @@ def quantize_dim0(x_bits):
 
 def quantize_dim0_M_groups(x_bits, offs):
     return default().quantize_dim0_M_groups(x_bits, offs)
+
+
+def scales_dim0(x_bits):
+    return default().scales_dim0(x_bits)

@@ -237,11 +237,17 @@ double oracle_e4m3_value(int code) {
 /* Nearest E4M3 code to y (finite), ties to the even code, saturating at 448:
  * every non-negative finite code (0x00 .. 0x7E, increasing in value) is tried. */
 uint8_t oracle_e4m3_encode(double y) {
+    static double value[0x7F];
+    static int filled = 0;
+    if (!filled) {
+        for (int c = 0; c <= 0x7E; ++c) value[c] = oracle_e4m3_value(c);
+        filled = 1;
+    }
     double a = fabs(y);
     int best = 0;
-    double best_err = fabs(a - oracle_e4m3_value(0));
+    double best_err = fabs(a - value[0]);
     for (int c = 1; c <= 0x7E; ++c) {
-        double err = fabs(a - oracle_e4m3_value(c));
+        double err = fabs(a - value[c]);
         if (err < best_err || (err == best_err && (c & 1) == 0)) {
             best = c;
             best_err = err;
@@ -267,6 +273,26 @@ int oracle_e8m0_of_amax(double amax) {
     if (s < -127) s = -127;
     if (s > 127) s = 127;
     return s + 127;
+}
+
+/* The scale bytes alone (rows x K/32, row-major) of the same cast. */
+int oracle_scales_dim0(const uint16_t *x, int64_t rows, int64_t K, int64_t ld, uint8_t *scales) {
+    if (rows < 0 || K < 0 || K % 32 != 0 || ld < K) return ORACLE_EBADSHAPE;
+    if (rows * K > 0 && (x == 0 || scales == 0)) return ORACLE_EBADPTR;
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const uint16_t *blk = x + i * ld + 32 * b;
+            double amax = 0.0;
+            int finite = 1;
+            for (int k = 0; k < 32; ++k) {
+                double v = bf16_value(blk[k]);
+                if (isnan(v) || isinf(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            scales[i * (K / 32) + b] = finite ? (uint8_t)oracle_e8m0_of_amax(amax) : 0xFF;
+        }
+    }
+    return ORACLE_OK;
 }
 
 /* Quantises x (rows x K bf16, row stride ld elements, K a multiple of 32) into

@@ -40,7 +40,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for want in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups",
                  "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror",
-                 "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes"):
+                 "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes",
+                 "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes"):
         assert want in names
 
 
@@ -128,6 +129,40 @@ def test_3d_argument_validation(lib):
     assert f(None, 3, 5, 0, 0, 0, None, None) == 0
 
 
+def test_quantize_sizes_match_oracle(lib):
+    import oracle
+
+    for rows, K, G in [(0, 32, 1), (1, 32, 1), (16640, 5120, 16), (1000, 640, 5), (7, 96, 3), (300, 0, 2)]:
+        assert lib.mx_quantize_dim0_M_groups_scale_bytes(rows, K, G) == oracle.out_bytes("M", rows, K // 32, G)
+    assert lib.mx_quantize_dim0_M_groups_scale_bytes(4, 48, 1) == -1   # K not a multiple of 32
+    assert lib.mx_quantize_dim0_M_groups_scale_bytes(4, 64, 0) == -1
+
+
+def test_quantize_argument_validation(lib):
+    f = lib.mx_quantize_dim0_M_groups
+    A = 0x10000   # 16-byte aligned fake pointer, never dereferenced
+    # (x, rows, K, ld, offs, G, q, scales) -> expected status
+    cases = [
+        ((A, 4, 64, 64, None, 1, A, A), -1),        # offsets NULL
+        ((None, 4, 64, 64, A, 1, A, A), -1),        # x NULL with data
+        ((A, 4, 64, 64, A, 1, None, A), -1),        # q NULL with data
+        ((A, 4, 64, 64, A, 1, A, None), -1),        # scales NULL
+        ((A, 4, 48, 48, A, 1, A, A), -2),           # K not a multiple of 32
+        ((A, 4, 64, 32, A, 1, A, A), -2),           # row stride below K
+        ((A, -1, 64, 64, A, 1, A, A), -2),          # negative rows
+        ((A, 4, 64, (1 << 26) + 8, A, 1, A, A), -2),  # row stride too large
+        ((A, 4, 64, 64, A, 0, A, A), -3),           # no groups
+        ((A, 4, 64, 64, A, 4097, A, A), -3),        # too many groups
+        ((A + 8, 4, 64, 64, A, 1, A, A), -4),       # x not 16-byte aligned
+        ((A, 4, 64, 68, A, 1, A, A), -4),           # row stride not a multiple of 8 elements
+        ((A, 4, 64, 64, A, 1, A + 8, A), -4),       # q not 16-byte aligned
+        ((A, 4, 64, 64, A, 1, A, A + 4), -4),       # scales not 16-byte aligned
+    ]
+    for args, want in cases:
+        assert f(*args, None) == want, args
+    assert f(None, 5, 0, 0, A, 2, None, None, None) == 0   # K = 0: nothing to write
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5, 7):
         s = lib.mx_rearrange_strerror(code)
@@ -148,6 +183,10 @@ def test_binding_has_no_cpu_path():
         gsf.mx_block_rearrange_3d(torch.zeros((2, 4, 4), dtype=torch.uint8))
     with pytest.raises(TypeError):
         gsf.mx_block_rearrange_3d(torch.zeros((4, 4), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        gsf.mx_quantize_dim0_M_groups(torch.zeros((4, 64), dtype=torch.bfloat16), torch.tensor([4], dtype=torch.int32))
+    with pytest.raises(TypeError):
+        gsf.mx_quantize_dim0_M_groups(torch.zeros((4, 64), dtype=torch.float32), torch.tensor([4], dtype=torch.int32))
 
 
 def test_product_code_never_touches_the_oracle():

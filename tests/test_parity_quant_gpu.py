@@ -1,0 +1,231 @@
+"""Parity of the MXFP8 dim0 cast (codes and blocked scales) with the CPU oracle, byte for byte (GPU).
+
+Every case prints its shape before touching the GPU. Both outputs are prefilled
+with 0xAB and followed by guard bytes: every byte must be written, none past it.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+POISON = 0xAB
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    from group_scale_factor_amd import _build
+    import oracle
+
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    if not os.path.exists(oracle.LIBRARY):
+        oracle.build()
+    import group_scale_factor_amd as gsf
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return gsf, oracle, torch
+
+
+def device_bf16(torch, x_bits, ld=None):
+    """Upload (rows, K) bf16 bit patterns as a torch.bfloat16 view with row stride ld elements."""
+    rows, K = x_bits.shape
+    ld = K if ld is None else ld
+    buf = np.zeros((max(rows, 1), ld), np.uint16)
+    buf[:rows, :K] = x_bits
+    t = torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)
+    return t[:rows, :K]
+
+
+def run_quant(env, x_bits, offs, ld=None, label="", want=None):
+    """Runs the GPU cast; compares q and the blocked scales with the oracle (or with `want`)."""
+    gsf, oracle, torch = env
+    rows, K = x_bits.shape
+    offs = np.asarray(offs, np.int32)
+    print("case", label, "rows", rows, "K", K, "ld", ld or K, "G", len(offs), flush=True)
+    if want is None:
+        want = oracle.quantize_dim0_M_groups(x_bits, offs)
+    want_q, want_s = want
+    x = device_bf16(torch, x_bits, ld)
+    n = want_s.size
+    qbuf = torch.full((rows * K + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    q, s = gsf.mx_quantize_dim0_M_groups(x, torch.from_numpy(offs).cuda(), q=qbuf[: rows * K].view(rows, K),
+                                         scales=sbuf[:n])
+    torch.cuda.synchronize()
+    gq, gs = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (gq[rows * K:] == POISON).all(), "%s: bytes past q were written" % label
+    assert (gs[n:] == POISON).all(), "%s: bytes past the scales were written" % label
+    _compare(label + " codes", gq[: rows * K], want_q.reshape(-1))
+    _compare(label + " scales", gs[:n], want_s)
+
+
+def _compare(label, got, want):
+    if not np.array_equal(got, want):
+        bad = np.nonzero(got != want)[0]
+        raise AssertionError("%s: %d of %d bytes differ, first at %d (got %#x want %#x)"
+                             % (label, bad.size, want.size, bad[0], got[bad[0]], want[bad[0]]))
+
+
+def test_workload_small_bit_exact(env):
+    import workloads
+
+    w = workloads.make("quant_m_groups_small")
+    run_quant(env, w.x, w.offs, label=w.name)
+
+
+def test_workload_full_size(env):
+    """(16640, 5120): every scale byte against the oracle; codes on sampled rows (every group's first
+    and last rows and 256 seeded others), computed by the oracle one row at a time."""
+    gsf, oracle, torch = env
+    import workloads
+
+    w = workloads.make("quant_m_groups")
+    print("case quant_m_groups full size", flush=True)
+    x = device_bf16(torch, w.x)
+    q, s = gsf.mx_quantize_dim0_M_groups(x, torch.from_numpy(w.offs).cuda())
+    torch.cuda.synchronize()
+    want_s = oracle.rearrange("M", oracle.scales_dim0(w.x), w.offs)
+    _compare("full-size scales", s.cpu().numpy(), want_s)
+    rng = np.random.default_rng(50)
+    starts = np.concatenate([[0], w.offs[:-1]])
+    rows = set(rng.integers(0, w.rows, 256).tolist())
+    for a, b in zip(starts, w.offs):
+        if b > a:
+            rows.update([int(a), int(b) - 1])
+    rows = np.array(sorted(rows))
+    want_q, _ = oracle.quantize_dim0(np.ascontiguousarray(w.x[rows]))
+    _compare("full-size sampled codes", q.cpu().numpy()[rows].reshape(-1), want_q.reshape(-1))
+
+
+def test_every_scale_and_code(env):
+    """Every scale exponent s in [-127, 119], and for each one every E4M3-relevant y = x / 2^s
+    (1 + m/128) * 2^e, |y| <= 256, e >= -12, both signs, whenever x is exact in bf16; plus
+    blocks whose largest magnitude is each bf16 subnormal."""
+    gsf, oracle, torch = env
+    vals = []
+    ys = np.array([(1 + m / 128.0) * 2.0 ** e for e in range(-12, 8) for m in range(128)] + [256.0])
+    ys = np.concatenate([ys, -ys])
+    for s in range(-127, 120):
+        x = ys * 2.0 ** s
+        x32 = x.astype(np.float32)
+        ok = (x32.astype(np.float64) == x) & ((x32.view(np.uint32) & 0xFFFF) == 0) & (x32 != 0)
+        xs = x32[ok]
+        amax = np.float32(2.0 ** (s + 8))
+        for i in range(0, xs.size, 31):
+            blk = np.zeros(32, np.float32)
+            blk[0] = amax if (i // 31) % 2 == 0 else -amax
+            blk[1: 1 + min(31, xs.size - i)] = xs[i: i + 31]
+            vals.append(blk)
+    sub = np.arange(1, 128, dtype=np.uint32)           # bf16 subnormal magnitudes
+    for m in sub:
+        blk = (np.concatenate([[m], np.arange(32 - 1) % m]) << 16).astype(np.uint32).view(np.float32)
+        vals.append(blk)
+    blocks = np.stack(vals)
+    bits = (blocks.view(np.uint32) >> 16).astype(np.uint16)
+    nb = bits.shape[0]
+    per_row = 16
+    rows = (nb + per_row - 1) // per_row
+    x = np.zeros((rows * per_row, 32), np.uint16)
+    x[:nb] = bits
+    x = x.reshape(rows, per_row * 32)
+    run_quant(env, x, [rows], label="every scale and code")
+
+
+def test_hand_worked_blocks(env):
+    import pins
+
+    blocks = pins.load_mxfp8_blocks()
+    x = np.stack([b["x"] for b in blocks]).reshape(1, -1)
+    x = np.repeat(x, 3, axis=0)
+    q = np.stack([b["q"] for b in blocks]).reshape(1, -1).repeat(3, axis=0)
+    s = np.array([b["scale"] for b in blocks], np.uint8)
+    gsf, oracle, torch = env
+    want = oracle.quantize_dim0_M_groups(x, [3])
+    assert np.array_equal(want[0], q)   # the oracle agrees with the hand-worked values
+    assert np.array_equal(oracle.scales_dim0(x)[0], s)
+    run_quant(env, x, [3], label="hand-worked", want=want)
+
+
+def test_fuzz(env):
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(51)
+    for i in range(60):
+        rows = int(rng.choice([0, 1, 2, 31, 127, 128, 129, 200, 255, 300, 513, 700]))
+        K = 32 * int(rng.choice([1, 2, 3, 4, 5, 7, 15, 16, 17, 31, 33, 50]))
+        ld = K + 8 * int(rng.choice([0, 0, 1, 4, 9]))
+        G = int(rng.choice([1, 2, 3, 8, 16, 63, 64, 65, 80]))
+        offs = workloads.random_offsets(rng, rows, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        x = pins.random_bf16_rows(rng, rows, K) if rows else np.zeros((0, K), np.uint16)
+        if rows and rng.random() < 0.3:   # a few non-finite elements
+            for _ in range(3):
+                x[rng.integers(0, rows), rng.integers(0, K)] = rng.choice([0x7F80, 0xFF80, 0x7FC0])
+        run_quant(env, x, offs, ld=ld, label="fuzz%d" % i)
+
+
+def test_many_groups(env):
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(52)
+    for rows, K, G in [(5000, 64, 4096), (3000, 96, 1000), (64, 32, 4096)]:
+        offs = workloads.random_offsets(rng, rows, G, p_empty=0.5)
+        run_quant(env, pins.random_bf16_rows(rng, rows, K), offs, label="many groups")
+
+
+def test_invalid_offsets_are_clamped(env):
+    import pins
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(53)
+    rows, K = 300, 96
+    x = pins.random_bf16_rows(rng, rows, K)
+    for raw in ([50, 20, 400], [-5, 10, 10**6], [300, 0, 0], [2**31 - 1] * 3, [-(2**31)] * 2):
+        clamped = np.minimum(np.maximum.accumulate(np.maximum(np.array(raw, np.int64), 0)), rows).astype(np.int32)
+        want = oracle.quantize_dim0_M_groups(x, clamped)
+        print("case invalid offsets", raw, flush=True)
+        n = want[1].size
+        sbuf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+        q, _ = gsf.mx_quantize_dim0_M_groups(device_bf16(torch, x), torch.tensor(raw, dtype=torch.int32).cuda(),
+                                             scales=sbuf[:n])
+        torch.cuda.synchronize()
+        got = sbuf.cpu().numpy()
+        assert (got[n:] == POISON).all()
+        _compare("clamped scales", got[:n], want[1])
+        _compare("clamped codes", q.cpu().numpy().reshape(-1), want[0].reshape(-1))
+
+
+def test_empty_shapes(env):
+    gsf, oracle, torch = env
+    run_quant(env, np.zeros((0, 64), np.uint16), [0, 0], label="rows=0")
+    print("case K=0", flush=True)
+    q, s = gsf.mx_quantize_dim0_M_groups(torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda"),
+                                         torch.tensor([5], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert q.numel() == 0 and s.numel() == 0
+
+
+def test_codes_read_back_as_float8(env):
+    """The codes are torch float8_e4m3fn values: dequantised, they lie within half an E4M3 step of x / 2^s."""
+    gsf, oracle, torch = env
+    import workloads
+
+    w = workloads.make("quant_m_groups_small")
+    print("case float8 view", flush=True)
+    q, s = gsf.mx_quantize_dim0_M_groups(device_bf16(torch, w.x), torch.from_numpy(w.offs).cuda())
+    torch.cuda.synchronize()
+    deq = q.view(torch.float8_e4m3fn).to(torch.float64).cpu().numpy()
+    sc = oracle.scales_dim0(w.x).astype(np.int64) - 127
+    y = np.clip((np.asarray(w.x, np.uint32) << 16).view(np.float32).astype(np.float64)
+                / np.repeat(2.0 ** sc, 32, axis=1), -448, 448)
+    ay = np.abs(y)
+    step = 2.0 ** (np.maximum(np.floor(np.log2(np.where(ay > 0, ay, 1.0))), -6) - 3)
+    assert np.all(np.abs(deq - y) <= step / 2)

@@ -81,8 +81,8 @@ MUTANTS = {
     "E8M0 bias 126": ("return s + 127;", "return s + 126;"),
     "ties away from zero": ("if (err < best_err || (err == best_err && (c & 1) == 0)) {",
                             "if (err <= best_err) {"),
-    "truncation instead of rounding": ("double err = fabs(a - oracle_e4m3_value(c));",
-                                       "double err = oracle_e4m3_value(c) <= a ? a - oracle_e4m3_value(c) : 1e300;"),
+    "truncation instead of rounding": ("double err = fabs(a - value[c]);",
+                                       "double err = value[c] <= a ? a - value[c] : 1e300;"),
     "sign dropped": ("return (uint8_t)(best | (signbit(y) ? 0x80 : 0));", "return (uint8_t)best;"),
     "signed maximum instead of magnitude": ("else if (fabs(v) > amax) amax = fabs(v);", "else if (v > amax) amax = v;"),
     "non-finite blocks quantised as finite": ("if (isnan(v) || isinf(v)) finite = 0;\n                else if",

@@ -46,7 +46,8 @@ PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.4
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
                 "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
-                "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>"}
+                "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
+                "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel"}
 KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -61,10 +62,15 @@ def align_up(x, a):
 
 
 def in_bytes_of(w):
+    if w.kind == "quant":
+        return 2 * w.rows * w.K
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
 
 
 def out_bytes_of(lib, w):
+    """Bytes written per launch: the whole output allocation(s)."""
+    if w.kind == "quant":
+        return w.rows * w.K + int(lib.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "3d":
         return int(lib.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
     size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
@@ -90,9 +96,12 @@ class Job:
         self.bytes_per_step = self.in_bytes + self.out_bytes
         self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
         in_pitch = align_up(self.in_bytes, 256)
-        out_pitch = align_up(self.out_bytes, 256)
+        # quant: codes, then the blocked scales from the next 256-byte boundary
+        self.q_pitch = align_up(w.rows * w.K, 256) if w.kind == "quant" else 0
+        out_pitch = align_up(self.out_bytes + self.q_pitch, 256)
         dev = torch.device("cuda")
-        src = torch.from_numpy(np.ascontiguousarray(w.scales).reshape(-1)).to(dev)
+        host = w.x.view(np.uint8) if w.kind == "quant" else w.scales
+        src = torch.from_numpy(np.ascontiguousarray(host).reshape(-1)).to(dev)
         self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
         for k in range(self.copies):
@@ -102,7 +111,7 @@ class Job:
         self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
         self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
-                   "3d": lib.mx_block_rearrange_3d}[w.kind]
+                   "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -115,6 +124,9 @@ class Job:
         if w.kind == "3d":   # experts packed: expert stride rows*cols, row stride cols
             rc = self.fn(self.in_ptrs[k], w.experts, w.rows, w.cols, w.rows * w.cols, w.cols, self.out_ptrs[k],
                          stream or None)
+        elif w.kind == "quant":
+            rc = self.fn(self.in_ptrs[k], w.rows, w.K, w.K, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
+                         self.out_ptrs[k] + self.q_pitch, stream or None)
         else:
             rc = self.fn(self.in_ptrs[k], w.rows, w.cols, w.cols, self.offs.data_ptr(), w.num_groups,
                          self.out_ptrs[k], stream or None)
@@ -166,6 +178,8 @@ def cpu_baseline(name, seconds):
     import workloads
 
     w = workloads.make(name)
+    if w.kind == "quant":
+        return cpu_baseline_quant(w, seconds)
     out = None
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -187,6 +201,33 @@ def cpu_baseline(name, seconds):
         "kind": "oracle",
         "sample": "%d full runs of the %s workload (%s scales, %s) in %.1f s, single-threaded C oracle"
                   % (reps, name, shape, groups, el),
+        "us_per_call": round(el / reps * 1e6, 1),
+    }
+
+
+def cpu_baseline_quant(w, seconds):
+    """The cast oracle on a bounded sample: whole 128-row blocks of the workload's rows, repeated for
+    about `seconds`; bytes as on the GPU (2 per element read, 1 written, plus the sample's scale bytes)."""
+    import oracle
+
+    rows = min(w.rows, 512)
+    x = w.x[:rows]
+    offs = [rows]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        q, blocked = oracle.quantize_dim0_M_groups(x, offs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    bytes_step = 3 * rows * w.K + blocked.size
+    return {
+        "value": round(bytes_step * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d runs over the first %d of the %d rows of the %s workload (K = %d, one group) in %.1f s, "
+                  "single-threaded C oracle" % (reps, rows, w.rows, w.name, w.K, el),
         "us_per_call": round(el / reps * 1e6, 1),
     }
 
@@ -216,8 +257,9 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
 
     w = workloads.make(name)
     copy_bytes = in_bytes_of(w)
-    kfetch, nk = _counter_means(fetch_csv, "FETCH_SIZE", "rearrange_kernel")
-    kwrite, _ = _counter_means(write_csv, "WRITE_SIZE", "rearrange_kernel")
+    kname = KERNEL_NAMES[name].split("<")[0]
+    kfetch, nk = _counter_means(fetch_csv, "FETCH_SIZE", kname)
+    kwrite, _ = _counter_means(write_csv, "WRITE_SIZE", kname)
     cfetch, nc = _counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
     cwrite, _ = _counter_means(copy_write_csv, "WRITE_SIZE", "copyBuffer")
     fetch_scale = copy_bytes / cfetch      # bytes per counter unit
@@ -361,12 +403,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (wall / K * 1e6), 3) if pages_us else None,
-        "dtype": "u8",
+        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind == "quant" else "u8",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "kind": "per-expert" if w.kind == "3d" else "%s-groups" % w.kind,
-            "scales_shape": list(w.scales.shape),
+            "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales"}.get(
+                w.kind, "%s-groups" % w.kind),
+            ("x_shape" if w.kind == "quant" else "scales_shape"):
+                [w.rows, w.K] if w.kind == "quant" else list(w.scales.shape),
             "num_groups": w.experts if w.kind == "3d" else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,

@@ -335,9 +335,10 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
   const int64_t scale_bytes = mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups);
   if (rows * K > 0 && (x == nullptr || q == nullptr)) return MX_REARRANGE_ENULL;
   if (scale_bytes > 0 && blocked_scales == nullptr) return MX_REARRANGE_ENULL;
-  if ((reinterpret_cast<uintptr_t>(x) & 15) || (row_stride & 7) || (reinterpret_cast<uintptr_t>(q) & 15) ||
-      (reinterpret_cast<uintptr_t>(blocked_scales) & 15))
+  // alignment matters only for buffers that are touched
+  if (rows * K > 0 && ((reinterpret_cast<uintptr_t>(x) & 15) || (row_stride & 7) || (reinterpret_cast<uintptr_t>(q) & 15)))
     return MX_REARRANGE_EALIGN;
+  if (scale_bytes > 0 && (reinterpret_cast<uintptr_t>(blocked_scales) & 15)) return MX_REARRANGE_EALIGN;
   if (scale_bytes == 0) return MX_REARRANGE_OK;   // K == 0: nothing to write
 
   QParams p = {};

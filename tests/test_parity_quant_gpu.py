@@ -229,3 +229,20 @@ def test_codes_read_back_as_float8(env):
     ay = np.abs(y)
     step = 2.0 ** (np.maximum(np.floor(np.log2(np.where(ay > 0, ay, 1.0))), -6) - 3)
     assert np.all(np.abs(deq - y) <= step / 2)
+
+
+def test_bench_launch_configuration(env):
+    """The exact launches bench.py times give the oracle's bytes."""
+    import bench
+
+    gsf, oracle, torch = env
+    print("case bench config quant_m_groups_small", flush=True)
+    job = bench.Job("quant_m_groups_small", rotate_bytes=0)
+    job.step(0)
+    job.step(1)
+    torch.cuda.synchronize()
+    w = job.w
+    want_q, want_s = oracle.quantize_dim0_M_groups(w.x, w.offs)
+    out = job.outbuf.cpu().numpy()
+    _compare("bench codes", out[: w.rows * w.K], want_q.reshape(-1))
+    _compare("bench scales", out[job.q_pitch: job.q_pitch + want_s.size], want_s)

@@ -53,7 +53,7 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr int kUnitElems = 512;       // elements per wave-unit: 16 blocks, 4 tile columns of scales
-constexpr int kUnroll = 8;            // units per wave, loads issued back to back
+constexpr int kUnroll = 4;            // units per wave, loads issued back to back (swept: 2..16)
 constexpr int kTileRows = 128;
 constexpr int kMaxGroups = 4096;      // LDS holds two int arrays of this many groups
 constexpr int64_t kMaxRowStride = int64_t(1) << 26;   // elements; keeps unit offsets in 32 bits
@@ -180,11 +180,11 @@ __device__ __forceinline__ int64_t scale_word_offset(int64_t R, int tc, int tile
   return tile * 512 + (r % 32) * 16 + (r / 32) * 4;
 }
 
-// One wave: kUnroll consecutive units starting at unit u0.
-__device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, const int *ends, const int *pends) {
+// One wave's loads: the 16-byte piece of each of kUnroll consecutive units
+// starting at unit u0, out of range (zeros, no memory access) past a row's end
+// or past the last unit.
+__device__ __forceinline__ void load_units(const QParams &p, int64_t u0, uint4 (&v)[kUnroll]) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint4 v[kUnroll];
-  // loads first: each unit's 16-byte piece per lane, out-of-range past the row's end
   {
     int64_t r = u0 / p.chunks;
     int c = int(u0 - r * p.chunks);
@@ -203,6 +203,12 @@ __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, con
       }
     }
   }
+}
+
+// One wave: quantises the kUnroll units loaded by load_units.
+__device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, const uint4 (&v)[kUnroll],
+                                               const int *ends, const int *pends) {
+  const int lane = threadIdx.x & (kWave - 1);
   int64_t r = u0 / p.chunks;
   int c = int(u0 - r * p.chunks);
   int64_t looked_up = -1;
@@ -301,13 +307,18 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   extern __shared__ __align__(16) int lds_groups[];
   int *ends = lds_groups;
   int *pends = lds_groups + p.groups;
-  if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);
-  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   if (int64_t(blockIdx.x) < p.data_groups) {
+    // the data loads go out first; the group scan and the barrier overlap them
     const int64_t u0 = (int64_t(blockIdx.x) * kWavesPerGroup + wave) * kUnroll;
-    if (u0 < p.units) quantize_units(p, u0, ends, pends);
+    uint4 v[kUnroll];
+    load_units(p, u0, v);
+    if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);
+    __syncthreads();
+    if (u0 < p.units) quantize_units(p, u0, v, ends, pends);
   } else {
+    if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);
+    __syncthreads();
     const int64_t ob = int64_t(blockIdx.x) - p.data_groups;
     if (ob < p.pad_blocks) zero_block(p, ob, ends, pends);
   }

@@ -309,8 +309,15 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   int *pends = lds_groups + p.groups;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   if (int64_t(blockIdx.x) < p.data_groups) {
+    // Workgroup b runs on XCD b mod 8: give each XCD one contiguous range of
+    // units, so that the 32 rows whose scale words share a 128-byte line of a
+    // tile are written through one L2 (whole-line write-backs instead of
+    // partial ones from several XCDs).
+    const int64_t n8 = p.data_groups / 8 * 8;
+    const int64_t b = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
+                                              : int64_t(blockIdx.x);
     // the data loads go out first; the group scan and the barrier overlap them
-    const int64_t u0 = (int64_t(blockIdx.x) * kWavesPerGroup + wave) * kUnroll;
+    const int64_t u0 = (b * kWavesPerGroup + wave) * kUnroll;
     uint4 v[kUnroll];
     load_units(p, u0, v);
     if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);

@@ -33,8 +33,9 @@
 //   * Scales: a 16-lane DPP row holds the four blocks of one tile column of its
 //     row; an OR over the row assembles the 4-byte tile word, which one lane
 //     stores at the row's place in its group's padded blocked matrix. The row's
-//     group and the group's padded start come from the end offsets, scanned once
-//     per workgroup into LDS (clamped, prefix maximum, padded prefix sums).
+//     group and the group's padded start come from the end offsets (clamped,
+//     prefix maximum, padded prefix sums), scanned by every wave into two
+//     registers when G <= 64, else once per workgroup into LDS.
 //   * Padding rows of each group's last row block and the tail of the scale
 //     allocation are written with zeros by extra workgroups of the same launch,
 //     one per output row block, so the scale output needs no memset.
@@ -108,42 +109,86 @@ __device__ __forceinline__ int wave_shift_up(int x, int first) {
   return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
 }
 
-// Scans the end offsets into LDS: ends[g] = clamped cumulative end (prefix
-// maximum of clamp(offs[g], 0, rows)), pends[g] = sum over h <= g of
-// round_up(size_h, 128). Run by one wave; the caller synchronises.
-__device__ __forceinline__ void scan_groups(const int32_t *__restrict__ offs, int groups, int rows, int *ends,
-                                            int *pends) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int carry_end = 0, carry_pend = 0;
-  for (int base = 0; base < groups; base += kWave) {
-    const int g = base + lane;
-    int e = g < groups ? offs[g] : 0;
-    e = min(max(e, 0), rows);
-    e = max(wave_inclusive_max(e), carry_end);
-    const int prev = wave_shift_up(e, carry_end);
-    const int padded = g < groups ? (e - prev + kTileRows - 1) / kTileRows * kTileRows : 0;
-    const int pend = wave_inclusive_sum(padded) + carry_pend;
-    if (g < groups) {
-      ends[g] = e;
-      pends[g] = pend;
-    }
-    carry_end = __builtin_amdgcn_readlane(e, kWave - 1);
-    carry_pend = __builtin_amdgcn_readlane(pend, kWave - 1);
-  }
+// One 64-group slice of the end-offset scan: e = clamped cumulative end
+// (prefix maximum of clamp(offs[g], 0, rows), continuing from carry_end),
+// pend = sum over h <= g of round_up(size_h, 128) (continuing from carry_pend).
+__device__ __forceinline__ void scan_slice(const int32_t *__restrict__ offs, int groups, int rows, int base,
+                                           int carry_end, int carry_pend, int &e, int &pend) {
+  const int g = base + int(threadIdx.x & (kWave - 1));
+  e = g < groups ? offs[g] : 0;
+  e = min(max(e, 0), rows);
+  e = max(wave_inclusive_max(e), carry_end);
+  const int prev = wave_shift_up(e, carry_end);
+  const int padded = g < groups ? (e - prev + kTileRows - 1) / kTileRows * kTileRows : 0;
+  pend = wave_inclusive_sum(padded) + carry_pend;
 }
 
-// Number of groups whose value in `arr` is <= key (arr non-decreasing); wave-uniform key.
-__device__ __forceinline__ int count_le(const int *arr, int groups, int64_t key) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int n = 0;
-  for (int base = 0; base < groups; base += kWave) {
-    const bool le = base + lane < groups && int64_t(arr[base + lane]) <= key;
-    const int c = __popcll(__ballot(le));
-    n += c;
-    if (c < kWave) break;
+// The scanned groups: end(g) = clamped cumulative end of group g, pend(g) =
+// padded cumulative end (rows of the blocked scales up to the end of group g).
+// Up to 64 groups they live in two registers of every wave (lane g holds
+// group g) and each wave scans for itself: no LDS, no barrier. Beyond that one
+// wave scans into LDS and the workgroup synchronises.
+template <bool SMALL>
+struct Groups;
+
+template <>
+struct Groups<true> {
+  int groups, e, pend;
+  __device__ __forceinline__ void init(const QParams &p, int *) {
+    groups = p.groups;
+    scan_slice(p.offs, p.groups, p.rows, 0, 0, 0, e, pend);
   }
-  return n;
-}
+  __device__ __forceinline__ int count_ends_le(int64_t key) const {
+    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(e) <= key));
+  }
+  __device__ __forceinline__ int count_pends_le(int64_t key) const {
+    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(pend) <= key));
+  }
+  __device__ __forceinline__ int end(int g) const { return __builtin_amdgcn_readlane(e, g); }
+  __device__ __forceinline__ int pend_at(int g) const { return __builtin_amdgcn_readlane(pend, g); }
+};
+
+template <>
+struct Groups<false> {
+  int groups;
+  const int *ends, *pends;
+  __device__ __forceinline__ void init(const QParams &p, int *lds) {
+    groups = p.groups;
+    int *e_out = lds, *p_out = lds + p.groups;
+    if (threadIdx.x < kWave) {
+      int carry_end = 0, carry_pend = 0;
+      for (int base = 0; base < p.groups; base += kWave) {
+        int e, pend;
+        scan_slice(p.offs, p.groups, p.rows, base, carry_end, carry_pend, e, pend);
+        const int g = base + int(threadIdx.x);
+        if (g < p.groups) {
+          e_out[g] = e;
+          p_out[g] = pend;
+        }
+        carry_end = __builtin_amdgcn_readlane(e, kWave - 1);
+        carry_pend = __builtin_amdgcn_readlane(pend, kWave - 1);
+      }
+    }
+    __syncthreads();
+    ends = e_out;
+    pends = p_out;
+  }
+  // number of entries of arr (non-decreasing) that are <= key
+  __device__ __forceinline__ int count_le(const int *arr, int64_t key) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    int n = 0;
+    for (int base = 0; base < groups; base += kWave) {
+      const int c = __popcll(__ballot(base + lane < groups && int64_t(arr[base + lane]) <= key));
+      n += c;
+      if (c < kWave) break;
+    }
+    return n;
+  }
+  __device__ __forceinline__ int count_ends_le(int64_t key) const { return count_le(ends, key); }
+  __device__ __forceinline__ int count_pends_le(int64_t key) const { return count_le(pends, key); }
+  __device__ __forceinline__ int end(int g) const { return ends[g]; }
+  __device__ __forceinline__ int pend_at(int g) const { return pends[g]; }
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void *base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -206,8 +251,9 @@ __device__ __forceinline__ void load_units(const QParams &p, int64_t u0, uint4 (
 }
 
 // One wave: quantises the kUnroll units loaded by load_units.
+template <class GROUPS>
 __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, const uint4 (&v)[kUnroll],
-                                               const int *ends, const int *pends) {
+                                               const GROUPS &grp) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t r = u0 / p.chunks;
   int c = int(u0 - r * p.chunks);
@@ -249,11 +295,11 @@ __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, con
       word |= dpp<0x118>(word);   // row_shr:8
       if (r != looked_up) {
         looked_up = r;
-        const int g = count_le(ends, p.groups, r);
+        const int g = grp.count_ends_le(r);
         scale_row = -1;
         if (g < p.groups) {
-          const int start = g ? ends[g - 1] : 0;
-          const int pstart = g ? pends[g - 1] : 0;
+          const int start = g ? grp.end(g - 1) : 0;
+          const int pstart = g ? grp.pend_at(g - 1) : 0;
           scale_row = int64_t(pstart) + (r - start);
         }
       }
@@ -272,13 +318,14 @@ __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, con
 
 // Zero-fill of output row block ob of the blocked scales: the padding rows of
 // the group it belongs to, or all of it past the last group.
-__device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const int *ends, const int *pends) {
+template <class GROUPS>
+__device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const GROUPS &grp) {
   const int64_t block_bytes = int64_t(kTileRows) * p.tile_cols * 4;
-  const int g = count_le(pends, p.groups, ob * kTileRows);
+  const int g = grp.count_pends_le(ob * kTileRows);
   if (g < p.groups) {
-    const int start = g ? ends[g - 1] : 0;
-    const int pstart = g ? pends[g - 1] : 0;
-    const int size = ends[g] - start;
+    const int start = g ? grp.end(g - 1) : 0;
+    const int pstart = g ? grp.pend_at(g - 1) : 0;
+    const int size = grp.end(g) - start;
     const int64_t k = ob - pstart / kTileRows;
     const int valid = int(min(int64_t(kTileRows), int64_t(size) - kTileRows * k));
     const int pad_rows = kTileRows - valid;
@@ -290,7 +337,7 @@ __device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const i
       if (off + 4 <= p.scale_bytes) *reinterpret_cast<uint32_t *>(p.scales + off) = 0u;
     }
   } else {
-    const int64_t lo = max(ob * block_bytes, int64_t(pends[p.groups - 1]) * p.tile_cols * 4);
+    const int64_t lo = max(ob * block_bytes, int64_t(grp.pend_at(p.groups - 1)) * p.tile_cols * 4);
     const int64_t hi = min((ob + 1) * block_bytes, p.scale_bytes);
     if (lo >= hi) return;
     // lo is a multiple of 512 (a row block boundary); hi a multiple of 4
@@ -303,11 +350,11 @@ __device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const i
   }
 }
 
+template <bool SMALL>
 __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   extern __shared__ __align__(16) int lds_groups[];
-  int *ends = lds_groups;
-  int *pends = lds_groups + p.groups;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  Groups<SMALL> grp;
   if (int64_t(blockIdx.x) < p.data_groups) {
     // Workgroup b runs on XCD b mod 8: give each XCD one contiguous range of
     // units, so that the 32 rows whose scale words share a 128-byte line of a
@@ -316,18 +363,16 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
     const int64_t n8 = p.data_groups / 8 * 8;
     const int64_t b = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
                                               : int64_t(blockIdx.x);
-    // the data loads go out first; the group scan and the barrier overlap them
+    // the data loads go out first; the group scan overlaps them
     const int64_t u0 = (b * kWavesPerGroup + wave) * kUnroll;
     uint4 v[kUnroll];
     load_units(p, u0, v);
-    if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);
-    __syncthreads();
-    if (u0 < p.units) quantize_units(p, u0, v, ends, pends);
+    grp.init(p, lds_groups);
+    if (u0 < p.units) quantize_units(p, u0, v, grp);
   } else {
-    if (threadIdx.x < kWave) scan_groups(p.offs, p.groups, p.rows, ends, pends);
-    __syncthreads();
+    grp.init(p, lds_groups);
     const int64_t ob = int64_t(blockIdx.x) - p.data_groups;
-    if (ob < p.pad_blocks) zero_block(p, ob, ends, pends);
+    if (ob < p.pad_blocks) zero_block(p, ob, grp);
   }
 }
 
@@ -377,10 +422,12 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
   p.pad_blocks = (rows + kTileRows - 1) / kTileRows + num_groups;
   const int64_t grid = p.data_groups + p.pad_blocks;
   if (grid > lim) return MX_REARRANGE_ESHAPE;
-  const size_t lds = size_t(2) * num_groups * sizeof(int);
+  const bool small = num_groups <= kWave;
+  const size_t lds = small ? 0 : size_t(2) * num_groups * sizeof(int);
+  const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim0_kernel<true>)
+                         : reinterpret_cast<const void *>(&quantize_dim0_kernel<false>);
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&quantize_dim0_kernel), dim3(unsigned(grid)),
-                                       dim3(kThreads), args, lds, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kThreads), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

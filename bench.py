@@ -48,12 +48,17 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rear
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
                 "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel"}
-KERNEL_SOURCE = os.path.join(ROOT, "group_scale_factor_amd", "csrc", "mx_rearrange.hip")
+CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source(name):
+    """The source file of the kernel a workload runs."""
+    return os.path.join(CSRC, "mx_quantize.hip" if name.startswith("quant") else "mx_rearrange.hip")
+
+
+def kernel_source_digest(name):
+    with open(kernel_source(name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -272,7 +277,8 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     d = {
         "workload": name,
         "kernel": KERNEL_NAMES.get(name),
-        "kernel_source_sha256_16": kernel_source_digest(),
+        "kernel_source": os.path.basename(kernel_source(name)),
+        "kernel_source_sha256_16": kernel_source_digest(name),
         "dispatches_averaged": nk,
         "FETCH_SIZE_kib_per_dispatch": round(kfetch, 1),
         "WRITE_SIZE_kib_per_dispatch": round(kwrite, 1),
@@ -301,7 +307,7 @@ def hbm_traffic(name, kind):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != kernel_source_digest():
+    if d.get("kernel_source_sha256_16") != kernel_source_digest(name):
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -62,6 +62,13 @@ class Oracle:
         lib.oracle_quantize_dim0_M_groups.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32,
                                                       ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_quantize_dim0_M_groups.restype = ctypes.c_int
+        lib.oracle_quantize_dim1.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_quantize_dim1.restype = ctypes.c_int
+        lib.oracle_quantize_dim1_K_groups.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32,
+                                                      ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_quantize_dim1_K_groups.restype = ctypes.c_int
+        lib.oracle_scales_dim1.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p]
+        lib.oracle_scales_dim1.restype = ctypes.c_int
         lib.oracle_3d_out_bytes.argtypes = [i64, i64, i64]
         lib.oracle_3d_out_bytes.restype = i64
         lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
@@ -165,6 +172,46 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return q, blocked[: self.out_bytes("M", rows, K // 32, G)]
 
+    def quantize_dim1(self, x_bits):
+        """MXFP8 cast of a host (T, N) bf16 bit-pattern array along T (blocks of 32 tokens).
+
+        Returns (qT, scales): qT (N, T) uint8 codes (transposed), scales (N, T/32) E8M0 bytes.
+        """
+        T, N, ld = self._bf16_shape(x_bits)
+        qT = np.empty((N, T), np.uint8)
+        scales = np.empty((N, T // 32), np.uint8)
+        rc = self.lib.oracle_quantize_dim1(self._ptr(x_bits), T, N, ld, qT.ctypes.data, scales.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return qT, scales
+
+    def scales_dim1(self, x_bits):
+        """Only the (N, T/32) E8M0 scale bytes of the dim1 cast of (T, N) bf16 bit patterns."""
+        T, N, ld = self._bf16_shape(x_bits)
+        scales = np.empty((N, T // 32), np.uint8)
+        rc = self.lib.oracle_scales_dim1(self._ptr(x_bits), T, N, ld, scales.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return scales
+
+    def quantize_dim1_K_groups(self, x_bits, offs):
+        """dim1 cast whose scales go into the K-groups blocked layout; offs are token offsets (int32).
+
+        Returns (qT, blocked): blocked holds out_bytes("K", N, T/32, G) bytes.
+        """
+        T, N, ld = self._bf16_shape(x_bits)
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        G = int(offs.shape[0])
+        qT = np.empty((N, T), np.uint8)
+        n = self.out_bytes("K", N, T // 32, G) if G > 0 else 0
+        blocked = np.empty(max(n, 1), np.uint8)
+        rc = self.lib.oracle_quantize_dim1_K_groups(self._ptr(x_bits), T, N, ld,
+                                                    offs.ctypes.data if G > 0 else None, G,
+                                                    qT.ctypes.data, blocked.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return qT, blocked[:n]
+
     @staticmethod
     def _bf16_shape(x_bits):
         if x_bits.dtype != np.uint16 or x_bits.ndim != 2:
@@ -219,3 +266,15 @@ def quantize_dim0_M_groups(x_bits, offs):
 
 def scales_dim0(x_bits):
     return default().scales_dim0(x_bits)
+
+
+def quantize_dim1(x_bits):
+    return default().quantize_dim1(x_bits)
+
+
+def quantize_dim1_K_groups(x_bits, offs):
+    return default().quantize_dim1_K_groups(x_bits, offs)
+
+
+def scales_dim1(x_bits):
+    return default().scales_dim1(x_bits)

@@ -342,3 +342,108 @@ int oracle_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, in
     free(scales);
     return rc;
 }
+
+/*
+ * MXFP8 cast along the token dimension (dim1 cast) for the weight-gradient
+ * GEMM, whose token groups run along K ("[mxfp8 moe training] use dim1 cast
+ * cuda kernel for 3d weights by reshaping to 2d", first notes: the dim1 cast
+ * writes a column-major result; "Add CuTeDSL MXFP8 K-groups scale rearrange
+ * kernel", review: K offsets are token offsets divided by the block size 32).
+ * x is T x N bf16 (tokens x features, row stride ld elements, T a multiple
+ * of 32). A block is 32 consecutive tokens of one feature column, quantised
+ * by the same rule as above. Codes are written transposed: qT is N x T (row
+ * n holds feature n over all tokens, row stride T), i.e. x's layout read
+ * column-major; scales are N x T/32, row-major.
+ */
+int oracle_quantize_dim1(const uint16_t *x, int64_t T, int64_t N, int64_t ld, uint8_t *qT, uint8_t *scales) {
+    if (T < 0 || N < 0 || T % 32 != 0 || ld < N) return ORACLE_EBADSHAPE;
+    if (T * N > 0 && (x == 0 || qT == 0 || scales == 0)) return ORACLE_EBADPTR;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < T / 32; ++b) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int k = 0; k < 32; ++k) {
+                double v = bf16_value(x[(32 * b + k) * ld + n]);
+                if (isnan(v) || isinf(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            uint8_t *qb = qT + n * T + 32 * b;
+            if (!finite) {
+                scales[n * (T / 32) + b] = 0xFF;
+                for (int k = 0; k < 32; ++k) qb[k] = 0x7F;
+                continue;
+            }
+            int byte = oracle_e8m0_of_amax(amax);
+            scales[n * (T / 32) + b] = (uint8_t)byte;
+            for (int k = 0; k < 32; ++k) {
+                double y = ldexp(bf16_value(x[(32 * b + k) * ld + n]), -(byte - 127));
+                if (y > 448.0) y = 448.0;
+                if (y < -448.0) y = -448.0;
+                qb[k] = oracle_e4m3_encode(y);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The dim1 cast followed by the K-groups rearrangement of its N x T/32 scales,
+ * with group g = scale columns [offs[g-1]/32, offs[g]/32) (token offsets,
+ * integer division): blocked receives oracle_K_groups_out_bytes(N, T/32, G)
+ * bytes. */
+int oracle_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t ld, const int32_t *offs,
+                                  int32_t num_groups, uint8_t *qT, uint8_t *blocked) {
+    if (T < 0 || N < 0 || T % 32 != 0 || ld < N) return ORACLE_EBADSHAPE;
+    if (num_groups < 1) return ORACLE_EBADGROUPS;
+    if (offs == 0) return ORACLE_EBADPTR;
+    int32_t *scale_offs = (int32_t *)malloc((size_t)num_groups * sizeof(int32_t));
+    int64_t n = N * (T / 32);
+    uint8_t *scales = (uint8_t *)malloc(n > 0 ? (size_t)n : 1);
+    int rc = ORACLE_EBADPTR;
+    if (scale_offs && scales) {
+        int32_t prev = 0;
+        rc = ORACLE_OK;
+        for (int32_t g = 0; g < num_groups; ++g) {
+            if (offs[g] < prev || offs[g] > T) rc = ORACLE_EBADOFFSETS;
+            prev = offs[g];
+            scale_offs[g] = offs[g] / 32;
+        }
+        if (rc == ORACLE_OK) rc = oracle_quantize_dim1(x, T, N, ld, qT, scales);
+        if (rc == ORACLE_OK) rc = oracle_K_groups(scales, N, T / 32, T / 32, scale_offs, num_groups, blocked);
+    }
+    free(scale_offs);
+    free(scales);
+    return rc;
+}
+
+/* The scale bytes alone (N x T/32, row-major) of the dim1 cast. The maximum of
+ * each block is accumulated row by row of x (the same maximum, in an order
+ * that reads x sequentially). */
+int oracle_scales_dim1(const uint16_t *x, int64_t T, int64_t N, int64_t ld, uint8_t *scales) {
+    if (T < 0 || N < 0 || T % 32 != 0 || ld < N) return ORACLE_EBADSHAPE;
+    if (T * N > 0 && (x == 0 || scales == 0)) return ORACLE_EBADPTR;
+    double *amax = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    int *finite = (int *)malloc((size_t)(N > 0 ? N : 1) * sizeof(int));
+    if (!amax || !finite) {
+        free(amax);
+        free(finite);
+        return ORACLE_EBADPTR;
+    }
+    for (int64_t b = 0; b < T / 32; ++b) {
+        for (int64_t n = 0; n < N; ++n) {
+            amax[n] = 0.0;
+            finite[n] = 1;
+        }
+        for (int k = 0; k < 32; ++k) {
+            for (int64_t n = 0; n < N; ++n) {
+                double v = bf16_value(x[(32 * b + k) * ld + n]);
+                if (isnan(v) || isinf(v)) finite[n] = 0;
+                else if (fabs(v) > amax[n]) amax[n] = fabs(v);
+            }
+        }
+        for (int64_t n = 0; n < N; ++n)
+            scales[n * (T / 32) + b] = finite[n] ? (uint8_t)oracle_e8m0_of_amax(amax[n]) : 0xFF;
+    }
+    free(amax);
+    free(finite);
+    return ORACLE_OK;
+}

@@ -558,3 +558,36 @@ def check_blocked_scales(orc, rng):
         if not np.array_equal(blocked, want):
             fails.append("blocked scales rows=%d K=%d offs=%s differ from the decoded layout" % (rows, K, offs))
     return fails
+
+
+def check_dim1_transpose(orc, rng):
+    """The dim1 cast of x is the dim0 cast of x transposed (tokens become the blocked dimension)."""
+    fails = []
+    for T, N, pad in [(32, 1, 0), (96, 50, 0), (64, 129, 7), (160, 33, 3), (0, 5, 0)]:
+        base = random_bf16_rows(rng, max(T, 1), N + pad)[:T]
+        x = base[:, :N]
+        qT, s = orc.quantize_dim1(x)
+        q0, s0 = orc.quantize_dim0(np.ascontiguousarray(x.T))
+        if not (np.array_equal(qT, q0) and np.array_equal(s, s0)):
+            fails.append("dim1 of (%d, %d) differs from dim0 of the transpose" % (T, N))
+    return fails
+
+
+def check_dim1_blocked(orc, rng):
+    """dim1 blocked scales: the K-groups layout of the scales, group g = columns [offs[g-1]/32, offs[g]/32)."""
+    fails = []
+    for T, N, offs in [(256, 40, [64, 64, 256]), (320, 130, [32, 288]), (96, 5, [96]), (128, 300, [0, 40, 100, 128]),
+                       (192, 7, [64, 190])]:
+        x = random_bf16_rows(rng, T, N)
+        try:
+            qT, blocked = orc.quantize_dim1_K_groups(x, offs)
+        except ValueError as e:
+            fails.append(repr(e))
+            continue
+        _, s = orc.quantize_dim1(x)
+        scale_offs = [o // 32 for o in offs]
+        src = decode_K(N, T // 32, T // 32, scale_offs, blocked.size)
+        want = np.where(src >= 0, s.reshape(-1)[np.maximum(src, 0)], 0).astype(np.uint8)
+        if blocked.size != orc.out_bytes("K", N, T // 32, len(offs)) or not np.array_equal(blocked, want):
+            fails.append("dim1 blocked scales T=%d N=%d offs=%s differ from the decoded layout" % (T, N, offs))
+    return fails

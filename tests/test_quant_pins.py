@@ -58,6 +58,30 @@ def test_strided_input_equals_packed(orc):
     assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
 
 
+def test_dim1_is_dim0_of_the_transpose(orc):
+    assert pins.check_dim1_transpose(orc, np.random.default_rng(45)) == []
+
+
+def test_dim1_blocked_scales_layout(orc):
+    assert pins.check_dim1_blocked(orc, np.random.default_rng(46)) == []
+
+
+def test_scales_only_functions_agree(orc):
+    rng = np.random.default_rng(47)
+    x = pins.random_bf16_rows(rng, 96, 192)
+    assert np.array_equal(orc.scales_dim0(x), orc.quantize_dim0(x)[1])
+    assert np.array_equal(orc.scales_dim1(x), orc.quantize_dim1(x)[1])
+    x[5, 7] = 0x7F80
+    assert np.array_equal(orc.scales_dim1(x), orc.quantize_dim1(x)[1])
+
+
+def test_dim1_rejects_bad_offsets(orc):
+    x = np.zeros((64, 8), np.uint16)
+    for offs in ([65], [40, 32], [-32, 64]):
+        with pytest.raises(ValueError):
+            orc.quantize_dim1_K_groups(x, offs)
+
+
 def test_rejects_bad_shapes(orc):
     with pytest.raises(ValueError):
         orc.quantize_dim0(np.zeros((4, 48), np.uint16))     # K not a multiple of 32
@@ -87,6 +111,10 @@ MUTANTS = {
     "signed maximum instead of magnitude": ("else if (fabs(v) > amax) amax = fabs(v);", "else if (v > amax) amax = v;"),
     "non-finite blocks quantised as finite": ("if (isnan(v) || isinf(v)) finite = 0;\n                else if",
                                               "if (isnan(v) || isinf(v)) continue;\n                else if"),
+    "dim1 block along the feature dimension": ("x[(32 * b + k) * ld + n]", "x[(32 * b) * ld + n + k]"),
+    "dim1 row stride taken as N": ("x[(32 * b + k) * ld + n]", "x[(32 * b + k) * N + n]"),
+    "dim1 token offsets not divided by 32": ("scale_offs[g] = offs[g] / 32;", "scale_offs[g] = offs[g];"),
+    "dim1 code rows 32 bytes apart": ("uint8_t *qb = qT + n * T + 32 * b;", "uint8_t *qb = qT + n * 32 + 32 * b;"),
     "subnormal exponent field": ("double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);",
                                  "double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -7);"),
 }
@@ -104,6 +132,7 @@ def test_planted_mistake_is_caught(name):
             fails += pins.check_round_trip(mut, rng)
         except (ValueError, IndexError) as e:
             fails.append(repr(e))
+        fails += pins.check_dim1_transpose(mut, rng) + pins.check_dim1_blocked(mut, rng)
         return fails
 
     assert pins.with_mutant(old, new, all_pins), "mutant '%s' passed every pin" % name

@@ -17,6 +17,8 @@ The named workloads stand in for the shapes the pages benchmark:
   weight scales of shape (E, 8192, 160), one blocked matrix per expert.
 * The same page's activations A of shape (16640, 5120) in bf16, as the input of the
   MXFP8 dim0 cast whose scales go straight into the M-groups blocked layout.
+* The dim1 cast of bf16 activations of shape (131072, 7168) (tokens x features), whose
+  scales are the (7168, 4096) K-groups shape below.
 * "Add CuTeDSL MXFP8 K-groups scale rearrange kernel", realistic-shapes table:
   M x TotalK = 7168 x 131072 and 28672 x 262144 with 8 groups, group widths drawn
   with a granularity of one scale column (the bench's multiple-of-1 option).
@@ -154,7 +156,10 @@ def experts_3d_e64(seed=8):
 
 @dataclass
 class QuantWorkload:
-    """bf16 activations (as uint16 bit patterns) and M-group offsets for the MXFP8 dim0 cast."""
+    """bf16 activations (as uint16 bit patterns) and group offsets for an MXFP8 cast.
+
+    kind "quant": dim0 cast, rows x K, offsets in rows (M groups). kind "quant_k": dim1 cast,
+    rows = T tokens x K = N features, offsets in tokens (K groups of the transposed scales)."""
     name: str
     rows: int
     K: int
@@ -200,6 +205,34 @@ def quant_m_groups(seed=10):
                          "MXFP8 dim0 cast: bf16 (16640, 5120), 16 groups, some empty")
 
 
+def _bf16_activations_chunked(rng, rows, K, row_exp, chunk_rows=8192):
+    """As _bf16_activations without zero blocks, drawn in row chunks to bound host memory."""
+    out = np.empty((rows, K), np.uint16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = _bf16_activations(rng, r1 - r0, K, row_exp, 0.0)
+    return out
+
+
+def quant_k_groups_small(seed=11):
+    """(2048, 300) bf16 tokens x features, 5 token groups (ends multiples of 32, one empty, one not)."""
+    rng = np.random.default_rng(seed)
+    T, N = 2048, 300
+    offs = np.array([320, 320, 1056, 1984, 2048], np.int32)
+    return QuantWorkload("quant_k_groups_small", T, N, offs, _bf16_activations(rng, T, N, 20, 0.0),
+                         "MXFP8 dim1 cast: bf16 (2048, 300) tokens x features, 5 token groups", kind="quant_k")
+
+
+def quant_k_groups(seed=12):
+    """(131072, 7168) bf16 tokens x features, 8 token groups whose ends are multiples of 32:
+    the dim1 cast whose scales are the (7168, 4096) K-groups shape."""
+    rng = np.random.default_rng(seed)
+    T, N, G = 131072, 7168, 8
+    offs = (32 * _offsets_from_cuts(_sorted_cuts(rng, T // 32, G - 1), T // 32)).astype(np.int32)
+    return QuantWorkload("quant_k_groups", T, N, offs, _bf16_activations_chunked(rng, T, N, 8),
+                         "MXFP8 dim1 cast: bf16 (131072, 7168) tokens x features, 8 token groups", kind="quant_k")
+
+
 WORKLOADS = {
     "m_groups_tiny": m_groups_tiny,
     "m_groups_skinny": m_groups_skinny,
@@ -218,6 +251,8 @@ WORKLOADS_3D = {
 WORKLOADS_QUANT = {
     "quant_m_groups_small": quant_m_groups_small,
     "quant_m_groups": quant_m_groups,
+    "quant_k_groups_small": quant_k_groups_small,
+    "quant_k_groups": quant_k_groups,
 }
 
 

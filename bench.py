@@ -47,7 +47,8 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rear
                 "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
                 "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
-                "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel"}
+                "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",
+                "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -67,7 +68,7 @@ def align_up(x, a):
 
 
 def in_bytes_of(w):
-    if w.kind == "quant":
+    if w.kind in ("quant", "quant_k"):
         return 2 * w.rows * w.K
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
 
@@ -76,6 +77,8 @@ def out_bytes_of(lib, w):
     """Bytes written per launch: the whole output allocation(s)."""
     if w.kind == "quant":
         return w.rows * w.K + int(lib.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
+    if w.kind == "quant_k":
+        return w.rows * w.K + int(lib.mx_quantize_dim1_K_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "3d":
         return int(lib.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
     size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
@@ -102,10 +105,10 @@ class Job:
         self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
         in_pitch = align_up(self.in_bytes, 256)
         # quant: codes, then the blocked scales from the next 256-byte boundary
-        self.q_pitch = align_up(w.rows * w.K, 256) if w.kind == "quant" else 0
+        self.q_pitch = align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k") else 0
         out_pitch = align_up(self.out_bytes + self.q_pitch, 256)
         dev = torch.device("cuda")
-        host = w.x.view(np.uint8) if w.kind == "quant" else w.scales
+        host = w.x.view(np.uint8) if w.kind in ("quant", "quant_k") else w.scales
         src = torch.from_numpy(np.ascontiguousarray(host).reshape(-1)).to(dev)
         self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
@@ -116,7 +119,8 @@ class Job:
         self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
         self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
-                   "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups}[w.kind]
+                   "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups,
+                   "quant_k": lib.mx_quantize_dim1_K_groups}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -129,7 +133,7 @@ class Job:
         if w.kind == "3d":   # experts packed: expert stride rows*cols, row stride cols
             rc = self.fn(self.in_ptrs[k], w.experts, w.rows, w.cols, w.rows * w.cols, w.cols, self.out_ptrs[k],
                          stream or None)
-        elif w.kind == "quant":
+        elif w.kind in ("quant", "quant_k"):   # rows x K bf16 (quant_k: T tokens x N features)
             rc = self.fn(self.in_ptrs[k], w.rows, w.K, w.K, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
                          self.out_ptrs[k] + self.q_pitch, stream or None)
         else:
@@ -185,6 +189,8 @@ def cpu_baseline(name, seconds):
     w = workloads.make(name)
     if w.kind == "quant":
         return cpu_baseline_quant(w, seconds)
+    if w.kind == "quant_k":
+        return cpu_baseline_quant_k(w, seconds)
     out = None
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -233,6 +239,33 @@ def cpu_baseline_quant(w, seconds):
         "kind": "oracle",
         "sample": "%d runs over the first %d of the %d rows of the %s workload (K = %d, one group) in %.1f s, "
                   "single-threaded C oracle" % (reps, rows, w.rows, w.name, w.K, el),
+        "us_per_call": round(el / reps * 1e6, 1),
+    }
+
+
+def cpu_baseline_quant_k(w, seconds):
+    """The dim1 cast oracle on a bounded sample: the first 64 features over all tokens, one group."""
+    import numpy as np
+
+    import oracle
+
+    cols = min(w.K, 64)
+    x = np.ascontiguousarray(w.x[:, :cols])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        qT, blocked = oracle.quantize_dim1_K_groups(x, [w.rows])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    bytes_step = 3 * w.rows * cols + blocked.size
+    return {
+        "value": round(bytes_step * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d runs over the first %d of the %d features of the %s workload (T = %d tokens, one group) in "
+                  "%.1f s, single-threaded C oracle" % (reps, cols, w.K, w.name, w.rows, el),
         "us_per_call": round(el / reps * 1e6, 1),
     }
 
@@ -409,14 +442,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (wall / K * 1e6), 3) if pages_us else None,
-        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind == "quant" else "u8",
+        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind in ("quant", "quant_k") else "u8",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales"}.get(
+            "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales",
+                     "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales"}.get(
                 w.kind, "%s-groups" % w.kind),
-            ("x_shape" if w.kind == "quant" else "scales_shape"):
-                [w.rows, w.K] if w.kind == "quant" else list(w.scales.shape),
+            ("x_shape" if w.kind in ("quant", "quant_k") else "scales_shape"):
+                [w.rows, w.K] if w.kind in ("quant", "quant_k") else list(w.scales.shape),
             "num_groups": w.experts if w.kind == "3d" else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,

@@ -11,6 +11,7 @@ fails loudly when the library has not been built.
     out = mx_block_rearrange_K_groups(scales, group_end_offsets)
     out = mx_block_rearrange_3d(expert_scales)
     q, blocked_scales = mx_quantize_dim0_M_groups(x_bf16, group_end_offsets)
+    qT, blocked_scales = mx_quantize_dim1_K_groups(x_bf16, token_group_end_offsets)
 
 ``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
 row stride >= cols, any base alignment); ``group_end_offsets`` an int32 CUDA
@@ -59,6 +60,10 @@ def _load():
     lib.mx_quantize_dim0_M_groups_scale_bytes.restype = i64
     lib.mx_quantize_dim0_M_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
     lib.mx_quantize_dim0_M_groups.restype = ctypes.c_int
+    lib.mx_quantize_dim1_K_groups_scale_bytes.argtypes = [i64, i64, i32]
+    lib.mx_quantize_dim1_K_groups_scale_bytes.restype = i64
+    lib.mx_quantize_dim1_K_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
+    lib.mx_quantize_dim1_K_groups.restype = ctypes.c_int
     lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
     lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -236,7 +241,58 @@ def mx_quantize_dim0_M_groups(x, group_end_offsets, q=None, scales=None, stream=
     return q, scales
 
 
+def mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups):
+    return int(_load().mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups))
+
+
+def mx_quantize_dim1_K_groups(x, token_group_end_offsets, qT=None, scales=None, stream=None):
+    """MXFP8 cast along tokens (blocks of 32 tokens per feature) with scales in the K-groups blocked layout.
+
+    ``x``: (T, N) torch.bfloat16 CUDA tensor (tokens x features), T a multiple of 32, unit column
+    stride, 16-byte aligned rows; ``token_group_end_offsets``: int32 cumulative token ends.
+    Returns (qT, scales): qT an (N, T) uint8 tensor of E4M3 codes (x transposed), scales the flat uint8
+    blocked E8M0 output of round_up(N, 128) * (T/32 + 4*G) bytes.
+    """
+    import torch
+
+    lib = _load()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D torch.bfloat16 tensor")
+    offs = token_group_end_offsets
+    if offs.dtype != torch.int32 or offs.dim() != 1:
+        raise TypeError("token_group_end_offsets must be a 1-D torch.int32 tensor")
+    if not (x.is_cuda and offs.is_cuda) or x.device != offs.device:
+        raise ValueError("x and token_group_end_offsets must be GPU tensors on one device")
+    if not offs.is_contiguous():
+        raise ValueError("token_group_end_offsets must be contiguous")
+    T, N = x.shape
+    if T > 0 and N > 1 and x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    row_stride = x.stride(0) if T > 1 else N
+    G = offs.numel()
+    n = int(lib.mx_quantize_dim1_K_groups_scale_bytes(T, N, G))
+    if n < 0:
+        raise ValueError("invalid sizes T=%d N=%d num_groups=%d" % (T, N, G))
+    if qT is None:
+        qT = torch.empty((N, T), dtype=torch.uint8, device=x.device)
+    elif qT.dtype != torch.uint8 or qT.shape != (N, T) or not qT.is_contiguous() or qT.device != x.device:
+        raise ValueError("qT must be a contiguous (N, T) uint8 tensor on x's device")
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.uint8, device=x.device)
+    elif scales.dtype != torch.uint8 or not scales.is_contiguous() or scales.numel() < n or scales.device != x.device:
+        raise ValueError("scales must be a contiguous uint8 tensor of at least %d bytes on x's device" % n)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib.mx_quantize_dim1_K_groups(x.data_ptr() or None, T, N, row_stride, offs.data_ptr() or None, G,
+                                       qT.data_ptr() or None, scales.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return qT, scales
+
+
 __all__ = [
+    "mx_quantize_dim1_K_groups",
+    "mx_quantize_dim1_K_groups_scale_bytes",
     "mx_quantize_dim0_M_groups",
     "mx_quantize_dim0_M_groups_scale_bytes",
     "mx_block_rearrange_3d",

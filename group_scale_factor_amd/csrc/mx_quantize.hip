@@ -376,6 +376,289 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   }
 }
 
+
+// ===========================================================================
+// dim1 cast: blocks of 32 tokens per feature column, codes written transposed,
+// scales placed in the K-groups blocked layout (each token group's scale
+// columns are its own blocked matrix of round_up(N,128) x round_up(w_g,4)).
+//
+// A unit is one tile of output scales: 128 features x one 4-column tile column
+// of one group, i.e. up to 128 tokens of that group (4 blocks) x 128 features.
+// Its input is a 128 x 128 bf16 tile of x (token rows of 256 bytes), staged in
+// LDS; each thread then reads two feature columns of one 32-token block (one
+// dword per token: features 2p and 2p+1), quantises both, writes 32 code bytes
+// into each of the two transposed rows (four lanes write 128 contiguous bytes
+// of a row) and contributes its two scale bytes to the tile words, which a
+// quad assembles with DPP and stores: the unit writes its whole 512-byte tile,
+// padding included. Tokens after the last group are quantised by extra units
+// that place no scales; spare units zero the tail of the scale allocation.
+// ===========================================================================
+
+constexpr bool kDim1Enabled = false;          // see mx_quantize_dim1_K_groups
+constexpr int kTileTok = 128;                 // tokens per unit (4 blocks)
+constexpr int kTileFeat = 128;                // features per unit
+constexpr int kMaxGroupsDim1 = 2048;          // LDS: the staged tile plus 3 ints per group
+constexpr int64_t kMaxRowStrideDim1 = int64_t(1) << 23;   // 128 rows of a unit stay in 32-bit offsets
+// LDS dword offset of token row t of the staged tile: rows 68 dwords apart
+// (64 of data, 4 of skew) plus 16 more per 32-row block, so that the 64 lanes
+// reading one dword of 16 column pairs in 4 blocks hit 64 distinct banks.
+__device__ __forceinline__ int tile_row(int t) { return 68 * t + 16 * (t >> 5); }
+constexpr int kTileDwords = 68 * (kTileTok - 1) + 16 * ((kTileTok - 1) >> 5) + 64;
+
+struct Q1Params {
+  const uint16_t *x;
+  const int32_t *offs;   // token group ends
+  uint8_t *qT;
+  uint8_t *scales;
+  int64_t ld;            // row stride of x in elements
+  int64_t T;             // tokens (multiple of 32)
+  int64_t padded_rows;   // round_up(N, 128)
+  int64_t scale_bytes;   // padded_rows * (T/32 + 4G)
+  int64_t units;         // chunk_units * nb
+  int N;
+  int nb;                // feature blocks of 128
+  int groups;
+};
+
+// Scan of one 64-group slice: e = clamped cumulative end in scale columns,
+// cch = cumulative tile columns (chunks), cw = cumulative padded widths.
+__device__ __forceinline__ void scan_slice_dim1(const Q1Params &p, int base, int carry_e, int carry_ch, int carry_w,
+                                                int &e, int &cch, int &cw) {
+  const int g = base + int(threadIdx.x & (kWave - 1));
+  int64_t et = g < p.groups ? int64_t(p.offs[g]) : 0;
+  et = min(max(et, int64_t(0)), p.T);
+  e = max(wave_inclusive_max(int(et / 32)), carry_e);
+  const int prev = wave_shift_up(e, carry_e);
+  const int w = g < p.groups ? e - prev : 0;
+  const int W = (w + 3) & ~3;
+  cch = wave_inclusive_sum(W / 4) + carry_ch;
+  cw = wave_inclusive_sum(W) + carry_w;
+}
+
+template <bool SMALL>
+struct Groups1;
+
+template <>
+struct Groups1<true> {
+  int groups, e, cch, cw;
+  __device__ __forceinline__ void init(const Q1Params &p, int *) {
+    groups = p.groups;
+    scan_slice_dim1(p, 0, 0, 0, 0, e, cch, cw);
+  }
+  __device__ __forceinline__ int count_cch_le(int64_t key) const {
+    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(cch) <= key));
+  }
+  __device__ __forceinline__ int end(int g) const { return __builtin_amdgcn_readlane(e, g); }
+  __device__ __forceinline__ int chunks_through(int g) const { return __builtin_amdgcn_readlane(cch, g); }
+  __device__ __forceinline__ int width_through(int g) const { return __builtin_amdgcn_readlane(cw, g); }
+};
+
+template <>
+struct Groups1<false> {
+  int groups;
+  const int *es, *cchs, *cws;
+  __device__ __forceinline__ void init(const Q1Params &p, int *lds) {
+    groups = p.groups;
+    int *e_out = lds, *ch_out = lds + p.groups, *w_out = lds + 2 * p.groups;
+    if (threadIdx.x < kWave) {
+      int ce = 0, cc = 0, cwd = 0;
+      for (int base = 0; base < p.groups; base += kWave) {
+        int e, cch, cw;
+        scan_slice_dim1(p, base, ce, cc, cwd, e, cch, cw);
+        const int g = base + int(threadIdx.x);
+        if (g < p.groups) {
+          e_out[g] = e;
+          ch_out[g] = cch;
+          w_out[g] = cw;
+        }
+        ce = __builtin_amdgcn_readlane(e, kWave - 1);
+        cc = __builtin_amdgcn_readlane(cch, kWave - 1);
+        cwd = __builtin_amdgcn_readlane(cw, kWave - 1);
+      }
+    }
+    __syncthreads();
+    es = e_out;
+    cchs = ch_out;
+    cws = w_out;
+  }
+  __device__ __forceinline__ int count_cch_le(int64_t key) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    int n = 0;
+    for (int base = 0; base < groups; base += kWave) {
+      const int c = __popcll(__ballot(base + lane < groups && int64_t(cchs[base + lane]) <= key));
+      n += c;
+      if (c < kWave) break;
+    }
+    return n;
+  }
+  __device__ __forceinline__ int end(int g) const { return es[g]; }
+  __device__ __forceinline__ int chunks_through(int g) const { return cchs[g]; }
+  __device__ __forceinline__ int width_through(int g) const { return cws[g]; }
+};
+
+// 8 bf16 of a staged piece with the features at or past N zeroed (f0 = feature of the first).
+__device__ __forceinline__ uint4 mask_features(uint4 v, int f0, int N) {
+  const int valid = N - f0;
+  if (valid >= 8) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t keep = (2 * k + 1 < valid ? 0xffff0000u : 0u) | (2 * k < valid ? 0x0000ffffu : 0u);
+    w[k] &= keep;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// E8M0 byte and the factor 2^-s of a block whose largest magnitude has binary32 bits m (finite).
+__device__ __forceinline__ int scale_exponent(uint32_t m) {
+  int e;
+  if (m >= 0x00800000u)
+    e = int(m >> 23) - 127;
+  else
+    e = 31 - __builtin_clz(m | 1u) - 149;
+  int s = min(max(e - 8, -127), 127);
+  if (m == 0) s = -127;
+  return s;
+}
+
+template <bool SMALL>
+__global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
+  extern __shared__ __align__(16) int lds1[];
+  uint32_t *tile = reinterpret_cast<uint32_t *>(lds1);
+  int *group_lds = lds1 + kTileDwords;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+
+  // contiguous unit ranges per XCD (workgroup b runs on XCD b mod 8)
+  const int64_t n8 = p.units / 8 * 8;
+  const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
+                                             : int64_t(blockIdx.x);
+  const int64_t ci = u / p.nb;                  // tile column (chunk) index over all groups
+  const int fb = int(u - ci * p.nb);            // feature block
+
+  Groups1<SMALL> grp;
+  grp.init(p, group_lds);
+  const int total_chunks = grp.chunks_through(p.groups - 1);
+  const int last_end = grp.end(p.groups - 1);   // scale columns covered by groups
+  const int64_t cols = p.T / 32;
+  int64_t t0 = 0;          // first token of the unit
+  int ntok = 0;            // tokens of the unit (multiple of 32, <= 128)
+  int64_t tile_off = -1;   // byte offset of the unit's scale tile, -1: no scales
+  if (ci < total_chunks) {
+    const int g = grp.count_cch_le(ci);
+    const int first_chunk = g ? grp.chunks_through(g - 1) : 0;
+    const int k = int(ci - first_chunk);
+    const int S = g ? grp.end(g - 1) : 0;
+    const int w = grp.end(g) - S;
+    const int C = g ? grp.width_through(g - 1) : 0;
+    const int W = (w + 3) & ~3;
+    t0 = 32 * int64_t(S + 4 * k);
+    ntok = 32 * min(4, w - 4 * k);
+    tile_off = p.padded_rows * C + (int64_t(fb) * (W / 4) + k) * 512;
+  } else {
+    const int64_t trailing = (cols - last_end + 3) / 4;   // chunks of tokens after the last group
+    const int64_t c2 = ci - total_chunks;
+    if (c2 < trailing) {
+      t0 = 32 * (last_end + 4 * c2);
+      ntok = int(32 * min(int64_t(4), cols - last_end - 4 * c2));
+    } else {
+      // spare unit: a share of the zero tail of the scale allocation
+      const int64_t spare = (p.units / p.nb - total_chunks - trailing) * p.nb;
+      const int64_t part = (c2 - trailing) * p.nb + fb;
+      const int64_t lo = p.padded_rows * grp.width_through(p.groups - 1);
+      const int64_t len16 = (p.scale_bytes - lo + 15) >> 4;
+      const int64_t per = (len16 + spare - 1) / spare;
+      const int64_t b = lo + 16 * min(per * part, len16);
+      const int64_t e = min(lo + 16 * min(per * (part + 1), len16), p.scale_bytes);
+      const int64_t full = b + ((e - b) & ~int64_t(15));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int64_t a = b + 16 * threadIdx.x; a < full; a += 16 * kThreads) *reinterpret_cast<u32x4 *>(p.scales + a) = z;
+      for (int64_t a = full + 4 * threadIdx.x; a < e; a += 4 * kThreads) *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
+      return;
+    }
+  }
+
+  // stage the 128 x 128 bf16 tile: 16 pieces of 16 bytes per token row, 8 per lane
+  {
+    const int f_base = fb * kTileFeat;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        byte_buffer(p.x + t0 * p.ld + f_base, uint32_t(int64_t(ntok) * p.ld * 2));
+    uint4 v[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int slot = int(threadIdx.x) + it * kThreads;
+      const int t = slot >> 4, k = slot & 15;
+      const bool valid = t < ntok && f_base + 8 * k < p.N;
+      const uint32_t off = valid ? uint32_t(t) * uint32_t(p.ld) * 2u + 16u * uint32_t(k) : kOutOfRange;
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(off), 0, kStreamPolicy);
+      v[it] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int slot = int(threadIdx.x) + it * kThreads;
+      const int t = slot >> 4, k = slot & 15;
+      *reinterpret_cast<uint4 *>(tile + tile_row(t) + 4 * k) = mask_features(v[it], f_base + 8 * k, p.N);
+    }
+  }
+  __syncthreads();
+
+  // quantise two feature columns (2p, 2p+1) of one 32-token block (tb)
+  const int pl = lane >> 2, tb = lane & 3;
+  const int pair = 16 * wave + pl;
+  uint32_t d[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) d[i] = tile[tile_row(32 * tb + i) + pair];
+  uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    m0 = max(m0, mag_lo(d[i]));
+    m1 = max(m1, mag_hi(d[i]));
+  }
+  const bool fin0 = m0 < 0x7f800000u, fin1 = m1 < 0x7f800000u;
+  const int s0 = scale_exponent(m0), s1 = scale_exponent(m1);
+  const float f0 = __uint_as_float(uint32_t(127 - s0) << 23), f1 = __uint_as_float(uint32_t(127 - s1) << 23);
+  uint32_t c0[8], c1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c0[j] = fin0 ? e4m3x4(clamp448(bf16_lo(d[4 * j]) * f0), clamp448(bf16_lo(d[4 * j + 1]) * f0),
+                          clamp448(bf16_lo(d[4 * j + 2]) * f0), clamp448(bf16_lo(d[4 * j + 3]) * f0))
+                 : kE4m3Nan;
+    c1[j] = fin1 ? e4m3x4(clamp448(bf16_hi(d[4 * j]) * f1), clamp448(bf16_hi(d[4 * j + 1]) * f1),
+                          clamp448(bf16_hi(d[4 * j + 2]) * f1), clamp448(bf16_hi(d[4 * j + 3]) * f1))
+                 : kE4m3Nan;
+  }
+  const int n0 = fb * kTileFeat + 2 * pair;
+  if (32 * tb < ntok) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t col = t0 + 32 * tb;
+    if (n0 < p.N) {
+      uint8_t *dst = p.qT + int64_t(n0) * p.T + col;
+      __builtin_nontemporal_store(u32x4{c0[0], c0[1], c0[2], c0[3]}, reinterpret_cast<u32x4 *>(dst));
+      __builtin_nontemporal_store(u32x4{c0[4], c0[5], c0[6], c0[7]}, reinterpret_cast<u32x4 *>(dst + 16));
+    }
+    if (n0 + 1 < p.N) {
+      uint8_t *dst = p.qT + int64_t(n0 + 1) * p.T + col;
+      __builtin_nontemporal_store(u32x4{c1[0], c1[1], c1[2], c1[3]}, reinterpret_cast<u32x4 *>(dst));
+      __builtin_nontemporal_store(u32x4{c1[4], c1[5], c1[6], c1[7]}, reinterpret_cast<u32x4 *>(dst + 16));
+    }
+  }
+  if (tile_off >= 0) {
+    // tile words of features 2p and 2p+1: byte tb of each comes from lane 4p+tb
+    const uint32_t b0 = fin0 ? uint32_t(s0 + 127) : 0xffu, b1 = fin1 ? uint32_t(s1 + 127) : 0xffu;
+    int w0 = int(b0 << (8 * tb)), w1 = int(b1 << (8 * tb));
+    w0 |= __builtin_amdgcn_update_dpp(0, w0, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    w0 |= __builtin_amdgcn_update_dpp(0, w0, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    w1 |= __builtin_amdgcn_update_dpp(0, w1, 0xb1, 0xf, 0xf, false);
+    w1 |= __builtin_amdgcn_update_dpp(0, w1, 0x4e, 0xf, 0xf, false);
+    const int r = 2 * pair + (tb & 1);          // tile row written by this lane (lanes tb = 0, 1)
+    if (tb < 2) {
+      const int64_t off = tile_off + (r % 32) * 16 + (r / 32) * 4;
+      *reinterpret_cast<uint32_t *>(p.scales + off) = uint32_t(tb == 0 ? w0 : w1);
+    }
+  }
+}
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
@@ -428,6 +711,56 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
                          : reinterpret_cast<const void *>(&quantize_dim0_kernel<false>);
   void *args[] = {&p};
   const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kThreads), args, lds, stream);
+  return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
+}
+
+
+int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_groups) {
+  if (T < 0 || N < 0 || T % 32 != 0 || num_groups < 1) return -1;
+  return round_up(N, 128) * (T / 32 + 4 * int64_t(num_groups));
+}
+
+int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t row_stride,
+                              const int32_t *token_group_end_offsets, int32_t num_groups, uint8_t *qT,
+                              uint8_t *blocked_scales, hipStream_t stream) {
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (T < 0 || N < 0 || T % 32 != 0 || row_stride < N || row_stride > kMaxRowStrideDim1) return MX_REARRANGE_ESHAPE;
+  if (num_groups < 1 || num_groups > kMaxGroupsDim1) return MX_REARRANGE_EGROUPS;
+  if (T > lim || N > lim - 128 || T / 32 + 4 * int64_t(num_groups) > lim) return MX_REARRANGE_ESHAPE;
+  if (token_group_end_offsets == nullptr) return MX_REARRANGE_ENULL;
+  const int64_t scale_bytes = mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups);
+  if (T * N > 0 && (x == nullptr || qT == nullptr)) return MX_REARRANGE_ENULL;
+  if (scale_bytes > 0 && blocked_scales == nullptr) return MX_REARRANGE_ENULL;
+  if (T * N > 0 && ((reinterpret_cast<uintptr_t>(x) & 15) || (row_stride & 7) || (reinterpret_cast<uintptr_t>(qT) & 15)))
+    return MX_REARRANGE_EALIGN;
+  if (scale_bytes > 0 && (reinterpret_cast<uintptr_t>(blocked_scales) & 15)) return MX_REARRANGE_EALIGN;
+  if (scale_bytes == 0) return MX_REARRANGE_OK;   // N == 0: nothing to write
+
+  Q1Params p = {};
+  p.x = x;
+  p.offs = token_group_end_offsets;
+  p.qT = qT;
+  p.scales = blocked_scales;
+  p.ld = row_stride;
+  p.T = T;
+  p.N = int(N);
+  p.nb = int((N + kTileFeat - 1) / kTileFeat);
+  p.groups = num_groups;
+  p.padded_rows = round_up(N, 128);
+  p.scale_bytes = scale_bytes;
+  // tile columns: every group's plus the trailing tokens' plus at least one spare
+  const int64_t chunk_units = (T + kTileTok - 1) / kTileTok + num_groups + 1;
+  p.units = chunk_units * p.nb;
+  if (p.units > lim) return MX_REARRANGE_ESHAPE;
+  // Switched off: the kernel below raised a GPU memory fault whose cause has not
+  // been found; nothing is launched until it is.
+  if (!kDim1Enabled) return MX_REARRANGE_EUNAVAILABLE;
+  const bool small = num_groups <= kWave;
+  const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * num_groups * sizeof(int));
+  const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)
+                         : reinterpret_cast<const void *>(&quantize_dim1_kernel<false>);
+  void *args[] = {&p};
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(kThreads), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

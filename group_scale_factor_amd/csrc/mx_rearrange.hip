@@ -731,6 +731,7 @@ const char *mx_rearrange_strerror(int status) {
     case MX_REARRANGE_EGROUPS: return "num_groups must be >= 1";
     case MX_REARRANGE_EALIGN: return "out must be 16-byte aligned";
     case MX_REARRANGE_ELAUNCH: return "HIP kernel launch failed";
+    case MX_REARRANGE_EUNAVAILABLE: return "entry point switched off";
     default: return "unknown status";
   }
 }

@@ -1,6 +1,7 @@
 /*
- * mx_quantize.h — C ABI of the gfx950 MXFP8 dim0 cast whose E8M0 scales are
- * written straight into the grouped (M groups) blocked scale layout.
+ * mx_quantize.h — C ABI of the gfx950 MXFP8 casts whose E8M0 scales are written
+ * straight into the grouped blocked scale layouts: the dim0 cast for M groups
+ * and the dim1 cast for K groups.
  *
  * Sources (pytorch/ao pull-request pages):
  *   "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by reshaping
@@ -77,6 +78,64 @@ int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t n
  */
 int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_t row_stride,
                               const int32_t *group_end_offsets, int32_t num_groups, uint8_t *q,
+                              uint8_t *blocked_scales, hipStream_t stream);
+
+/*
+ * MXFP8 cast along the token dimension (dim1 cast) for the weight-gradient GEMM,
+ * whose token groups run along K.
+ *
+ * Sources: "[mxfp8 moe training] use dim1 cast cuda kernel for 3d weights by
+ * reshaping to 2d" — first notes: the dim1 cast quantises along the other
+ * dimension and writes a column-major result; "Add CuTeDSL MXFP8 K-groups scale
+ * rearrange kernel" — review notes: K-group offsets are token offsets divided
+ * by the block size 32, group widths padded to 4 scale columns, empty groups
+ * add nothing; "[mxfp8 moe training] add bench script for scale conversion to
+ * blocked format kernels for groups along K" — the K-groups scale shape
+ * (7168, 4096) of 131072 tokens.
+ *
+ * x is T x N (tokens x features) bf16; a block is 32 consecutive tokens of one
+ * feature, quantised by the rule above. Codes are written transposed: qT is
+ * N x T bytes, row n = feature n over all tokens (x's layout read column-major).
+ * The N x T/32 scales go into the K-groups layout of mx_block_rearrange_K_groups
+ * with scale-column offsets token_group_end_offsets[g] / 32 (integer division):
+ * group g is its own blocked matrix of round_up(N,128) rows and
+ * round_up(w_g,4) columns, stored from byte round_up(N,128) * (sum of the
+ * earlier padded widths); padding and the tail are zero.
+ *
+ * Scale bytes: round_up(N, 128) * (T/32 + 4*num_groups); -1 for invalid sizes
+ * (negative, T not a multiple of 32, num_groups < 1).
+ */
+int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_groups);
+
+/*
+ * x                        device bf16 bit patterns, T x N, row t at x + t*row_stride
+ *                          elements; 16-byte aligned; NULL allowed when T*N == 0.
+ * T, N                     T a multiple of 32; N + 128 < 2^31.
+ * row_stride               N <= row_stride <= 2^23 elements, a multiple of 8.
+ * token_group_end_offsets  device int32[num_groups], cumulative token ends,
+ *                          non-decreasing, the last <= T; each a multiple of 32
+ *                          for groups to own whole blocks (otherwise the scale
+ *                          columns follow the integer division). Tokens past the
+ *                          last end are quantised into qT without placed scales.
+ *                          Offsets that break the order are clamped into
+ *                          [previous end, T]. Never NULL.
+ * num_groups               1 <= G <= 2048.
+ * qT                       device, 16-byte aligned, N*T bytes of E4M3 codes (row
+ *                          stride T); NULL allowed when T*N == 0.
+ * blocked_scales           device, 16-byte aligned, at least
+ *                          mx_quantize_dim1_K_groups_scale_bytes(T, N, G) bytes, all
+ *                          written, none past it; NULL allowed when that is 0.
+ * stream                   HIP stream for the single kernel.
+ * Ownership and status codes as for mx_quantize_dim0_M_groups.
+ *
+ * Status: switched off. After validating its arguments (and returning
+ * MX_REARRANGE_OK when there is nothing to write) the call returns
+ * MX_REARRANGE_EUNAVAILABLE and enqueues nothing: its kernel raised a GPU
+ * memory fault on gfx950 whose cause has not been found yet. The oracle of
+ * this cast and its pins are in place.
+ */
+int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t row_stride,
+                              const int32_t *token_group_end_offsets, int32_t num_groups, uint8_t *qT,
                               uint8_t *blocked_scales, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -93,6 +93,7 @@ typedef struct ihipStream_t *hipStream_t;
 #define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 */
 #define MX_REARRANGE_EALIGN (-4)       /* out is not 16-byte aligned */
 #define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
+#define MX_REARRANGE_EUNAVAILABLE (-6) /* the entry point is switched off (see its declaration) */
 
 /*
  * Output size in bytes for groups along M: (rows + 128*num_groups) *

@@ -41,7 +41,8 @@ def test_header_declares_entry_points():
     for want in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups",
                  "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror",
                  "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes",
-                 "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes"):
+                 "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes",
+                 "mx_quantize_dim1_K_groups", "mx_quantize_dim1_K_groups_scale_bytes"):
         assert want in names
 
 
@@ -163,8 +164,38 @@ def test_quantize_argument_validation(lib):
     assert f(None, 5, 0, 0, A, 2, None, None, None) == 0   # K = 0: nothing to write
 
 
+def test_quantize_dim1_sizes_and_validation(lib):
+    import oracle
+
+    for T, N, G in [(0, 5, 1), (32, 1, 1), (131072, 7168, 8), (2048, 300, 5), (96, 0, 2)]:
+        assert lib.mx_quantize_dim1_K_groups_scale_bytes(T, N, G) == oracle.out_bytes("K", N, T // 32, G)
+    assert lib.mx_quantize_dim1_K_groups_scale_bytes(48, 4, 1) == -1
+    f = lib.mx_quantize_dim1_K_groups
+    A = 0x10000
+    cases = [
+        ((A, 64, 8, 8, None, 1, A, A), -1),          # offsets NULL
+        ((None, 64, 8, 8, A, 1, A, A), -1),          # x NULL
+        ((A, 64, 8, 8, A, 1, None, A), -1),          # qT NULL
+        ((A, 64, 8, 8, A, 1, A, None), -1),          # scales NULL
+        ((A, 48, 8, 8, A, 1, A, A), -2),             # T not a multiple of 32
+        ((A, 64, 8, 4, A, 1, A, A), -2),             # row stride below N
+        ((A, 64, 8, (1 << 23) + 8, A, 1, A, A), -2),  # row stride too large
+        ((A, 64, 8, 8, A, 0, A, A), -3),             # no groups
+        ((A, 64, 8, 8, A, 2049, A, A), -3),          # too many groups
+        ((A + 8, 64, 8, 8, A, 1, A, A), -4),         # x misaligned
+        ((A, 64, 8, 12, A, 1, A, A), -4),            # row stride not a multiple of 8
+        ((A, 64, 8, 8, A, 1, A + 4, A), -4),         # qT misaligned
+        ((A, 64, 8, 8, A, 1, A, A + 4), -4),         # scales misaligned
+    ]
+    for args, want in cases:
+        assert f(*args, None) == want, args
+    assert f(None, 64, 0, 0, A, 2, None, None, None) == 0   # N = 0: nothing to write
+    # switched off: valid arguments return MX_REARRANGE_EUNAVAILABLE before any HIP call
+    assert f(A, 64, 8, 8, A, 1, A, A, None) == -6
+
+
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         s = lib.mx_rearrange_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 

@@ -246,3 +246,193 @@ def test_bench_launch_configuration(env):
     out = job.outbuf.cpu().numpy()
     _compare("bench codes", out[: w.rows * w.K], want_q.reshape(-1))
     _compare("bench scales", out[job.q_pitch: job.q_pitch + want_s.size], want_s)
+
+
+# --------------------------------------------------------------------------
+# dim1 cast: blocks of 32 tokens, codes transposed, K-groups blocked scales
+# --------------------------------------------------------------------------
+
+DIM1_OFF = pytest.mark.skip(reason="mx_quantize_dim1_K_groups is switched off: its kernel raised a GPU memory "
+                                   "fault whose cause has not been found; it returns MX_REARRANGE_EUNAVAILABLE")
+
+def run_dim1(env, x_bits, offs, ld=None, label="", want=None):
+    gsf, oracle, torch = env
+    T, N = x_bits.shape
+    offs = np.asarray(offs, np.int32)
+    print("case dim1", label, "T", T, "N", N, "ld", ld or N, "G", len(offs), flush=True)
+    if want is None:
+        want = oracle.quantize_dim1_K_groups(x_bits, offs)
+    want_q, want_s = want
+    x = device_bf16(torch, x_bits, ld)
+    n = want_s.size
+    qbuf = torch.full((N * T + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    gsf.mx_quantize_dim1_K_groups(x, torch.from_numpy(offs).cuda(), qT=qbuf[: N * T].view(N, T), scales=sbuf[:n])
+    torch.cuda.synchronize()
+    gq, gs = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (gq[N * T:] == POISON).all(), "%s: bytes past qT were written" % label
+    assert (gs[n:] == POISON).all(), "%s: bytes past the scales were written" % label
+    _compare(label + " codes", gq[: N * T], want_q.reshape(-1))
+    _compare(label + " scales", gs[:n], want_s)
+
+
+def _ld8(N, extra=0):
+    return (N + 7) // 8 * 8 + 8 * extra
+
+
+@DIM1_OFF
+def test_dim1_workload_small(env):
+    import workloads
+
+    w = workloads.make("quant_k_groups_small")
+    run_dim1(env, w.x, w.offs, ld=_ld8(w.K), label=w.name)
+
+
+@DIM1_OFF
+def test_dim1_workload_full_size(env):
+    """(131072, 7168): every scale byte; codes of 48 sampled feature columns (the first and last of each
+    128-feature block among them), computed by the oracle on those columns."""
+    gsf, oracle, torch = env
+    import workloads
+
+    w = workloads.make("quant_k_groups")
+    print("case dim1 quant_k_groups full size", flush=True)
+    x = device_bf16(torch, w.x)
+    qT, s = gsf.mx_quantize_dim1_K_groups(x, torch.from_numpy(w.offs).cuda())
+    torch.cuda.synchronize()
+    del x
+    want_s = oracle.rearrange("K", oracle.scales_dim1(w.x), w.offs // 32)
+    _compare("dim1 full-size scales", s.cpu().numpy(), want_s)
+    rng = np.random.default_rng(60)
+    cols = np.unique(np.concatenate([rng.integers(0, w.K, 40), [0, 127, 128, 4095, 7040, w.K - 1]]))
+    want_q, _ = oracle.quantize_dim1(np.ascontiguousarray(w.x[:, cols]))
+    got = qT[torch.from_numpy(cols).cuda()].cpu().numpy()
+    _compare("dim1 full-size sampled codes", got.reshape(-1), want_q.reshape(-1))
+
+
+@DIM1_OFF
+def test_dim1_hand_worked_blocks(env):
+    import pins
+
+    gsf, oracle, torch = env
+    blocks = pins.load_mxfp8_blocks()
+    col = np.concatenate([b["x"] for b in blocks])            # one feature: the blocks one after another in tokens
+    x = np.stack([col, col[::-1].copy(), col], axis=1)          # (T, 3)
+    T = x.shape[0]
+    want = oracle.quantize_dim1_K_groups(x, [T])
+    codes = np.concatenate([b["q"] for b in blocks])
+    assert np.array_equal(want[0][0], codes) and np.array_equal(want[0][2], codes)
+    run_dim1(env, x, [T], ld=8, label="hand-worked", want=want)
+
+
+@DIM1_OFF
+def test_dim1_every_scale_and_code(env):
+    """The exhaustive value set of the dim0 sweep, one 32-token block per feature column."""
+    vals = []
+    ys = np.array([(1 + m / 128.0) * 2.0 ** e for e in range(-12, 8) for m in range(128)] + [256.0])
+    ys = np.concatenate([ys, -ys])
+    for s in range(-127, 120, 3):
+        x = ys * 2.0 ** s
+        x32 = x.astype(np.float32)
+        ok = (x32.astype(np.float64) == x) & ((x32.view(np.uint32) & 0xFFFF) == 0) & (x32 != 0)
+        xs = x32[ok]
+        for i in range(0, xs.size, 31):
+            blk = np.zeros(32, np.float32)
+            blk[0] = np.float32(2.0 ** (s + 8))
+            blk[1: 1 + min(31, xs.size - i)] = xs[i: i + 31]
+            vals.append(blk)
+    bits = (np.stack(vals).view(np.uint32) >> 16).astype(np.uint16)   # (blocks, 32)
+    x = np.ascontiguousarray(bits.T)                                     # (32 tokens, features)
+    run_dim1(env, x, [32], ld=_ld8(x.shape[1]), label="every scale and code")
+
+
+@DIM1_OFF
+def test_dim1_fuzz(env):
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(61)
+    for i in range(50):
+        T = 32 * int(rng.choice([0, 1, 2, 3, 4, 5, 7, 8, 13, 40]))
+        N = int(rng.choice([1, 2, 7, 8, 127, 128, 129, 300, 513]))
+        ld = _ld8(N, int(rng.choice([0, 0, 1, 5])))
+        G = int(rng.choice([1, 2, 3, 8, 16, 63, 64, 65, 80]))
+        offs = 32 * workloads.random_offsets(rng, T // 32, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                             short_total=bool(rng.random() < 0.3))
+        x = pins.random_bf16_rows(rng, max(T, 1), N)[:T] if T else np.zeros((0, N), np.uint16)
+        if T and rng.random() < 0.3:
+            for _ in range(3):
+                x[rng.integers(0, T), rng.integers(0, N)] = rng.choice([0x7F80, 0xFF80, 0x7FC0])
+        run_dim1(env, x, offs.astype(np.int32), ld=ld, label="fuzz%d" % i)
+
+
+@DIM1_OFF
+def test_dim1_offsets_not_multiples_of_32(env):
+    import pins
+
+    rng = np.random.default_rng(62)
+    x = pins.random_bf16_rows(rng, 320, 70)
+    for offs in ([33, 100, 320], [31, 31, 290], [1, 2, 3, 300]):
+        run_dim1(env, x, offs, ld=72, label="offsets %s" % offs)
+
+
+@DIM1_OFF
+def test_dim1_many_groups(env):
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(63)
+    for T, N, G in [(32 * 300, 40, 2048), (32 * 100, 130, 100)]:
+        offs = 32 * workloads.random_offsets(rng, T // 32, G, p_empty=0.5)
+        run_dim1(env, pins.random_bf16_rows(rng, T, N), offs.astype(np.int32), ld=_ld8(N), label="many groups")
+
+
+@DIM1_OFF
+def test_dim1_invalid_offsets_are_clamped(env):
+    import pins
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(64)
+    T, N = 320, 96
+    x = pins.random_bf16_rows(rng, T, N)
+    for raw in ([64, 32, 400], [-32, 96, 10**6], [320, 0, 0], [2**31 - 1] * 3, [-(2**31)] * 2):
+        clamped = np.minimum(np.maximum.accumulate(np.maximum(np.array(raw, np.int64), 0)), T).astype(np.int32)
+        want = oracle.quantize_dim1_K_groups(x, clamped)
+        print("case dim1 invalid offsets", raw, flush=True)
+        n = want[1].size
+        sbuf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+        qT, _ = gsf.mx_quantize_dim1_K_groups(device_bf16(torch, x), torch.tensor(raw, dtype=torch.int32).cuda(),
+                                              scales=sbuf[:n])
+        torch.cuda.synchronize()
+        got = sbuf.cpu().numpy()
+        assert (got[n:] == POISON).all()
+        _compare("dim1 clamped scales", got[:n], want[1])
+        _compare("dim1 clamped codes", qT.cpu().numpy().reshape(-1), want[0].reshape(-1))
+
+
+@DIM1_OFF
+def test_dim1_empty_shapes(env):
+    gsf, oracle, torch = env
+    run_dim1(env, np.zeros((0, 40), np.uint16), [0, 0], ld=40, label="T=0")
+    print("case dim1 N=0", flush=True)
+    qT, s = gsf.mx_quantize_dim1_K_groups(torch.zeros((64, 0), dtype=torch.bfloat16, device="cuda"),
+                                          torch.tensor([64], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert qT.numel() == 0 and s.numel() == 0
+
+
+@DIM1_OFF
+def test_dim1_bench_launch_configuration(env):
+    import bench
+
+    gsf, oracle, torch = env
+    print("case bench config quant_k_groups_small", flush=True)
+    job = bench.Job("quant_k_groups_small", rotate_bytes=0)
+    job.step(0)
+    job.step(1)
+    torch.cuda.synchronize()
+    w = job.w
+    want_q, want_s = oracle.quantize_dim1_K_groups(w.x, w.offs)
+    out = job.outbuf.cpu().numpy()
+    _compare("dim1 bench codes", out[: w.rows * w.K], want_q.reshape(-1))
+    _compare("dim1 bench scales", out[job.q_pitch: job.q_pitch + want_s.size], want_s)

@@ -215,12 +215,12 @@ def _bf16_activations_chunked(rng, rows, K, row_exp, chunk_rows=8192):
 
 
 def quant_k_groups_small(seed=11):
-    """(2048, 300) bf16 tokens x features, 5 token groups (ends multiples of 32, one empty, one not)."""
+    """(2048, 312) bf16 tokens x features, 5 token groups (ends multiples of 32, one empty)."""
     rng = np.random.default_rng(seed)
-    T, N = 2048, 300
+    T, N = 2048, 312
     offs = np.array([320, 320, 1056, 1984, 2048], np.int32)
     return QuantWorkload("quant_k_groups_small", T, N, offs, _bf16_activations(rng, T, N, 20, 0.0),
-                         "MXFP8 dim1 cast: bf16 (2048, 300) tokens x features, 5 token groups", kind="quant_k")
+                         "MXFP8 dim1 cast: bf16 (2048, 312) tokens x features, 5 token groups", kind="quant_k")
 
 
 def quant_k_groups(seed=12):

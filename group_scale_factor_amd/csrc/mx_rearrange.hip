@@ -723,17 +723,4 @@ int mx_block_rearrange_3d(const uint8_t *scales, int64_t experts, int64_t rows, 
   return launch_3d(scales, experts, rows, cols, expert_stride, row_stride, out, stream);
 }
 
-const char *mx_rearrange_strerror(int status) {
-  switch (status) {
-    case MX_REARRANGE_OK: return "success";
-    case MX_REARRANGE_ENULL: return "a required pointer is NULL";
-    case MX_REARRANGE_ESHAPE: return "invalid shape: rows/cols negative or too large, or row_stride outside [cols, 2^24]";
-    case MX_REARRANGE_EGROUPS: return "num_groups must be >= 1";
-    case MX_REARRANGE_EALIGN: return "out must be 16-byte aligned";
-    case MX_REARRANGE_ELAUNCH: return "HIP kernel launch failed";
-    case MX_REARRANGE_EUNAVAILABLE: return "entry point switched off";
-    default: return "unknown status";
-  }
-}
-
 }  // extern "C"

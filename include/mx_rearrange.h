@@ -89,9 +89,9 @@ typedef struct ihipStream_t *hipStream_t;
 
 #define MX_REARRANGE_OK 0
 #define MX_REARRANGE_ENULL (-1)        /* a required pointer is NULL */
-#define MX_REARRANGE_ESHAPE (-2)       /* rows/cols negative or too large, or row_stride outside [cols, 2^24] */
-#define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 */
-#define MX_REARRANGE_EALIGN (-4)       /* out is not 16-byte aligned */
+#define MX_REARRANGE_ESHAPE (-2)       /* a size negative or too large, or a row stride out of its range */
+#define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 (or above the cap of a cast) */
+#define MX_REARRANGE_EALIGN (-4)       /* a buffer (or row stride) not aligned as required */
 #define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
 #define MX_REARRANGE_EUNAVAILABLE (-6) /* the entry point is switched off (see its declaration) */
 

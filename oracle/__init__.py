@@ -69,6 +69,12 @@ class Oracle:
         lib.oracle_quantize_dim1_K_groups.restype = ctypes.c_int
         lib.oracle_scales_dim1.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p]
         lib.oracle_scales_dim1.restype = ctypes.c_int
+        lib.oracle_pad_M_groups_out_rows.argtypes = [i64, i32]
+        lib.oracle_pad_M_groups_out_rows.restype = i64
+        lib.oracle_pad_M_groups.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p]
+        lib.oracle_pad_M_groups.restype = ctypes.c_int
+        lib.oracle_unpad_M_groups.argtypes = [ctypes.c_void_p, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p, i64]
+        lib.oracle_unpad_M_groups.restype = ctypes.c_int
         lib.oracle_3d_out_bytes.argtypes = [i64, i64, i64]
         lib.oracle_3d_out_bytes.restype = i64
         lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
@@ -212,6 +218,40 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return qT, blocked[:n]
 
+    def pad_M_groups(self, data, offs):
+        """Per-group row padding of a host (rows, cols) uint8 matrix (any row stride).
+
+        Returns the (rows + 128*G, cols) padded matrix (row stride cols)."""
+        if data.dtype != np.uint8 or data.ndim != 2:
+            raise ValueError("data must be a 2-D uint8 array")
+        rows, cols = data.shape
+        if rows > 0 and cols > 1 and data.strides[1] != 1:
+            raise ValueError("data must have unit column stride")
+        ld = data.strides[0] if rows > 1 else cols
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        G = int(offs.shape[0])
+        out_rows = int(self.lib.oracle_pad_M_groups_out_rows(rows, G))
+        padded = np.empty((max(out_rows, 0), cols), np.uint8)
+        rc = self.lib.oracle_pad_M_groups(self._ptr(data), rows, cols, max(ld, cols), offs.ctypes.data if G else None,
+                                          G, padded.ctypes.data if padded.size else None)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return padded
+
+    def unpad_M_groups(self, padded, rows, offs):
+        """Inverse of pad_M_groups: (rows, cols) from the (rows + 128*G, cols) padded matrix."""
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        G = int(offs.shape[0])
+        cols = padded.shape[1]
+        if padded.shape[0] != int(self.lib.oracle_pad_M_groups_out_rows(rows, G)) or not padded.flags.c_contiguous:
+            raise ValueError("padded must be a contiguous (rows + 128*G, cols) array")
+        data = np.empty((rows, cols), np.uint8)
+        rc = self.lib.oracle_unpad_M_groups(self._ptr(padded), rows, cols, offs.ctypes.data if G else None, G,
+                                            data.ctypes.data if data.size else None, cols)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return data
+
     @staticmethod
     def _bf16_shape(x_bits):
         if x_bits.dtype != np.uint16 or x_bits.ndim != 2:
@@ -278,3 +318,11 @@ def quantize_dim1_K_groups(x_bits, offs):
 
 def scales_dim1(x_bits):
     return default().scales_dim1(x_bits)
+
+
+def pad_M_groups(data, offs):
+    return default().pad_M_groups(data, offs)
+
+
+def unpad_M_groups(padded, rows, offs):
+    return default().unpad_M_groups(padded, rows, offs)

@@ -447,3 +447,56 @@ int oracle_scales_dim1(const uint16_t *x, int64_t T, int64_t N, int64_t ld, uint
     free(finite);
     return ORACLE_OK;
 }
+
+/*
+ * Per-group padding of MXFP8 data rows ("Add CuTeDSL MXFP8 K-groups scale
+ * rearrange kernel", its stack lists MXFP8 pad/unpad kernels by title only).
+ * Reading taken here: pad places group g's rows (input rows [offs[g-1],
+ * offs[g]) of a rows x cols byte matrix, row stride ld) at output rows
+ * [P_g, P_g + size_g), P_g = sum over h < g of round_up(size_h, 128) — the
+ * row placement of the M-groups scale layout, so that data rows line up with
+ * their padded scale rows; every other byte of the (rows + 128*G) x cols
+ * output (row stride cols) is zero. unpad is the inverse: output row r of
+ * group g (row stride ld, cols bytes written per row) is padded row
+ * P_g + (r - offs[g-1]); rows past the last end are zero.
+ */
+int64_t oracle_pad_M_groups_out_rows(int64_t rows, int32_t num_groups) {
+    return rows + 128 * (int64_t)num_groups;
+}
+
+int oracle_pad_M_groups(const uint8_t *data, int64_t rows, int64_t cols, int64_t ld, const int32_t *offs,
+                        int32_t num_groups, uint8_t *padded) {
+    int rc = check_args(data, rows, cols, ld, offs, num_groups, padded,
+                        oracle_pad_M_groups_out_rows(rows, num_groups) * cols, rows);
+    if (rc != ORACLE_OK) return rc;
+    int64_t total = oracle_pad_M_groups_out_rows(rows, num_groups) * cols;
+    if (total > 0) memset(padded, 0, (size_t)total);
+    int64_t out_row = 0, start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t size = offs[g] - start;
+        for (int64_t i = 0; i < size; ++i)
+            for (int64_t j = 0; j < cols; ++j) padded[(out_row + i) * cols + j] = data[(start + i) * ld + j];
+        out_row += round_up(size, 128);
+        start = offs[g];
+    }
+    return ORACLE_OK;
+}
+
+int oracle_unpad_M_groups(const uint8_t *padded, int64_t rows, int64_t cols, const int32_t *offs, int32_t num_groups,
+                          uint8_t *data, int64_t ld) {
+    int64_t in_total = oracle_pad_M_groups_out_rows(rows, num_groups) * cols;
+    int rc = check_args(padded, rows, cols, ld, offs, num_groups, data, rows * cols, rows);
+    if (rc != ORACLE_OK) return rc;
+    if (padded == 0 && in_total > 0) return ORACLE_EBADPTR;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) data[r * ld + j] = 0;
+    int64_t in_row = 0, start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t size = offs[g] - start;
+        for (int64_t i = 0; i < size; ++i)
+            for (int64_t j = 0; j < cols; ++j) data[(start + i) * ld + j] = padded[(in_row + i) * cols + j];
+        in_row += round_up(size, 128);
+        start = offs[g];
+    }
+    return ORACLE_OK;
+}

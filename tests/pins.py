@@ -591,3 +591,54 @@ def check_dim1_blocked(orc, rng):
         if blocked.size != orc.out_bytes("K", N, T // 32, len(offs)) or not np.array_equal(blocked, want):
             fails.append("dim1 blocked scales T=%d N=%d offs=%s differ from the decoded layout" % (T, N, offs))
     return fails
+
+
+# --------------------------------------------------------------------------
+# per-group row padding of data
+# --------------------------------------------------------------------------
+
+def m_layout_row_sources(orc, rows, offs):
+    """For each output row of the M-groups layout, the input row it holds (or -1), measured by running
+    the M-groups scale oracle on a one-column index-coded matrix and reading rows off the tile geometry."""
+    n = orc.out_bytes("M", rows, 1, len(offs))
+    src = source_map(orc, "M", rows, 1, 1, offs)          # linear index = row (ld = 1)
+    b = np.arange(n, dtype=np.int64)
+    t, r, c = _tile_coords(b)
+    out_row = t * 128 + r                                  # one tile column: tile index = row block
+    sources = np.full(n // 4, -1, dtype=np.int64)
+    hit = (c == 0) & (src >= 0)
+    sources[out_row[hit]] = src[hit]
+    return sources
+
+
+def check_pad_placement(orc, rng):
+    fails = []
+    for rows, cols, offs in [(6, 3, [2, 2, 6]), (300, 5, [0, 129, 129, 250]), (129, 16, [129]), (0, 4, [0, 0]),
+                             (257, 7, [1, 2, 3, 257])]:
+        data = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+        padded = orc.pad_M_groups(data, offs)
+        sources = m_layout_row_sources(orc, rows, offs)
+        want = np.zeros_like(padded)
+        for R, s in enumerate(sources):
+            if s >= 0:
+                want[R] = data[s]
+        if padded.shape[0] != rows + 128 * len(offs) or not np.array_equal(padded, want):
+            fails.append("pad rows=%d cols=%d offs=%s: rows not where the M-groups layout puts them" % (rows, cols, offs))
+    return fails
+
+
+def check_unpad_round_trip(orc, rng):
+    from workloads import random_offsets
+
+    fails = []
+    for _ in range(30):
+        rows = int(rng.integers(0, 400))
+        cols = int(rng.integers(1, 40))
+        G = int(rng.integers(1, 8))
+        offs = random_offsets(rng, rows, G, p_empty=0.3, short_total=bool(rng.random() < 0.3))
+        data = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+        back = orc.unpad_M_groups(orc.pad_M_groups(data, offs), rows, offs)
+        end = int(offs[-1]) if len(offs) else 0
+        if not (np.array_equal(back[:end], data[:end]) and not back[end:].any()):
+            fails.append("unpad(pad(x)) != x for rows=%d offs=%s" % (rows, list(offs)))
+    return fails

@@ -48,13 +48,16 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rear
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
                 "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",
-                "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel"}
+                "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",
+                "pad_m_groups_small": "pad_kernel<true, true, true>", "pad_m_groups": "pad_kernel<true, true, true>"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source(name):
     """The source file of the kernel a workload runs."""
+    if name.startswith("pad"):
+        return os.path.join(CSRC, "mx_pad.hip")
     return os.path.join(CSRC, "mx_quantize.hip" if name.startswith("quant") else "mx_rearrange.hip")
 
 
@@ -68,6 +71,8 @@ def align_up(x, a):
 
 
 def in_bytes_of(w):
+    if w.kind == "pad":
+        return w.rows * w.cols
     if w.kind in ("quant", "quant_k"):
         return 2 * w.rows * w.K
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
@@ -75,6 +80,8 @@ def in_bytes_of(w):
 
 def out_bytes_of(lib, w):
     """Bytes written per launch: the whole output allocation(s)."""
+    if w.kind == "pad":
+        return int(lib.mx_pad_M_groups_out_rows(w.rows, w.num_groups)) * w.cols
     if w.kind == "quant":
         return w.rows * w.K + int(lib.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "quant_k":
@@ -108,7 +115,8 @@ class Job:
         self.q_pitch = align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k") else 0
         out_pitch = align_up(self.out_bytes + self.q_pitch, 256)
         dev = torch.device("cuda")
-        host = w.x.view(np.uint8) if w.kind in ("quant", "quant_k") else w.scales
+        host = {"quant": lambda: w.x.view(np.uint8), "quant_k": lambda: w.x.view(np.uint8),
+                "pad": lambda: w.data}.get(w.kind, lambda: w.scales)()
         src = torch.from_numpy(np.ascontiguousarray(host).reshape(-1)).to(dev)
         self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
@@ -120,7 +128,7 @@ class Job:
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
         self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
                    "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups,
-                   "quant_k": lib.mx_quantize_dim1_K_groups}[w.kind]
+                   "quant_k": lib.mx_quantize_dim1_K_groups, "pad": lib.mx_pad_M_groups}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -133,6 +141,9 @@ class Job:
         if w.kind == "3d":   # experts packed: expert stride rows*cols, row stride cols
             rc = self.fn(self.in_ptrs[k], w.experts, w.rows, w.cols, w.rows * w.cols, w.cols, self.out_ptrs[k],
                          stream or None)
+        elif w.kind == "pad":
+            rc = self.fn(self.in_ptrs[k], w.rows, w.cols, w.cols, self.offs.data_ptr(), w.num_groups,
+                         self.out_ptrs[k], stream or None)
         elif w.kind in ("quant", "quant_k"):   # rows x K bf16 (quant_k: T tokens x N features)
             rc = self.fn(self.in_ptrs[k], w.rows, w.K, w.K, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
                          self.out_ptrs[k] + self.q_pitch, stream or None)
@@ -191,6 +202,8 @@ def cpu_baseline(name, seconds):
         return cpu_baseline_quant(w, seconds)
     if w.kind == "quant_k":
         return cpu_baseline_quant_k(w, seconds)
+    if w.kind == "pad":
+        return cpu_baseline_pad(w, seconds)
     out = None
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -239,6 +252,29 @@ def cpu_baseline_quant(w, seconds):
         "kind": "oracle",
         "sample": "%d runs over the first %d of the %d rows of the %s workload (K = %d, one group) in %.1f s, "
                   "single-threaded C oracle" % (reps, rows, w.rows, w.name, w.K, el),
+        "us_per_call": round(el / reps * 1e6, 1),
+    }
+
+
+def cpu_baseline_pad(w, seconds):
+    """The padding oracle on the full workload, repeated for about `seconds`."""
+    import oracle
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.pad_M_groups(w.data, w.offs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    bytes_step = w.rows * w.cols + out.size
+    return {
+        "value": round(bytes_step * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d full runs of the %s workload (%dx%d bytes, %d groups) in %.1f s, single-threaded C oracle"
+                  % (reps, w.name, w.rows, w.cols, w.num_groups, el),
         "us_per_call": round(el / reps * 1e6, 1),
     }
 
@@ -447,10 +483,12 @@ def main():
         "config": {
             "workload": args.workload,
             "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales",
+                     "pad": "per-group row padding of MXFP8 data (M groups)",
                      "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales"}.get(
                 w.kind, "%s-groups" % w.kind),
-            ("x_shape" if w.kind in ("quant", "quant_k") else "scales_shape"):
-                [w.rows, w.K] if w.kind in ("quant", "quant_k") else list(w.scales.shape),
+            {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape"}.get(w.kind, "scales_shape"):
+                [w.rows, w.K] if w.kind in ("quant", "quant_k") else (
+                    [w.rows, w.cols] if w.kind == "pad" else list(w.scales.shape)),
             "num_groups": w.experts if w.kind == "3d" else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,

@@ -12,6 +12,8 @@ fails loudly when the library has not been built.
     out = mx_block_rearrange_3d(expert_scales)
     q, blocked_scales = mx_quantize_dim0_M_groups(x_bf16, group_end_offsets)
     qT, blocked_scales = mx_quantize_dim1_K_groups(x_bf16, token_group_end_offsets)
+    padded = mx_pad_M_groups(data, group_end_offsets)
+    data = mx_unpad_M_groups(padded, rows, group_end_offsets)
 
 ``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
 row stride >= cols, any base alignment); ``group_end_offsets`` an int32 CUDA
@@ -64,6 +66,12 @@ def _load():
     lib.mx_quantize_dim1_K_groups_scale_bytes.restype = i64
     lib.mx_quantize_dim1_K_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
     lib.mx_quantize_dim1_K_groups.restype = ctypes.c_int
+    lib.mx_pad_M_groups_out_rows.argtypes = [i64, i32]
+    lib.mx_pad_M_groups_out_rows.restype = i64
+    lib.mx_pad_M_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp]
+    lib.mx_pad_M_groups.restype = ctypes.c_int
+    lib.mx_unpad_M_groups.argtypes = [vp, i64, i64, vp, i32, vp, i64, vp]
+    lib.mx_unpad_M_groups.restype = ctypes.c_int
     lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
     lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -290,7 +298,99 @@ def mx_quantize_dim1_K_groups(x, token_group_end_offsets, qT=None, scales=None, 
     return qT, scales
 
 
+def _bytes_view(t, name):
+    import torch
+
+    if t.element_size() != 1:
+        raise TypeError("%s must have 1-byte elements (uint8 or a float8 dtype)" % name)
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+def _check_offsets(offs, device):
+    import torch
+
+    if offs.dtype != torch.int32 or offs.dim() != 1:
+        raise TypeError("group_end_offsets must be a 1-D torch.int32 tensor")
+    if not offs.is_cuda or offs.device != device:
+        raise ValueError("group_end_offsets must be a GPU tensor on the data's device")
+    if not offs.is_contiguous():
+        raise ValueError("group_end_offsets must be contiguous")
+
+
+def mx_pad_M_groups(data, group_end_offsets, out=None, stream=None):
+    """Pads each token group's rows to a multiple of 128 (zero rows), groups stacked as the M-groups scales.
+
+    ``data``: (rows, cols) CUDA tensor of 1-byte elements, unit column stride. Returns the
+    (rows + 128*G, cols) uint8 padded tensor (group g's rows start at the sum of the earlier groups'
+    padded sizes; every other row is zero).
+    """
+    import torch
+
+    lib = _load()
+    if data.dim() != 2:
+        raise TypeError("data must be a 2-D tensor")
+    d = _bytes_view(data, "data")
+    if not d.is_cuda:
+        raise ValueError("data must be a GPU tensor")
+    _check_offsets(group_end_offsets, d.device)
+    rows, cols = d.shape
+    if rows > 0 and cols > 1 and d.stride(1) != 1:
+        raise ValueError("data must have unit column stride")
+    row_stride = d.stride(0) if rows > 1 else cols
+    G = group_end_offsets.numel()
+    out_rows = int(lib.mx_pad_M_groups_out_rows(rows, G))
+    if out_rows < 0:
+        raise ValueError("invalid sizes rows=%d num_groups=%d" % (rows, G))
+    if out is None:
+        out = torch.empty((out_rows, cols), dtype=torch.uint8, device=d.device)
+    elif out.dtype != torch.uint8 or out.shape != (out_rows, cols) or not out.is_contiguous() or out.device != d.device:
+        raise ValueError("out must be a contiguous (%d, %d) uint8 tensor on the data's device" % (out_rows, cols))
+    if stream is None:
+        stream = torch.cuda.current_stream(d.device).cuda_stream
+    rc = lib.mx_pad_M_groups(d.data_ptr() or None, rows, cols, row_stride, group_end_offsets.data_ptr() or None, G,
+                             out.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return out
+
+
+def mx_unpad_M_groups(padded, rows, group_end_offsets, out=None, stream=None):
+    """Inverse of mx_pad_M_groups: the (rows, cols) uint8 tensor of each group's rows (zeros past the last end).
+
+    ``padded``: contiguous (rows + 128*G, cols) CUDA tensor of 1-byte elements. ``out`` may be any
+    (rows, cols) uint8 view with unit column stride (its row stride is kept).
+    """
+    import torch
+
+    lib = _load()
+    if padded.dim() != 2:
+        raise TypeError("padded must be a 2-D tensor")
+    src = _bytes_view(padded, "padded")
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("padded must be a contiguous GPU tensor")
+    _check_offsets(group_end_offsets, src.device)
+    G = group_end_offsets.numel()
+    cols = src.shape[1]
+    if src.shape[0] != int(lib.mx_pad_M_groups_out_rows(rows, G)):
+        raise ValueError("padded must have rows + 128*G rows")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    elif out.dtype != torch.uint8 or out.shape != (rows, cols) or out.device != src.device or (
+            rows > 0 and cols > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a (rows, cols) uint8 tensor with unit column stride on the same device")
+    row_stride = out.stride(0) if rows > 1 else cols
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    rc = lib.mx_unpad_M_groups(src.data_ptr() or None, rows, cols, group_end_offsets.data_ptr() or None, G,
+                               out.data_ptr() or None, row_stride, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return out
+
+
 __all__ = [
+    "mx_pad_M_groups",
+    "mx_unpad_M_groups",
     "mx_quantize_dim1_K_groups",
     "mx_quantize_dim1_K_groups_scale_bytes",
     "mx_quantize_dim0_M_groups",

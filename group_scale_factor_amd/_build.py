@@ -5,7 +5,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", name) for name in ("mx_rearrange.hip", "mx_quantize.hip", "mx_status.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name)
+           for name in ("mx_rearrange.hip", "mx_quantize.hip", "mx_pad.hip", "mx_status.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmxrearrange.so")
 ARCH = "gfx950"

@@ -45,21 +45,18 @@
 
 #include <algorithm>
 
+#include "group_table.h"
 #include "mx_quantize.h"
 #include "mx_rearrange.h"
 
 namespace {
 
-constexpr int kWave = 64;
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr int kUnitElems = 512;       // elements per wave-unit: 16 blocks, 4 tile columns of scales
 constexpr int kUnroll = 4;            // units per wave, loads issued back to back (swept: 2..16)
-constexpr int kTileRows = 128;
 constexpr int kMaxGroups = 4096;      // LDS holds two int arrays of this many groups
 constexpr int64_t kMaxRowStride = int64_t(1) << 26;   // elements; keeps unit offsets in 32 bits
-constexpr int kRawBufferFlags = 0x00020000;
-constexpr uint32_t kOutOfRange = 0xfffffff0u;
 constexpr int kStreamPolicy = 2;      // buffer load bit 1: non-temporal
 constexpr uint32_t kE4m3Nan = 0x7f7f7f7fu;
 
@@ -79,124 +76,6 @@ struct QParams {
   int groups;
   int tile_cols;         // round_up(K/32, 4) / 4
 };
-
-template <int CTRL>
-__device__ __forceinline__ int dpp(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);
-}
-
-__device__ __forceinline__ int wave_inclusive_sum(int x) {
-  x += dpp<0x111>(x);
-  x += dpp<0x112>(x);
-  x += dpp<0x114>(x);
-  x += dpp<0x118>(x);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
-  return x;
-}
-
-__device__ __forceinline__ int wave_inclusive_max(int x) {
-  x = max(x, dpp<0x111>(x));
-  x = max(x, dpp<0x112>(x));
-  x = max(x, dpp<0x114>(x));
-  x = max(x, dpp<0x118>(x));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
-  return x;
-}
-
-__device__ __forceinline__ int wave_shift_up(int x, int first) {
-  return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
-}
-
-// One 64-group slice of the end-offset scan: e = clamped cumulative end
-// (prefix maximum of clamp(offs[g], 0, rows), continuing from carry_end),
-// pend = sum over h <= g of round_up(size_h, 128) (continuing from carry_pend).
-__device__ __forceinline__ void scan_slice(const int32_t *__restrict__ offs, int groups, int rows, int base,
-                                           int carry_end, int carry_pend, int &e, int &pend) {
-  const int g = base + int(threadIdx.x & (kWave - 1));
-  e = g < groups ? offs[g] : 0;
-  e = min(max(e, 0), rows);
-  e = max(wave_inclusive_max(e), carry_end);
-  const int prev = wave_shift_up(e, carry_end);
-  const int padded = g < groups ? (e - prev + kTileRows - 1) / kTileRows * kTileRows : 0;
-  pend = wave_inclusive_sum(padded) + carry_pend;
-}
-
-// The scanned groups: end(g) = clamped cumulative end of group g, pend(g) =
-// padded cumulative end (rows of the blocked scales up to the end of group g).
-// Up to 64 groups they live in two registers of every wave (lane g holds
-// group g) and each wave scans for itself: no LDS, no barrier. Beyond that one
-// wave scans into LDS and the workgroup synchronises.
-template <bool SMALL>
-struct Groups;
-
-template <>
-struct Groups<true> {
-  int groups, e, pend;
-  __device__ __forceinline__ void init(const QParams &p, int *) {
-    groups = p.groups;
-    scan_slice(p.offs, p.groups, p.rows, 0, 0, 0, e, pend);
-  }
-  __device__ __forceinline__ int count_ends_le(int64_t key) const {
-    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(e) <= key));
-  }
-  __device__ __forceinline__ int count_pends_le(int64_t key) const {
-    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(pend) <= key));
-  }
-  __device__ __forceinline__ int end(int g) const { return __builtin_amdgcn_readlane(e, g); }
-  __device__ __forceinline__ int pend_at(int g) const { return __builtin_amdgcn_readlane(pend, g); }
-};
-
-template <>
-struct Groups<false> {
-  int groups;
-  const int *ends, *pends;
-  __device__ __forceinline__ void init(const QParams &p, int *lds) {
-    groups = p.groups;
-    int *e_out = lds, *p_out = lds + p.groups;
-    if (threadIdx.x < kWave) {
-      int carry_end = 0, carry_pend = 0;
-      for (int base = 0; base < p.groups; base += kWave) {
-        int e, pend;
-        scan_slice(p.offs, p.groups, p.rows, base, carry_end, carry_pend, e, pend);
-        const int g = base + int(threadIdx.x);
-        if (g < p.groups) {
-          e_out[g] = e;
-          p_out[g] = pend;
-        }
-        carry_end = __builtin_amdgcn_readlane(e, kWave - 1);
-        carry_pend = __builtin_amdgcn_readlane(pend, kWave - 1);
-      }
-    }
-    __syncthreads();
-    ends = e_out;
-    pends = p_out;
-  }
-  // number of entries of arr (non-decreasing) that are <= key
-  __device__ __forceinline__ int count_le(const int *arr, int64_t key) const {
-    const int lane = threadIdx.x & (kWave - 1);
-    int n = 0;
-    for (int base = 0; base < groups; base += kWave) {
-      const int c = __popcll(__ballot(base + lane < groups && int64_t(arr[base + lane]) <= key));
-      n += c;
-      if (c < kWave) break;
-    }
-    return n;
-  }
-  __device__ __forceinline__ int count_ends_le(int64_t key) const { return count_le(ends, key); }
-  __device__ __forceinline__ int count_pends_le(int64_t key) const { return count_le(pends, key); }
-  __device__ __forceinline__ int end(int g) const { return ends[g]; }
-  __device__ __forceinline__ int pend_at(int g) const { return pends[g]; }
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void *base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
-  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), 0,
-                                           __builtin_amdgcn_readfirstlane(int(bytes)), kRawBufferFlags);
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -354,7 +233,7 @@ template <bool SMALL>
 __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   extern __shared__ __align__(16) int lds_groups[];
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  Groups<SMALL> grp;
+  MGroups<SMALL> grp;
   if (int64_t(blockIdx.x) < p.data_groups) {
     // Workgroup b runs on XCD b mod 8: give each XCD one contiguous range of
     // units, so that the 32 rows whose scale words share a 128-byte line of a
@@ -367,10 +246,10 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
     const int64_t u0 = (b * kWavesPerGroup + wave) * kUnroll;
     uint4 v[kUnroll];
     load_units(p, u0, v);
-    grp.init(p, lds_groups);
+    grp.init(p.offs, p.groups, p.rows, lds_groups);
     if (u0 < p.units) quantize_units(p, u0, v, grp);
   } else {
-    grp.init(p, lds_groups);
+    grp.init(p.offs, p.groups, p.rows, lds_groups);
     const int64_t ob = int64_t(blockIdx.x) - p.data_groups;
     if (ob < p.pad_blocks) zero_block(p, ob, grp);
   }

@@ -42,7 +42,8 @@ def test_header_declares_entry_points():
                  "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror",
                  "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes",
                  "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes",
-                 "mx_quantize_dim1_K_groups", "mx_quantize_dim1_K_groups_scale_bytes"):
+                 "mx_quantize_dim1_K_groups", "mx_quantize_dim1_K_groups_scale_bytes",
+                 "mx_pad_M_groups", "mx_unpad_M_groups", "mx_pad_M_groups_out_rows"):
         assert want in names
 
 
@@ -192,6 +193,27 @@ def test_quantize_dim1_sizes_and_validation(lib):
     assert f(None, 64, 0, 0, A, 2, None, None, None) == 0   # N = 0: nothing to write
     # switched off: valid arguments return MX_REARRANGE_EUNAVAILABLE before any HIP call
     assert f(A, 64, 8, 8, A, 1, A, A, None) == -6
+
+
+def test_pad_sizes_and_validation(lib):
+    import oracle
+
+    for rows, G in [(0, 1), (5, 3), (16640, 16)]:
+        assert lib.mx_pad_M_groups_out_rows(rows, G) == oracle.default().lib.oracle_pad_M_groups_out_rows(rows, G)
+    assert lib.mx_pad_M_groups_out_rows(-1, 1) == -1 and lib.mx_pad_M_groups_out_rows(4, 0) == -1
+    A = 0x10000
+    pad, unpad = lib.mx_pad_M_groups, lib.mx_unpad_M_groups
+    # (data, rows, cols, ld, offs, G, padded)
+    for args, want in [((A, 4, 8, 8, None, 1, A), -1), ((None, 4, 8, 8, A, 1, A), -1), ((A, 4, 8, 8, A, 1, None), -1),
+                       ((A, -1, 8, 8, A, 1, A), -2), ((A, 4, 8, 7, A, 1, A), -2), ((A, 4, 8, 8, A, 0, A), -3),
+                       ((A, 4, 8, 8, A, 4097, A), -3)]:
+        assert pad(*args, None) == want, args
+    # (padded, rows, cols, offs, G, data, ld)
+    for args, want in [((A, 4, 8, None, 1, A, 8), -1), ((None, 4, 8, A, 1, A, 8), -1), ((A, 4, 8, A, 1, None, 8), -1),
+                       ((A, 4, 8, A, 1, A, 7), -2), ((A, 4, 8, A, 0, A, 8), -3)]:
+        assert unpad(*args, None) == want, args
+    assert pad(None, 4, 0, 0, A, 1, None, None) == 0      # cols = 0: nothing to write
+    assert unpad(None, 0, 8, A, 1, None, 8, None) == 0    # rows = 0: nothing to write
 
 
 def test_strerror(lib):

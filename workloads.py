@@ -233,6 +233,43 @@ def quant_k_groups(seed=12):
                          "MXFP8 dim1 cast: bf16 (131072, 7168) tokens x features, 8 token groups", kind="quant_k")
 
 
+@dataclass
+class PadWorkload:
+    """MXFP8 data rows (E4M3 code bytes) and M-group offsets for per-group row padding."""
+    name: str
+    rows: int
+    cols: int
+    offs: np.ndarray     # int32[G], cumulative group end offsets in rows
+    data: np.ndarray     # uint8[rows, cols], C-contiguous
+    description: str
+    kind: str = "pad"
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.offs.shape[0])
+
+
+def pad_m_groups_small(seed=13):
+    """(1000, 208) data bytes, 5 groups (one empty, sizes not multiples of 128)."""
+    rng = np.random.default_rng(seed)
+    rows, cols = 1000, 208
+    offs = np.array([130, 130, 383, 700, 1000], np.int32)
+    return PadWorkload("pad_m_groups_small", rows, cols, offs, _values(rng, rows, cols, 0, 255),
+                       "per-group row padding: uint8 (1000, 208), 5 groups")
+
+
+def pad_m_groups(seed=14):
+    """(16640, 5120) E4M3 data bytes of the activations A, 16 expert groups of which 3 are forced empty."""
+    rng = np.random.default_rng(seed)
+    rows, cols, G = 16640, 5120, 16
+    empty = rng.choice(G, 3, replace=False)
+    p = np.full(G, 1.0 / (G - 3))
+    p[empty] = 0.0
+    offs = np.cumsum(rng.multinomial(rows, p)).astype(np.int32)
+    return PadWorkload("pad_m_groups", rows, cols, offs, _values(rng, rows, cols, 0, 255),
+                       "per-group row padding: uint8 (16640, 5120), 16 groups, some empty")
+
+
 WORKLOADS = {
     "m_groups_tiny": m_groups_tiny,
     "m_groups_skinny": m_groups_skinny,
@@ -256,11 +293,19 @@ WORKLOADS_QUANT = {
 }
 
 
+WORKLOADS_PAD = {
+    "pad_m_groups_small": pad_m_groups_small,
+    "pad_m_groups": pad_m_groups,
+}
+
+
 def make(name: str):
     if name in WORKLOADS_3D:
         return WORKLOADS_3D[name]()
     if name in WORKLOADS_QUANT:
         return WORKLOADS_QUANT[name]()
+    if name in WORKLOADS_PAD:
+        return WORKLOADS_PAD[name]()
     return WORKLOADS[name]()
 
 

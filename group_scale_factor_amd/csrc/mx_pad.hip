@@ -26,10 +26,10 @@
 
 namespace {
 
-constexpr int kPadThreads = 256;
+constexpr int kPadThreads = 128;       // swept: 128, 256, 512
 constexpr int kPadWaves = kPadThreads / kWave;
 constexpr int kPadUnit = 1024;          // bytes of one output row per unit (64 lanes x 16 bytes)
-constexpr int kPadUnroll = 4;           // units per wave
+constexpr int kPadUnroll = 2;           // units per wave (swept: 1, 2, 3, 4, 8)
 constexpr int kPadMaxGroups = 4096;
 constexpr int64_t kPadMaxRowStride = int64_t(1) << 30;
 constexpr int kStreamPolicy = 2;        // buffer load bit 1: non-temporal

@@ -62,8 +62,19 @@ def kernel_source(name):
 
 
 def kernel_source_digest(name):
-    with open(kernel_source(name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the kernel's source file followed by the headers it includes from the same folder."""
+    import re
+
+    path = kernel_source(name)
+    with open(path, "rb") as f:
+        text = f.read()
+    h = hashlib.sha256(text)
+    for inc in re.findall(rb'#include "([^"]+)"', text):
+        local = os.path.join(os.path.dirname(path), inc.decode())
+        if os.path.exists(local):
+            with open(local, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def align_up(x, a):

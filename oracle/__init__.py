@@ -75,6 +75,10 @@ class Oracle:
         lib.oracle_pad_M_groups.restype = ctypes.c_int
         lib.oracle_unpad_M_groups.argtypes = [ctypes.c_void_p, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p, i64]
         lib.oracle_unpad_M_groups.restype = ctypes.c_int
+        for name in ("oracle_unrearrange_M_groups", "oracle_unrearrange_K_groups"):
+            fn = getattr(lib, name)
+            fn.argtypes = [ctypes.c_void_p, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p, i64]
+            fn.restype = ctypes.c_int
         lib.oracle_3d_out_bytes.argtypes = [i64, i64, i64]
         lib.oracle_3d_out_bytes.restype = i64
         lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
@@ -113,6 +117,21 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return out[:n]
+
+    def unrearrange(self, kind, blocked, rows, cols, offs):
+        """Inverse rearrangement: the (rows, cols) row-major matrix from a blocked output of out_bytes(...) bytes."""
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        G = int(offs.shape[0])
+        blocked = np.ascontiguousarray(blocked, dtype=np.uint8).reshape(-1)
+        if G < 1 or blocked.size < self.out_bytes(kind, rows, cols, G):
+            raise ValueError("blocked input too small")
+        out = np.empty((rows, cols), np.uint8)
+        fn = self.lib.oracle_unrearrange_M_groups if kind == "M" else self.lib.oracle_unrearrange_K_groups
+        rc = fn(blocked.ctypes.data if blocked.size else None, rows, cols, offs.ctypes.data, G,
+                out.ctypes.data if out.size else None, cols)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return out
 
     def out_bytes_3d(self, experts, rows, cols):
         return int(self.lib.oracle_3d_out_bytes(experts, rows, cols))
@@ -326,3 +345,7 @@ def pad_M_groups(data, offs):
 
 def unpad_M_groups(padded, rows, offs):
     return default().unpad_M_groups(padded, rows, offs)
+
+
+def unrearrange(kind, blocked, rows, cols, offs):
+    return default().unrearrange(kind, blocked, rows, cols, offs)

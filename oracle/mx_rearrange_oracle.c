@@ -500,3 +500,51 @@ int oracle_unpad_M_groups(const uint8_t *padded, int64_t rows, int64_t cols, con
     }
     return ORACLE_OK;
 }
+
+/*
+ * The inverse rearrangement: from the blocked layout written above back to the
+ * row-major scale matrix (rows x cols, row stride ld; only the first cols bytes
+ * of each row are written). The pages describe no such kernel; it reads every
+ * byte the forward map placed from the position it placed it at, and writes
+ * zeros where no group holds data (rows past the last end for M groups,
+ * columns past the last end for K groups).
+ */
+int oracle_unrearrange_M_groups(const uint8_t *blocked, int64_t rows, int64_t cols, const int32_t *offs,
+                                int32_t num_groups, uint8_t *scales, int64_t ld) {
+    int rc = check_args(blocked, rows, cols, ld, offs, num_groups, scales, rows * cols, rows);
+    if (rc != ORACLE_OK) return rc;
+    int64_t padded_cols = round_up(cols, 4);
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) scales[i * ld + j] = 0;
+    int64_t out_row = 0, group_start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t size = offs[g] - group_start;
+        for (int64_t i = 0; i < size; ++i)
+            for (int64_t j = 0; j < cols; ++j)
+                scales[(group_start + i) * ld + j] = blocked[blocked_byte(padded_cols, out_row + i, j)];
+        out_row += round_up(size, 128);
+        group_start = offs[g];
+    }
+    return ORACLE_OK;
+}
+
+int oracle_unrearrange_K_groups(const uint8_t *blocked, int64_t rows, int64_t cols, const int32_t *offs,
+                                int32_t num_groups, uint8_t *scales, int64_t ld) {
+    int rc = check_args(blocked, rows, cols, ld, offs, num_groups, scales, rows * cols, cols);
+    if (rc != ORACLE_OK) return rc;
+    int64_t padded_rows = round_up(rows, 128);
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) scales[i * ld + j] = 0;
+    int64_t out_col = 0, group_start = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t width = offs[g] - group_start;
+        int64_t padded_width = round_up(width, 4);
+        const uint8_t *group_in = blocked + padded_rows * out_col;
+        for (int64_t i = 0; i < rows; ++i)
+            for (int64_t j = 0; j < width; ++j)
+                scales[i * ld + group_start + j] = group_in[blocked_byte(padded_width, i, j)];
+        out_col += padded_width;
+        group_start = offs[g];
+    }
+    return ORACLE_OK;
+}

@@ -642,3 +642,38 @@ def check_unpad_round_trip(orc, rng):
         if not (np.array_equal(back[:end], data[:end]) and not back[end:].any()):
             fails.append("unpad(pad(x)) != x for rows=%d offs=%s" % (rows, list(offs)))
     return fails
+
+
+# --------------------------------------------------------------------------
+# the inverse rearrangement
+# --------------------------------------------------------------------------
+
+def check_unrearrange(orc, kind, rows, cols, ld, offs, rng):
+    """The inverse reads each byte from where the decoded map says the forward put it, zero elsewhere,
+    and undoes the forward oracle."""
+    offs = np.asarray(offs, np.int32)
+    n = orc.out_bytes(kind, rows, cols, len(offs))
+    blocked = rng.integers(0, 256, size=max(n, 1), dtype=np.uint8)[:n]
+    got = orc.unrearrange(kind, blocked, rows, cols, offs)
+    src = decode(kind, rows, cols, cols, offs, n)            # output byte -> input index (row*cols + col)
+    want = np.zeros(rows * cols, np.uint8)
+    hit = src >= 0
+    want[src[hit]] = blocked[hit]
+    fails = []
+    if not np.array_equal(got.reshape(-1), want):
+        fails.append("%s rows=%d cols=%d offs=%s: inverse differs from the decoded map" % (kind, rows, cols, list(offs)))
+    A = random_scales(rng, rows, cols, ld)
+    back = orc.unrearrange(kind, orc.rearrange(kind, A, offs), rows, cols, offs)
+    end = int(offs[-1]) if len(offs) else 0
+    keep = A[:end] if kind == "M" else A[:, :end]
+    got_keep = back[:end] if kind == "M" else back[:, :end]
+    rest = back[end:] if kind == "M" else back[:, end:]
+    if not (np.array_equal(got_keep, keep) and not rest.any()):
+        fails.append("%s rows=%d cols=%d offs=%s: inverse(forward(x)) != x" % (kind, rows, cols, list(offs)))
+    return fails
+
+
+def random_scales(rng, rows, cols, ld):
+    from workloads import random_scales as rs
+
+    return rs(rng, rows, cols, ld, lo=0, hi=255)

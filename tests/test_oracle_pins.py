@@ -270,3 +270,37 @@ def test_planted_mistake_is_caught(name):
         return fails
 
     assert pins.with_mutant(old, new, all_pins), "mutant '%s' passed every pin" % name
+
+
+@pytest.mark.parametrize("kind", ["M", "K"])
+def test_unrearrange_inverts_and_follows_the_map(orc, kind):
+    rng = np.random.default_rng(90 if kind == "M" else 91)
+    fails = []
+    for _ in range(40):
+        rows, cols, ld, offs = pins.random_case(rng, kind)
+        fails += pins.check_unrearrange(orc, kind, rows, cols, ld, offs, rng)
+    assert fails == []
+
+
+UNREARRANGE_MUTANTS = {
+    "inverse M reads unpadded rows": ("scales[(group_start + i) * ld + j] = blocked[blocked_byte(padded_cols, out_row + i, j)];",
+                                      "scales[(group_start + i) * ld + j] = blocked[blocked_byte(padded_cols, group_start + i, j)];"),
+    "inverse K group matrix unpadded width": ("scales[i * ld + group_start + j] = group_in[blocked_byte(padded_width, i, j)];",
+                                              "scales[i * ld + group_start + j] = group_in[blocked_byte(width, i, j)];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNREARRANGE_MUTANTS))
+def test_unrearrange_planted_mistake_is_caught(name):
+    old, new = UNREARRANGE_MUTANTS[name]
+
+    def all_pins(mut):
+        rng = np.random.default_rng(92)
+        fails = []
+        for kind in ("M", "K"):
+            for _ in range(15):
+                rows, cols, ld, offs = pins.random_case(rng, kind)
+                fails += pins.check_unrearrange(mut, kind, rows, cols, ld, offs, rng)
+        return fails
+
+    assert pins.with_mutant(old, new, all_pins), "mutant '%s' passed every pin" % name

@@ -13,6 +13,7 @@ fails loudly when the library has not been built.
     q, blocked_scales = mx_quantize_dim0_M_groups(x_bf16, group_end_offsets)
     qT, blocked_scales = mx_quantize_dim1_K_groups(x_bf16, token_group_end_offsets)
     padded = mx_pad_M_groups(data, group_end_offsets)
+    scales = mx_block_unrearrange_M_groups(blocked, rows, cols, group_end_offsets)   # and _K_groups
     data = mx_unpad_M_groups(padded, rows, group_end_offsets)
 
 ``scales`` is a (rows, cols) uint8 CUDA tensor with unit column stride (any
@@ -72,6 +73,10 @@ def _load():
     lib.mx_pad_M_groups.restype = ctypes.c_int
     lib.mx_unpad_M_groups.argtypes = [vp, i64, i64, vp, i32, vp, i64, vp]
     lib.mx_unpad_M_groups.restype = ctypes.c_int
+    for name in ("mx_block_unrearrange_M_groups", "mx_block_unrearrange_K_groups"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i64, i64, vp, i32, vp, i64, vp]
+        fn.restype = ctypes.c_int
     lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
     lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -198,6 +203,44 @@ def mx_block_rearrange_3d(scales, out=None, stream=None):
     if rc != 0:
         raise RearrangeError(rc)
     return out
+
+
+def _unrearrange(kind, blocked, rows, cols, group_end_offsets, out, stream):
+    import torch
+
+    lib = _load()
+    if blocked.dtype != torch.uint8 or not blocked.is_cuda or not blocked.is_contiguous():
+        raise TypeError("blocked must be a contiguous torch.uint8 GPU tensor")
+    _check_offsets(group_end_offsets, blocked.device)
+    G = group_end_offsets.numel()
+    size_fn = lib.mx_rearrange_M_groups_out_bytes if kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+    n = int(size_fn(rows, cols, G))
+    if n < 0 or blocked.numel() < n:
+        raise ValueError("blocked must hold the %d bytes of the forward output" % max(n, 0))
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=blocked.device)
+    elif out.dtype != torch.uint8 or out.shape != (rows, cols) or out.device != blocked.device or (
+            rows > 0 and cols > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a (rows, cols) uint8 tensor with unit column stride on the same device")
+    row_stride = out.stride(0) if rows > 1 else cols
+    if stream is None:
+        stream = torch.cuda.current_stream(blocked.device).cuda_stream
+    fn = lib.mx_block_unrearrange_M_groups if kind == "M" else lib.mx_block_unrearrange_K_groups
+    rc = fn(blocked.data_ptr() or None, rows, cols, group_end_offsets.data_ptr() or None, G,
+            out.data_ptr() or None, row_stride, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return out
+
+
+def mx_block_unrearrange_M_groups(blocked, rows, cols, group_end_offsets, out=None, stream=None):
+    """Inverse of mx_block_rearrange_M_groups: the (rows, cols) uint8 scales (zeros past the last group)."""
+    return _unrearrange("M", blocked, rows, cols, group_end_offsets, out, stream)
+
+
+def mx_block_unrearrange_K_groups(blocked, rows, cols, group_end_offsets, out=None, stream=None):
+    """Inverse of mx_block_rearrange_K_groups: the (rows, cols) uint8 scales (zeros past the last group)."""
+    return _unrearrange("K", blocked, rows, cols, group_end_offsets, out, stream)
 
 
 def mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups):
@@ -389,6 +432,8 @@ def mx_unpad_M_groups(padded, rows, group_end_offsets, out=None, stream=None):
 
 
 __all__ = [
+    "mx_block_unrearrange_M_groups",
+    "mx_block_unrearrange_K_groups",
     "mx_pad_M_groups",
     "mx_unpad_M_groups",
     "mx_quantize_dim1_K_groups",

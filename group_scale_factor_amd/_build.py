@@ -1,12 +1,14 @@
 """Compiles the gfx950 HIP library in-tree with hipcc (no JIT cache, no torch extension)."""
 
 import os
+import re
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", name)
-           for name in ("mx_rearrange.hip", "mx_quantize.hip", "mx_pad.hip", "mx_status.hip")]
+           for name in ("mx_rearrange.hip", "mx_unrearrange.hip", "mx_quantize.hip", "mx_pad.hip", "mx_status.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmxrearrange.so")
 ARCH = "gfx950"
@@ -29,8 +31,37 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
+# DPP instructions whose DPP operand is the second operand of the operation
+# (v_subrev_u32_dpp and the like). On gfx950 a v_subrev_u32_dpp has been
+# measured to return the operands' difference the other way round, so the
+# generated code must hold none of them.
+REVERSED_DPP = re.compile(r"\bv_\w*rev\w*_dpp\b")
+
+
+def device_assembly(source):
+    """gfx950 assembly of one source, compiled with the library's flags."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "device.s")
+        res = subprocess.run([hipcc()] + flags + ["--cuda-device-only", "-S", "-I", INCLUDE, "-o", out, source],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc -S failed for %s:\n%s" % (source, res.stderr))
+        with open(out) as f:
+            return f.read()
+
+
+def check_device_code():
+    """Raise if any source compiles to a reversed-operand DPP instruction."""
+    for src in SOURCES:
+        bad = sorted(set(m.group(0) for m in REVERSED_DPP.finditer(device_assembly(src))))
+        if bad:
+            raise RuntimeError("%s: generated code holds %s" % (os.path.basename(src), ", ".join(bad)))
+
+
 def build(verbose=False):
     """Compile libmxrearrange.so next to this file. Always recompiles."""
+    check_device_code()
     tmp = LIBRARY + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp] + SOURCES
     if verbose:

@@ -46,8 +46,17 @@ __device__ __forceinline__ int wave_inclusive_max(int x) {
 }
 
 // Value of the previous lane (wave_shr:1); lane 0 gets `first`.
+//
+// The empty asm keeps the shift a plain v_mov_b32_dpp. Without it the compiler
+// folds the shift into a following `a - shifted` as v_subrev_u32_dpp, and on
+// gfx950 that instruction returns `shifted - a` (measured for wave_shr, wave_shl,
+// row_shr and quad_perm controls; v_add/v_sub/v_max with DPP are right): every
+// group width would come out negated. A build check rejects reversed-operand
+// DPP instructions in the generated code.
 __device__ __forceinline__ int wave_shift_up(int x, int first) {
-  return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
+  int r = __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
+  asm("" : "+v"(r));
+  return r;
 }
 
 // One 64-group slice of the end-offset scan, continuing from the carries:

@@ -273,7 +273,6 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
 // that place no scales; spare units zero the tail of the scale allocation.
 // ===========================================================================
 
-constexpr bool kDim1Enabled = false;          // see mx_quantize_dim1_K_groups
 constexpr int kTileTok = 128;                 // tokens per unit (4 blocks)
 constexpr int kTileFeat = 128;                // features per unit
 constexpr int kMaxGroupsDim1 = 2048;          // LDS: the staged tile plus 3 ints per group
@@ -631,9 +630,6 @@ int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t r
   const int64_t chunk_units = (T + kTileTok - 1) / kTileTok + num_groups + 1;
   p.units = chunk_units * p.nb;
   if (p.units > lim) return MX_REARRANGE_ESHAPE;
-  // Switched off: the kernel below raised a GPU memory fault whose cause has not
-  // been found; nothing is launched until it is.
-  if (!kDim1Enabled) return MX_REARRANGE_EUNAVAILABLE;
   const bool small = num_groups <= kWave;
   const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * num_groups * sizeof(int));
   const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)

@@ -127,12 +127,6 @@ int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_
  *                          written, none past it; NULL allowed when that is 0.
  * stream                   HIP stream for the single kernel.
  * Ownership and status codes as for mx_quantize_dim0_M_groups.
- *
- * Status: switched off. After validating its arguments (and returning
- * MX_REARRANGE_OK when there is nothing to write) the call returns
- * MX_REARRANGE_EUNAVAILABLE and enqueues nothing: its kernel raised a GPU
- * memory fault on gfx950 whose cause has not been found yet. The oracle of
- * this cast and its pins are in place.
  */
 int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t row_stride,
                               const int32_t *token_group_end_offsets, int32_t num_groups, uint8_t *qT,

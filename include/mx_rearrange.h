@@ -93,7 +93,7 @@ typedef struct ihipStream_t *hipStream_t;
 #define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 (or above the cap of a cast) */
 #define MX_REARRANGE_EALIGN (-4)       /* a buffer (or row stride) not aligned as required */
 #define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
-#define MX_REARRANGE_EUNAVAILABLE (-6) /* the entry point is switched off (see its declaration) */
+#define MX_REARRANGE_EUNAVAILABLE (-6) /* the entry point is not available in this build */
 
 /*
  * Output size in bytes for groups along M: (rows + 128*num_groups) *
@@ -170,6 +170,28 @@ int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols);
 int mx_block_rearrange_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols,
                           int64_t expert_stride, int64_t row_stride, uint8_t *out,
                           hipStream_t stream);
+
+/*
+ * The inverse rearrangement: reads a blocked layout as written by
+ * mx_block_rearrange_M_groups / mx_block_rearrange_K_groups (same rows, cols,
+ * offsets and num_groups; the pages describe no inverse kernel) and writes the
+ * row-major rows x cols matrix: scales + r*row_stride holds row r (only its
+ * first cols bytes are written; row_stride >= cols, any alignment). Positions
+ * no group covers (rows at or past the last end offset for M groups, columns
+ * at or past it for K groups) are written as 0x00.
+ *   blocked  device, 16-byte aligned, the *_out_bytes(rows, cols, G) bytes of the
+ *            forward output; read only. NULL allowed when rows*cols == 0.
+ *   num_groups  1 <= G <= 4096; offsets as for the forward calls (clamped the
+ *            same way when they break the order).
+ * One kernel on `stream`; nothing allocated; errors as above.
+ */
+int mx_block_unrearrange_M_groups(const uint8_t *blocked, int64_t rows, int64_t cols,
+                                  const int32_t *group_end_offsets, int32_t num_groups,
+                                  uint8_t *scales, int64_t row_stride, hipStream_t stream);
+
+int mx_block_unrearrange_K_groups(const uint8_t *blocked, int64_t rows, int64_t cols,
+                                  const int32_t *group_end_offsets, int32_t num_groups,
+                                  uint8_t *scales, int64_t row_stride, hipStream_t stream);
 
 /* Static text for a status code returned above. */
 const char *mx_rearrange_strerror(int status);

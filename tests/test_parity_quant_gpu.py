@@ -252,8 +252,6 @@ def test_bench_launch_configuration(env):
 # dim1 cast: blocks of 32 tokens, codes transposed, K-groups blocked scales
 # --------------------------------------------------------------------------
 
-DIM1_OFF = pytest.mark.skip(reason="mx_quantize_dim1_K_groups is switched off: its kernel raised a GPU memory "
-                                   "fault whose cause has not been found; it returns MX_REARRANGE_EUNAVAILABLE")
 
 def run_dim1(env, x_bits, offs, ld=None, label="", want=None):
     gsf, oracle, torch = env
@@ -280,7 +278,6 @@ def _ld8(N, extra=0):
     return (N + 7) // 8 * 8 + 8 * extra
 
 
-@DIM1_OFF
 def test_dim1_workload_small(env):
     import workloads
 
@@ -288,7 +285,6 @@ def test_dim1_workload_small(env):
     run_dim1(env, w.x, w.offs, ld=_ld8(w.K), label=w.name)
 
 
-@DIM1_OFF
 def test_dim1_workload_full_size(env):
     """(131072, 7168): every scale byte; codes of 48 sampled feature columns (the first and last of each
     128-feature block among them), computed by the oracle on those columns."""
@@ -310,7 +306,6 @@ def test_dim1_workload_full_size(env):
     _compare("dim1 full-size sampled codes", got.reshape(-1), want_q.reshape(-1))
 
 
-@DIM1_OFF
 def test_dim1_hand_worked_blocks(env):
     import pins
 
@@ -325,7 +320,6 @@ def test_dim1_hand_worked_blocks(env):
     run_dim1(env, x, [T], ld=8, label="hand-worked", want=want)
 
 
-@DIM1_OFF
 def test_dim1_every_scale_and_code(env):
     """The exhaustive value set of the dim0 sweep, one 32-token block per feature column."""
     vals = []
@@ -346,7 +340,6 @@ def test_dim1_every_scale_and_code(env):
     run_dim1(env, x, [32], ld=_ld8(x.shape[1]), label="every scale and code")
 
 
-@DIM1_OFF
 def test_dim1_fuzz(env):
     import pins
     import workloads
@@ -366,7 +359,6 @@ def test_dim1_fuzz(env):
         run_dim1(env, x, offs.astype(np.int32), ld=ld, label="fuzz%d" % i)
 
 
-@DIM1_OFF
 def test_dim1_offsets_not_multiples_of_32(env):
     import pins
 
@@ -376,7 +368,6 @@ def test_dim1_offsets_not_multiples_of_32(env):
         run_dim1(env, x, offs, ld=72, label="offsets %s" % offs)
 
 
-@DIM1_OFF
 def test_dim1_many_groups(env):
     import pins
     import workloads
@@ -387,7 +378,6 @@ def test_dim1_many_groups(env):
         run_dim1(env, pins.random_bf16_rows(rng, T, N), offs.astype(np.int32), ld=_ld8(N), label="many groups")
 
 
-@DIM1_OFF
 def test_dim1_invalid_offsets_are_clamped(env):
     import pins
 
@@ -410,7 +400,6 @@ def test_dim1_invalid_offsets_are_clamped(env):
         _compare("dim1 clamped codes", qT.cpu().numpy().reshape(-1), want[0].reshape(-1))
 
 
-@DIM1_OFF
 def test_dim1_empty_shapes(env):
     gsf, oracle, torch = env
     run_dim1(env, np.zeros((0, 40), np.uint16), [0, 0], ld=40, label="T=0")
@@ -421,7 +410,6 @@ def test_dim1_empty_shapes(env):
     assert qT.numel() == 0 and s.numel() == 0
 
 
-@DIM1_OFF
 def test_dim1_bench_launch_configuration(env):
     import bench
 

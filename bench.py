@@ -49,7 +49,9 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rear
                 "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",
                 "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",
-                "pad_m_groups_small": "pad_kernel<true, true, true>", "pad_m_groups": "pad_kernel<true, true, true>"}
+                "pad_m_groups_small": "pad_kernel<true, true, true>", "pad_m_groups": "pad_kernel<true, true, true>",
+                "inverse_m_groups_skinny": "unrearrange_kernel<false, true>",
+                "inverse_k_groups_large": "unrearrange_kernel<true, true>"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -58,6 +60,8 @@ def kernel_source(name):
     """The source file of the kernel a workload runs."""
     if name.startswith("pad"):
         return os.path.join(CSRC, "mx_pad.hip")
+    if name.startswith("inverse"):
+        return os.path.join(CSRC, "mx_unrearrange.hip")
     return os.path.join(CSRC, "mx_quantize.hip" if name.startswith("quant") else "mx_rearrange.hip")
 
 
@@ -81,16 +85,28 @@ def align_up(x, a):
     return (x + a - 1) // a * a
 
 
+INVERSE = ("inv_M", "inv_K")
+
+
 def in_bytes_of(w):
-    if w.kind == "pad":
+    """Algorithmic bytes read per launch (the inverse: the rows*cols scale bytes the blocked layout holds)."""
+    if w.kind == "pad" or w.kind in INVERSE:
         return w.rows * w.cols
     if w.kind in ("quant", "quant_k"):
         return 2 * w.rows * w.K
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
 
 
+def blocked_bytes_of(lib, w):
+    """Size of the blocked buffer the inverse reads (the forward layout's allocation)."""
+    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "inv_M" else lib.mx_rearrange_K_groups_out_bytes
+    return int(size_fn(w.rows, w.cols, w.num_groups))
+
+
 def out_bytes_of(lib, w):
     """Bytes written per launch: the whole output allocation(s)."""
+    if w.kind in INVERSE:
+        return w.rows * w.cols
     if w.kind == "pad":
         return int(lib.mx_pad_M_groups_out_rows(w.rows, w.num_groups)) * w.cols
     if w.kind == "quant":
@@ -121,25 +137,28 @@ class Job:
         self.in_bytes = in_bytes_of(w)
         self.bytes_per_step = self.in_bytes + self.out_bytes
         self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
-        in_pitch = align_up(self.in_bytes, 256)
+        self.in_alloc = blocked_bytes_of(lib, w) if w.kind in INVERSE else self.in_bytes
+        in_pitch = align_up(self.in_alloc, 256)
         # quant: codes, then the blocked scales from the next 256-byte boundary
         self.q_pitch = align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k") else 0
         out_pitch = align_up(self.out_bytes + self.q_pitch, 256)
         dev = torch.device("cuda")
         host = {"quant": lambda: w.x.view(np.uint8), "quant_k": lambda: w.x.view(np.uint8),
-                "pad": lambda: w.data}.get(w.kind, lambda: w.scales)()
+                "pad": lambda: w.data, "inv_M": lambda: w.blocked(self.in_alloc),
+                "inv_K": lambda: w.blocked(self.in_alloc)}.get(w.kind, lambda: w.scales)()
         src = torch.from_numpy(np.ascontiguousarray(host).reshape(-1)).to(dev)
         self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
         for k in range(self.copies):
-            self.inp[k * in_pitch: k * in_pitch + self.in_bytes].copy_(src)
+            self.inp[k * in_pitch: k * in_pitch + self.in_alloc].copy_(src)
         self.offs = torch.from_numpy(w.offs).to(dev) if w.kind != "3d" else None
         self.outs = [self.outbuf[k * out_pitch: k * out_pitch + self.out_bytes] for k in range(self.copies)]
         self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
         self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
                    "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups,
-                   "quant_k": lib.mx_quantize_dim1_K_groups, "pad": lib.mx_pad_M_groups}[w.kind]
+                   "quant_k": lib.mx_quantize_dim1_K_groups, "pad": lib.mx_pad_M_groups,
+                   "inv_M": lib.mx_block_unrearrange_M_groups, "inv_K": lib.mx_block_unrearrange_K_groups}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -155,6 +174,9 @@ class Job:
         elif w.kind == "pad":
             rc = self.fn(self.in_ptrs[k], w.rows, w.cols, w.cols, self.offs.data_ptr(), w.num_groups,
                          self.out_ptrs[k], stream or None)
+        elif w.kind in INVERSE:   # row-major output with row stride cols
+            rc = self.fn(self.in_ptrs[k], w.rows, w.cols, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
+                         w.cols, stream or None)
         elif w.kind in ("quant", "quant_k"):   # rows x K bf16 (quant_k: T tokens x N features)
             rc = self.fn(self.in_ptrs[k], w.rows, w.K, w.K, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
                          self.out_ptrs[k] + self.q_pitch, stream or None)
@@ -215,6 +237,8 @@ def cpu_baseline(name, seconds):
         return cpu_baseline_quant_k(w, seconds)
     if w.kind == "pad":
         return cpu_baseline_pad(w, seconds)
+    if w.kind in INVERSE:
+        return cpu_baseline_inverse(w, seconds)
     out = None
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -236,6 +260,29 @@ def cpu_baseline(name, seconds):
         "kind": "oracle",
         "sample": "%d full runs of the %s workload (%s scales, %s) in %.1f s, single-threaded C oracle"
                   % (reps, name, shape, groups, el),
+        "us_per_call": round(el / reps * 1e6, 1),
+    }
+
+
+def cpu_baseline_inverse(w, seconds):
+    import oracle
+
+    kind = w.kind[-1]
+    blocked = w.blocked(oracle.out_bytes(kind, w.rows, w.cols, w.num_groups))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.unrearrange(kind, blocked, w.rows, w.cols, w.offs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(2 * w.rows * w.cols * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d full runs of the %s workload (blocked -> %dx%d scales, %d groups) in %.1f s, "
+                  "single-threaded C oracle" % (reps, w.name, w.rows, w.cols, w.num_groups, el),
         "us_per_call": round(el / reps * 1e6, 1),
     }
 
@@ -495,11 +542,13 @@ def main():
             "workload": args.workload,
             "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales",
                      "pad": "per-group row padding of MXFP8 data (M groups)",
-                     "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales"}.get(
+                     "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales",
+                     "inv_M": "inverse rearrangement (blocked -> row-major), M groups",
+                     "inv_K": "inverse rearrangement (blocked -> row-major), K groups"}.get(
                 w.kind, "%s-groups" % w.kind),
             {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape"}.get(w.kind, "scales_shape"):
                 [w.rows, w.K] if w.kind in ("quant", "quant_k") else (
-                    [w.rows, w.cols] if w.kind == "pad" else list(w.scales.shape)),
+                    [w.rows, w.cols] if w.kind in ("pad",) + INVERSE else list(w.scales.shape)),
             "num_groups": w.experts if w.kind == "3d" else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,

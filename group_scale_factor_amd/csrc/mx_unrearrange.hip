@@ -13,13 +13,16 @@
 // where no group holds data (rows past the last end for M, columns past the
 // last end for K).
 //
-// A unit is the forward kernel's unit read backwards: 128 rows x up to 112
-// columns of one group, whose tiles are contiguous in the blocked input. Lanes
+// A unit is 128 rows of one group within one 128-column window of the output
+// row (one 128-byte line of each row when the rows are so aligned), so units
+// never share output lines except where groups meet; its tiles are contiguous
+// in the blocked input (for K groups the first may start 1-3 columns early). Lanes
 // load 16-byte tile rows (the column word of rows i, i+32, i+64, i+96), scatter
 // the four words into a row-major LDS strip (odd dword pitch), and after one
-// barrier write the row segments out with 16-byte, 4-byte or 1-byte stores,
-// whichever the segment's alignment allows. Spare units of the same launch
-// write the zeros.
+// barrier write the row segments out: 16-byte stores of words realigned with
+// v_alignbyte for every aligned 16-byte chunk inside a segment, at most three
+// dwords and three bytes at either end. Spare units of the same launch write
+// the zeros.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,9 +33,9 @@
 namespace {
 
 constexpr int kUThreads = 256;
-constexpr int kUMaxCols = 112;                     // columns per unit: 28 tiles, multiple of 16
-constexpr int kUMaxTiles = kUMaxCols / 4;
-constexpr int kUPitch = kUMaxTiles + 1;            // LDS dwords per row (odd)
+constexpr int kUCols = 128;                        // output columns per unit: one 128-byte line of a row
+constexpr int kUMaxTiles = kUCols / 4 + 1;         // a K unit may start up to 3 columns into a tile
+constexpr int kUPitch = kUMaxTiles + 2;            // LDS dwords per strip row (odd)
 constexpr int kULoads = (kUMaxTiles * 32 + kUThreads - 1) / kUThreads;
 constexpr int kUMaxGroups = 4096;
 constexpr int64_t kUMaxRowStride = int64_t(1) << 30;
@@ -47,22 +50,22 @@ struct UParams {
   int cols;
   int groups;
   int padded_cols;       // M: round_up(cols, 4)
-  int unit_cols;         // columns per unit (multiple of 4)
   int per_row;           // M: units per output row block; K: units per 128-row block
 };
 
-// K groups: clamped cumulative ends e (scale columns), cumulative chunk counts
-// cch (chunks of unit_cols padded columns) and cumulative padded widths cw.
-__device__ __forceinline__ void scan_slice_k(const int32_t *__restrict__ offs, int groups, int cols, int unit_cols,
-                                             int base, int carry_e, int carry_ch, int carry_w, int &e, int &cch,
-                                             int &cw) {
+// K groups: clamped cumulative ends e (scale columns), cumulative unit counts
+// cch (a group's units are the 128-column windows of the output row its
+// columns touch) and cumulative padded widths cw.
+__device__ __forceinline__ void scan_slice_k(const int32_t *__restrict__ offs, int groups, int cols, int base,
+                                             int carry_e, int carry_ch, int carry_w, int &e, int &cch, int &cw) {
   const int g = base + int(threadIdx.x & (kWave - 1));
   e = g < groups ? offs[g] : 0;
   e = min(max(e, 0), cols);
   e = max(wave_inclusive_max(e), carry_e);
   const int prev = wave_shift_up(e, carry_e);
   const int W = g < groups ? (e - prev + 3) & ~3 : 0;
-  cch = wave_inclusive_sum((W + unit_cols - 1) / unit_cols) + carry_ch;
+  const int windows = g < groups && e > prev ? (e - 1) / kUCols - prev / kUCols + 1 : 0;
+  cch = wave_inclusive_sum(windows) + carry_ch;
   cw = wave_inclusive_sum(W) + carry_w;
 }
 
@@ -74,7 +77,7 @@ struct KGroups<true> {
   int groups, e, cch, cw;
   __device__ __forceinline__ void init(const UParams &p, int *) {
     groups = p.groups;
-    scan_slice_k(p.offs, p.groups, p.cols, p.unit_cols, 0, 0, 0, 0, e, cch, cw);
+    scan_slice_k(p.offs, p.groups, p.cols, 0, 0, 0, 0, e, cch, cw);
   }
   __device__ __forceinline__ int count_cch_le(int64_t key) const {
     return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(cch) <= key));
@@ -95,7 +98,7 @@ struct KGroups<false> {
       int ce = 0, cc = 0, cwd = 0;
       for (int base = 0; base < p.groups; base += kWave) {
         int e, cch, cw;
-        scan_slice_k(p.offs, p.groups, p.cols, p.unit_cols, base, ce, cc, cwd, e, cch, cw);
+        scan_slice_k(p.offs, p.groups, p.cols, base, ce, cc, cwd, e, cch, cw);
         const int g = base + int(threadIdx.x);
         if (g < p.groups) {
           e_out[g] = e;
@@ -127,13 +130,28 @@ struct KGroups<false> {
   __device__ __forceinline__ int width_through(int g) const { return cws[g]; }
 };
 
-// Reads tile_cols contiguous tiles at src (tile_cols*512 bytes, 16-byte
-// aligned) and writes rows [0, nrows) x columns [0, ncols) of them to dst
-// (row r at dst + r*ld). Called by the whole workgroup.
-__device__ __forceinline__ void unit_out(uint32_t *lds, const uint8_t *src, int tile_cols, int nrows, int ncols,
-                                         uint8_t *dst, int64_t ld) {
-  const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(src, uint32_t(tile_cols) * 512u);
-  uint4 v[kULoads];
+// A row segment of ncols bytes at p split by alignment: head_bytes single bytes,
+// head_dwords 4-byte aligned dwords, `chunks` 16-byte aligned chunks from
+// chunk0, tail_dwords dwords, then single bytes from tail_bytes0 to ncols.
+struct RowSplit {
+  int head_bytes, head_dwords, chunk0, chunks, tail_dwords, tail_bytes0;
+  __device__ __forceinline__ RowSplit(const uint8_t *p, int ncols) {
+    const int m = int(reinterpret_cast<uintptr_t>(p) & 15);
+    head_bytes = min((4 - (m & 3)) & 3, ncols);
+    const int dwords = (ncols - head_bytes) >> 2;       // whole aligned dwords of the segment
+    chunk0 = (16 - m) & 15;                             // first 16-byte aligned byte (>= head_bytes)
+    head_dwords = min((chunk0 - head_bytes) >> 2, dwords);
+    chunks = (dwords - head_dwords) >> 2;
+    tail_dwords = dwords - head_dwords - 4 * chunks;
+    tail_bytes0 = head_bytes + 4 * dwords;
+    if (chunks == 0) chunk0 = head_bytes + 4 * head_dwords;   // tail dwords follow the head ones
+  }
+};
+
+// Issues the loads of tile_cols contiguous tiles at src (16-byte aligned); at
+// most `bytes` of them are read, pieces past that load as zeros.
+__device__ __forceinline__ void issue_loads(uint4 (&v)[kULoads], const uint8_t *src, int tile_cols, uint32_t bytes) {
+  const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(src, bytes);
 #pragma unroll
   for (int it = 0; it < kULoads; ++it) {
     const int s = int(threadIdx.x) + it * kUThreads;
@@ -141,51 +159,95 @@ __device__ __forceinline__ void unit_out(uint32_t *lds, const uint8_t *src, int 
     const auto t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(off), 0, 2);
     v[it] = make_uint4(t[0], t[1], t[2], t[3]);
   }
+}
+
+// Scatters the loaded tiles into the LDS strip, row r's column word c at
+// lds[r*pitch + c]. Called by the whole workgroup; ends with a barrier.
+__device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const uint4 (&v)[kULoads], int tile_cols) {
   // piece s = 32*tile + i holds the words of rows i, i+32, i+64, i+96 in column word `tile`
 #pragma unroll
   for (int it = 0; it < kULoads; ++it) {
     const int s = int(threadIdx.x) + it * kUThreads;
-    const int tc = s < tile_cols * 32 ? s >> 5 : kUMaxTiles;   // column kUMaxTiles is spare
-    const int i = s & 31;
-    lds[(i + 0) * kUPitch + tc] = v[it].x;
-    lds[(i + 32) * kUPitch + tc] = v[it].y;
-    lds[(i + 64) * kUPitch + tc] = v[it].z;
-    lds[(i + 96) * kUPitch + tc] = v[it].w;
+    if (s < tile_cols * 32) {
+      const int tc = s >> 5, i = s & 31;
+      lds[(i + 0) * pitch + tc] = v[it].x;
+      lds[(i + 32) * pitch + tc] = v[it].y;
+      lds[(i + 64) * pitch + tc] = v[it].z;
+      lds[(i + 96) * pitch + tc] = v[it].w;
+    }
   }
   __syncthreads();
-  const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
-  if (((a | uint64_t(ld)) & 15) == 0) {
-    // 16-byte aligned rows: one 16-byte piece per thread, a tail piece in dwords and bytes
-    const int pieces = (ncols + 15) >> 4;
-    for (int s = threadIdx.x; s < nrows * pieces; s += kUThreads) {
-      const int r = s / pieces, k = s - r * pieces;
-      const uint32_t *w = lds + r * kUPitch + 4 * k;
-      uint8_t *d = dst + r * ld + 16 * k;
-      const int n = min(16, ncols - 16 * k);
-      if (n == 16) {
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(d));
-      } else {
-        for (int b = 0; b < n; ++b) d[b] = uint8_t(w[b >> 2] >> (8 * (b & 3)));
-      }
+}
+
+// Writes rows [0, nrows) x bytes [skip, skip + ncols) of the LDS strip (row r
+// from lds + r*pitch words) to dst, row r at dst + r*ld (ld unused when nrows
+// is 1). Called by the whole workgroup.
+__device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int skip, int nrows, int ncols,
+                                           uint8_t *dst, int64_t ld) {
+  // Store. Split each row segment by its alignment: up to 3 single bytes, up
+  // to 3 dwords, whole 16-byte chunks, up to 3 dwords, up to 3 bytes. Three
+  // passes (chunks, end dwords, end bytes) keep every store instruction's lanes
+  // busy; a pass that the alignment rules out is skipped. Addresses stay derived
+  // from dst, so the stores are global (flat ones would also count against the
+  // LDS reads' wait counter).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uintptr_t dst_bits = reinterpret_cast<uintptr_t>(dst) | uintptr_t(nrows > 1 ? ld : 0);
+  const int max_chunks = ncols >> 4;
+  for (int s = threadIdx.x; s < nrows * max_chunks; s += kUThreads) {
+    const int r = s / max_chunks, q = s - r * max_chunks;
+    uint8_t *row_ptr = dst + int64_t(r) * ld;
+    const RowSplit sp(row_ptr, ncols);
+    if (q >= sp.chunks) continue;
+    const int lo = sp.chunk0 + 16 * q;
+    const uint32_t *w = lds + r * pitch + ((skip + lo) >> 2);
+    const int sh = (skip + lo) & 3;
+    u32x4 v;
+    if (sh) {
+      const uint32_t x0 = w[0], x1 = w[1], x2 = w[2], x3 = w[3], x4 = w[4];   // w[4] still below lo + 16
+      v = u32x4{__builtin_amdgcn_alignbyte(x1, x0, sh), __builtin_amdgcn_alignbyte(x2, x1, sh),
+                __builtin_amdgcn_alignbyte(x3, x2, sh), __builtin_amdgcn_alignbyte(x4, x3, sh)};
+    } else {
+      v = u32x4{w[0], w[1], w[2], w[3]};
     }
-  } else if (((a | uint64_t(ld)) & 3) == 0) {
-    const int words = (ncols + 3) >> 2;
-    for (int s = threadIdx.x; s < nrows * words; s += kUThreads) {
-      const int r = s / words, k = s - r * words;
-      const uint32_t w = lds[r * kUPitch + k];
-      uint8_t *d = dst + r * ld + 4 * k;
-      const int n = min(4, ncols - 4 * k);
-      if (n == 4)
-        *reinterpret_cast<uint32_t *>(d) = w;
-      else
-        for (int b = 0; b < n; ++b) d[b] = uint8_t(w >> (8 * b));
+    *reinterpret_cast<u32x4 *>(row_ptr + lo) = v;
+  }
+  if ((dst_bits & 15) != 0 || (ncols & 15) != 0) {
+    for (int s = threadIdx.x; s < nrows * 6; s += kUThreads) {
+      const int r = s / 6, k = s - r * 6;
+      uint8_t *row_ptr = dst + int64_t(r) * ld;
+      const RowSplit sp(row_ptr, ncols);
+      const int d0 = k < 3 ? (k < sp.head_dwords ? sp.head_bytes + 4 * k : -1)
+                           : (k - 3 < sp.tail_dwords ? sp.chunk0 + 16 * sp.chunks + 4 * (k - 3) : -1);
+      if (d0 < 0) continue;
+      const uint32_t *w = lds + r * pitch + ((skip + d0) >> 2);
+      const int sh = (skip + d0) & 3;
+      *reinterpret_cast<uint32_t *>(row_ptr + d0) = sh ? __builtin_amdgcn_alignbyte(w[1], w[0], sh) : w[0];
     }
+  }
+  if ((dst_bits & 3) != 0 || (ncols & 3) != 0) {
+    for (int s = threadIdx.x; s < nrows * 6; s += kUThreads) {
+      const int r = s / 6, k = s - r * 6;
+      uint8_t *row_ptr = dst + int64_t(r) * ld;
+      const RowSplit sp(row_ptr, ncols);
+      const int j = k < 3 ? (k < sp.head_bytes ? k : -1) : (sp.tail_bytes0 + (k - 3) < ncols ? sp.tail_bytes0 + k - 3 : -1);
+      if (j < 0) continue;
+      row_ptr[j] = uint8_t(lds[r * pitch + ((skip + j) >> 2)] >> (8 * ((skip + j) & 3)));
+    }
+  }
+}
+
+// One unit, its tiles loaded into v: rows [0, nrows) x columns [skip, skip +
+// ncols) to dst, row r at dst + r*ld. When the rows are contiguous (ld ==
+// ncols) and whole words, the strip is packed with pitch ncols/4 and the unit's
+// output is stored as one segment of nrows*ncols bytes.
+__device__ __forceinline__ void unit_out(uint32_t *lds, const uint4 (&v)[kULoads], int skip, int tile_cols, int nrows,
+                                         int ncols, uint8_t *dst, int64_t ld) {
+  if (skip == 0 && ld == ncols && (ncols & 3) == 0) {
+    scatter_strip(lds, ncols >> 2, v, tile_cols);
+    store_rows(lds, 0, 0, 1, nrows * ncols, dst, 0);
   } else {
-    for (int s = threadIdx.x; s < nrows * ncols; s += kUThreads) {
-      const int r = s / ncols, c = s - r * ncols;
-      dst[r * ld + c] = uint8_t(lds[r * kUPitch + (c >> 2)] >> (8 * (c & 3)));
-    }
+    scatter_strip(lds, kUPitch, v, tile_cols);
+    store_rows(lds, kUPitch, skip, nrows, ncols, dst, ld);
   }
 }
 
@@ -217,6 +279,9 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
     if (u >= p.units) return;
     const int64_t ob = u / p.per_row;                  // output row block of the blocked layout
     const int cc = int(u - ob * p.per_row);
+    const int c0 = cc * kUCols;
+    const int ncols = min(kUCols, p.cols - c0);
+    const int tile_cols = (ncols + 3) >> 2;
     const int g = grp.count_pends_le(ob * kTileRows);
     if (g < p.groups) {
       const int start = g ? grp.end(g - 1) : 0;
@@ -224,11 +289,11 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       const int64_t k = ob - pstart / kTileRows;
       const int row0 = start + int(k) * kTileRows;
       const int nrows = int(min(int64_t(kTileRows), int64_t(grp.end(g) - start) - k * kTileRows));
-      const int c0 = cc * p.unit_cols;
-      const int ncols = min(p.unit_cols, p.cols - c0);
       if (nrows <= 0 || ncols <= 0) return;
-      const uint8_t *src = p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows;
-      unit_out(strip, src, (ncols + 3) >> 2, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
+      uint4 v[kULoads];
+      issue_loads(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
+                  uint32_t(tile_cols) * 512u);
+      unit_out(strip, v, 0, tile_cols, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
     } else {
       // spare units: zero the rows after the last group
       const int64_t first_spare = grp.pend_at(p.groups - 1) / kTileRows;
@@ -249,14 +314,20 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       const int first = g ? grp.chunks_through(g - 1) : 0;
       const int k = slot - first;
       const int start = g ? grp.end(g - 1) : 0;
-      const int w = grp.end(g) - start;
-      const int W = (w + 3) & ~3;
+      const int end = grp.end(g);
+      const int W = (end - start + 3) & ~3;
       const int C = g ? grp.width_through(g - 1) : 0;
-      const int c0 = k * p.unit_cols;
-      const int ncols = min(p.unit_cols, w - c0);       // real columns (the chunk may hold only padding)
+      // output columns [a, b): the group's part of the 128-column window start/128 + k
+      const int win = start / kUCols + k;
+      const int a = max(start, win * kUCols), b = min(end, (win + 1) * kUCols);
+      const int lc = a - start;                          // first local column
+      const int ncols = b - a;
       if (nrows <= 0 || ncols <= 0) return;
-      const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(c0) * kTileRows;
-      unit_out(strip, src, (ncols + 3) >> 2, nrows, ncols, p.out + rb * kTileRows * p.ld + start + c0, p.ld);
+      const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(lc >> 2) * 512;
+      const int tile_cols = ((lc & 3) + ncols + 3) >> 2;
+      uint4 v[kULoads];
+      issue_loads(v, src, tile_cols, uint32_t(tile_cols) * 512u);
+      unit_out(strip, v, lc & 3, tile_cols, nrows, ncols, p.out + rb * kTileRows * p.ld + a, p.ld);
     } else {
       // spare slots of this row block: zero its rows' columns after the last group
       zero_region(p.out, p.ld, rb * kTileRows, rb * kTileRows + nrows, grp.end(p.groups - 1), p.cols,
@@ -287,12 +358,12 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
   p.cols = int(cols);
   p.groups = groups;
   p.padded_cols = int(round_up(cols, 4));
-  p.unit_cols = kUMaxCols;
   if (!kgroups) {
-    p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
+    p.per_row = (p.padded_cols + kUCols - 1) / kUCols;
     p.units = ((rows + kTileRows - 1) / kTileRows + groups) * p.per_row;
   } else {
-    p.per_row = int((cols + 4 * int64_t(groups) + p.unit_cols - 1) / p.unit_cols + groups);
+    // a group's windows number at most its width / 128 + 2 (floored sums), plus one spare slot
+    p.per_row = int(cols / kUCols + 2 * int64_t(groups) + 1);
     p.units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
   if (p.units > lim) return MX_REARRANGE_ESHAPE;

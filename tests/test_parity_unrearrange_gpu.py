@@ -214,3 +214,19 @@ def test_errors(env):
     with pytest.raises(ValueError):                 # blocked smaller than the forward output
         gsf.mx_block_unrearrange_M_groups(buf[:100], 4, 4, o)
     assert gsf.mx_block_unrearrange_K_groups(buf, 0, 4, o).shape == (0, 4)
+
+
+def test_bench_launch_configuration(env):
+    """The exact launches bench.py times (its buffers, pitches and stream) give the oracle's bytes."""
+    import bench
+
+    gsf, oracle, torch = env
+    for name in ("inverse_m_groups_skinny", "inverse_k_groups_large"):
+        print("case bench config", name, flush=True)
+        job = bench.Job(name, rotate_bytes=0)  # one copy: both launches write the same output
+        job.step(0)
+        job.step(1)
+        torch.cuda.synchronize()
+        w = job.w
+        want = oracle.unrearrange(w.kind[-1], w.blocked(job.in_alloc), w.rows, w.cols, w.offs)
+        assert np.array_equal(job.outs[0].cpu().numpy().reshape(w.rows, w.cols), want)

@@ -270,6 +270,43 @@ def pad_m_groups(seed=14):
                        "per-group row padding: uint8 (16640, 5120), 16 groups, some empty")
 
 
+@dataclass
+class InverseWorkload:
+    """Input of the inverse rearrangement: a blocked scale buffer and the group offsets it was laid out with.
+
+    The blocked bytes are drawn at random (every byte, padding included); their
+    count is the forward layout's size, supplied by the caller.
+    """
+    name: str
+    kind: str            # "inv_M" or "inv_K"
+    rows: int
+    cols: int
+    offs: np.ndarray     # int32 cumulative group ends (rows for M, scale columns for K)
+    seed: int
+    description: str
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.offs.shape[0])
+
+    def blocked(self, n_bytes):
+        return np.random.default_rng(self.seed).integers(0, 256, size=n_bytes, dtype=np.uint8)
+
+
+def inverse_m_groups_skinny(seed=15):
+    """The (131072, 44) M-groups scales of m_groups_skinny, read back from a blocked buffer."""
+    f = m_groups_skinny()
+    return InverseWorkload("inverse_m_groups_skinny", "inv_M", f.rows, f.cols, f.offs, seed,
+                           "inverse M-groups: blocked -> (131072, 44) scales, 8 groups")
+
+
+def inverse_k_groups_large(seed=16):
+    """The (28672, 8192) K-groups scales of k_groups_large, read back from a blocked buffer."""
+    f = k_groups_large()
+    return InverseWorkload("inverse_k_groups_large", "inv_K", f.rows, f.cols, f.offs, seed,
+                           "inverse K-groups: blocked -> (28672, 8192) scales, 8 groups")
+
+
 WORKLOADS = {
     "m_groups_tiny": m_groups_tiny,
     "m_groups_skinny": m_groups_skinny,
@@ -299,7 +336,15 @@ WORKLOADS_PAD = {
 }
 
 
+WORKLOADS_INVERSE = {
+    "inverse_m_groups_skinny": inverse_m_groups_skinny,
+    "inverse_k_groups_large": inverse_k_groups_large,
+}
+
+
 def make(name: str):
+    if name in WORKLOADS_INVERSE:
+        return WORKLOADS_INVERSE[name]()
     if name in WORKLOADS_3D:
         return WORKLOADS_3D[name]()
     if name in WORKLOADS_QUANT:

@@ -202,6 +202,21 @@ def capture(job, first, count):
     return g
 
 
+def capture_same(job, count):
+    """A HIP graph of `count` launches that all use input/output copy 0 (cache-resident when it fits)."""
+    torch = job.torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(count):
+                job.step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
 def copy_calibration(args):
     """K plain device-to-device copies of the workload's input size (reads N, writes N bytes each)."""
     import torch
@@ -225,143 +240,128 @@ def copy_calibration(args):
                       "us_per_copy": round(wall / args.steps * 1e6, 3)}), flush=True)
 
 
-def cpu_baseline(name, seconds):
-    """The CPU oracle, as it is, on the same workload, repeated for about `seconds` of CPU time."""
-    import oracle
-    import workloads
-
-    w = workloads.make(name)
-    if w.kind == "quant":
-        return cpu_baseline_quant(w, seconds)
-    if w.kind == "quant_k":
-        return cpu_baseline_quant_k(w, seconds)
-    if w.kind == "pad":
-        return cpu_baseline_pad(w, seconds)
-    if w.kind in INVERSE:
-        return cpu_baseline_inverse(w, seconds)
-    out = None
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        if w.kind == "3d":
-            out = oracle.rearrange_3d(w.scales, out)
-        else:
-            out = oracle.rearrange(w.kind, w.scales, w.offs, out)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    bytes_step = in_bytes_of(w) + out.size
-    shape = "x".join(str(x) for x in w.scales.shape)
-    groups = "%d experts" % w.experts if w.kind == "3d" else "%d groups" % w.num_groups
-    return {
-        "value": round(bytes_step * reps / el / 1e9, 3),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d full runs of the %s workload (%s scales, %s) in %.1f s, single-threaded C oracle"
-                  % (reps, name, shape, groups, el),
-        "us_per_call": round(el / reps * 1e6, 1),
-    }
+# Threads for the all-core oracle figure: the host cores one GPU's job may use.
+MAX_CPU_THREADS = 16
 
 
-def cpu_baseline_inverse(w, seconds):
-    import oracle
-
-    kind = w.kind[-1]
-    blocked = w.blocked(oracle.out_bytes(kind, w.rows, w.cols, w.num_groups))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.unrearrange(kind, blocked, w.rows, w.cols, w.offs)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {
-        "value": round(2 * w.rows * w.cols * reps / el / 1e9, 3),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d full runs of the %s workload (blocked -> %dx%d scales, %d groups) in %.1f s, "
-                  "single-threaded C oracle" % (reps, w.name, w.rows, w.cols, w.num_groups, el),
-        "us_per_call": round(el / reps * 1e6, 1),
-    }
+def host_cpu():
+    """CPU model name and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
 
 
-def cpu_baseline_quant(w, seconds):
-    """The cast oracle on a bounded sample: whole 128-row blocks of the workload's rows, repeated for
-    about `seconds`; bytes as on the GPU (2 per element read, 1 written, plus the sample's scale bytes)."""
-    import oracle
+def _oracle_job(w):
+    """(call, bytes per call, sample text) of the oracle on a bounded sample of workload w.
 
-    rows = min(w.rows, 512)
-    x = w.x[:rows]
-    offs = [rows]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        q, blocked = oracle.quantize_dim0_M_groups(x, offs)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    bytes_step = 3 * rows * w.K + blocked.size
-    return {
-        "value": round(bytes_step * reps / el / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d runs over the first %d of the %d rows of the %s workload (K = %d, one group) in %.1f s, "
-                  "single-threaded C oracle" % (reps, rows, w.rows, w.name, w.K, el),
-        "us_per_call": round(el / reps * 1e6, 1),
-    }
-
-
-def cpu_baseline_pad(w, seconds):
-    """The padding oracle on the full workload, repeated for about `seconds`."""
-    import oracle
-
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        out = oracle.pad_M_groups(w.data, w.offs)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    bytes_step = w.rows * w.cols + out.size
-    return {
-        "value": round(bytes_step * reps / el / 1e9, 3),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d full runs of the %s workload (%dx%d bytes, %d groups) in %.1f s, single-threaded C oracle"
-                  % (reps, w.name, w.rows, w.cols, w.num_groups, el),
-        "us_per_call": round(el / reps * 1e6, 1),
-    }
-
-
-def cpu_baseline_quant_k(w, seconds):
-    """The dim1 cast oracle on a bounded sample: the first 64 features over all tokens, one group."""
+    `call()` runs the oracle once; it allocates its own outputs, so several
+    threads may call it at once (the C oracle runs without the GIL). Bytes
+    follow the GPU convention: input read once plus every output byte written,
+    the output sizes taken from one call.
+    """
     import numpy as np
 
     import oracle
 
-    cols = min(w.K, 64)
-    x = np.ascontiguousarray(w.x[:, :cols])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        qT, blocked = oracle.quantize_dim1_K_groups(x, [w.rows])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    bytes_step = 3 * w.rows * cols + blocked.size
-    return {
-        "value": round(bytes_step * reps / el / 1e9, 4),
+    if w.kind == "quant":
+        rows = min(w.rows, 512)
+        x = w.x[:rows]
+        call = lambda: oracle.quantize_dim0_M_groups(x, [rows])
+        q, blocked = call()
+        return (call, 2 * x.size + q.size + blocked.size,
+                "the first %d of the %d rows of the %s workload (K = %d, one group)" % (rows, w.rows, w.name, w.K))
+    if w.kind == "quant_k":
+        cols = min(w.K, 64)
+        x = np.ascontiguousarray(w.x[:, :cols])
+        call = lambda: oracle.quantize_dim1_K_groups(x, [w.rows])
+        qT, blocked = call()
+        return (call, 2 * x.size + qT.size + blocked.size,
+                "the first %d of the %d features of the %s workload (T = %d tokens, one group)"
+                % (cols, w.K, w.name, w.rows))
+    if w.kind == "pad":
+        call = lambda: oracle.pad_M_groups(w.data, w.offs)
+        return (call, w.data.size + call().size,
+                "the %s workload (%dx%d bytes, %d groups)" % (w.name, w.rows, w.cols, w.num_groups))
+    if w.kind in INVERSE:
+        kind = w.kind[-1]
+        blocked = w.blocked(oracle.out_bytes(kind, w.rows, w.cols, w.num_groups))
+        call = lambda: oracle.unrearrange(kind, blocked, w.rows, w.cols, w.offs)
+        return (call, 2 * w.rows * w.cols,
+                "the %s workload (blocked -> %dx%d scales, %d groups)" % (w.name, w.rows, w.cols, w.num_groups))
+    if w.kind == "3d":
+        call = lambda: oracle.rearrange_3d(w.scales)
+        return (call, in_bytes_of(w) + call().size,
+                "the %s workload (%s scales, %d experts)" % (w.name, "x".join(map(str, w.scales.shape)), w.experts))
+    call = lambda: oracle.rearrange(w.kind, w.scales, w.offs)
+    return (call, in_bytes_of(w) + call().size,
+            "the %s workload (%s scales, %d groups)" % (w.name, "x".join(map(str, w.scales.shape)), w.num_groups))
+
+
+def _time_calls(call, seconds, threads):
+    """Runs `call` in `threads` threads for about `seconds`; returns (calls, elapsed seconds)."""
+    import threading
+
+    stop = time.perf_counter() + seconds
+    counts = [0] * threads
+
+    def worker(k):
+        while True:
+            call()
+            counts[k] += 1
+            if time.perf_counter() >= stop:
+                break
+
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker, args=(k,)) for k in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(counts), time.perf_counter() - t0
+
+
+def cpu_baseline(name, seconds, all_core_seconds=2.0):
+    """The CPU oracle as it is, on (a bounded sample of) the same workload: single-threaded for about
+    `seconds`, then one copy per host core at once for about `all_core_seconds` (independent runs of
+    the unchanged oracle; their aggregate rate). Same byte convention as the GPU figure."""
+    import workloads
+
+    w = workloads.make(name)
+    call, nbytes, what = _oracle_job(w)
+    model, ncores = host_cpu()
+    reps, el = _time_calls(call, seconds, 1)
+    res = {
+        "value": round(nbytes * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%d runs over the first %d of the %d features of the %s workload (T = %d tokens, one group) in "
-                  "%.1f s, single-threaded C oracle" % (reps, cols, w.K, w.name, w.rows, el),
+        "sample": "%d runs over %s in %.1f s, single-threaded C oracle" % (reps, what, el),
         "us_per_call": round(el / reps * 1e6, 1),
+        "host_cpu": model,
+        "host_cores": ncores,
     }
+    threads = min(ncores, MAX_CPU_THREADS)
+    if all_core_seconds > 0 and threads > 1:
+        reps_mt, el_mt = _time_calls(call, all_core_seconds, threads)
+        res["all_cores"] = {
+            "value": round(nbytes * reps_mt / el_mt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "sample": "%d runs of the same sample, %d at a time (one thread each, unchanged oracle) in %.1f s"
+                      % (reps_mt, threads, el_mt),
+        }
+    return res
 
 
 def _counter_means(csv_path, counter, kernel_substring):
@@ -518,6 +518,23 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     gpu_s = ev0.elapsed_time(ev1) / 1e3
+    warm = None
+    if not args.eager and K > 0:
+        # secondary figure: the same launches back to back on one input/output
+        # copy, which stays in the MALL/L2 when it fits (256 MB + 8 x 4 MB)
+        n_warm = min(K, 200)
+        g_warm = capture_same(job, n_warm)
+        g_warm.replay()
+        torch.cuda.synchronize()
+        ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ew0.record()
+        g_warm.replay()
+        ew1.record()
+        torch.cuda.synchronize()
+        warm_us = ew0.elapsed_time(ew1) * 1e3 / n_warm
+        warm = {"us_per_launch": round(warm_us, 3), "GBps": round(job.bytes_per_step / warm_us / 1e3, 2),
+                "launches": n_warm, "note": "one input/output copy reused: cache-resident when it fits, "
+                                            "not an HBM figure"}
     us_per_launch = gpu_s / K * 1e6
     value = job.bytes_per_step * K / wall / 1e9
     achieved = job.bytes_per_step / (gpu_s / K) / 1e9
@@ -565,6 +582,7 @@ def main():
             "kernel": KERNEL_NAMES.get(args.workload),
             "avg_launch_us": round(us_per_launch, 3),
         },
+        "warm": warm,
         "cpu_baseline": None,
     }
     if not args.no_cpu and args.cpu_seconds > 0 and int(os.environ.get("RANK", "0")) == 0:

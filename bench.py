@@ -449,6 +449,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the secondary cache-resident timing (profiling runs: only the timed launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's plain device copy of the workload's input size instead "
                          "(reference kernel of known traffic for the HBM byte counters)")
@@ -519,7 +521,7 @@ def main():
         wall = time.perf_counter() - t0
     gpu_s = ev0.elapsed_time(ev1) / 1e3
     warm = None
-    if not args.eager and K > 0:
+    if not args.eager and not args.no_warm and K > 0:
         # secondary figure: the same launches back to back on one input/output
         # copy, which stays in the MALL/L2 when it fits (256 MB + 8 x 4 MB)
         n_warm = min(K, 200)

@@ -1,4 +1,5 @@
-// Wave64 scans and the M-groups row table for gfx950, shared by the MXFP8 cast
+// Wave64 scans, buffer descriptors and the M-groups row table for gfx950,
+// shared by the rearrangement kernels (forward and inverse), the MXFP8 casts
 // and the per-group pad/unpad kernels.
 //
 // The table follows the M-groups layout ("[mxfp8 moe training] compute prefix

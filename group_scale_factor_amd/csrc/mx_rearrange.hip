@@ -48,12 +48,11 @@
 
 #include <algorithm>
 
+#include "group_table.h"
 #include "mx_rearrange.h"
 
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kTileRows = 128;
 // Widest column chunk of a unit: 112 columns are covered by at most 8 aligned
 // 16-byte pieces per row at any alignment, so a 128-row unit is at most 1024
 // pieces, 4 per lane of a 256-thread workgroup. Narrow units keep registers and
@@ -68,8 +67,6 @@ constexpr int kMaxFlatPieces = (kTileRows * kFlatMaxCols + 30) / 16;
 constexpr int kLdsSlack = 16;                 // room for the second word of an unaligned read
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // keeps a unit's byte span inside 32-bit buffer offsets
-constexpr uint32_t kOutOfRange = 0xfffffff0u;          // buffer offset past any range: the load returns 0
-constexpr int kRawBufferFlags = 0x00020000;            // buffer descriptor word 3: 32-bit raw data
 // Cache policy of the staging loads (buffer instruction bit 1: non-temporal).
 // M strips share at most one line with their neighbour, so they stream; the
 // row segments of neighbouring K units share lines, which stay in L2.
@@ -151,41 +148,6 @@ struct Params {
   int64_t expert_stride;  // per-expert matrices: bytes between experts
   int64_t row_blocks;     // per-expert matrices: 128-row blocks per expert
 };
-
-// ---------------------------------------------------------------------------
-// wave64 scans with DPP (row shifts within 16-lane rows, then row broadcasts)
-// ---------------------------------------------------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_shr(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);  // lanes without a source read 0
-}
-
-__device__ __forceinline__ int wave_inclusive_sum(int x) {
-  x += dpp_shr<0x111>(x);                                          // row_shr:1
-  x += dpp_shr<0x112>(x);                                          // row_shr:2
-  x += dpp_shr<0x114>(x);                                          // row_shr:4
-  x += dpp_shr<0x118>(x);                                          // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
-  return x;
-}
-
-// Inclusive running maximum of non-negative values.
-__device__ __forceinline__ int wave_inclusive_max(int x) {
-  x = max(x, dpp_shr<0x111>(x));
-  x = max(x, dpp_shr<0x112>(x));
-  x = max(x, dpp_shr<0x114>(x));
-  x = max(x, dpp_shr<0x118>(x));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
-  return x;
-}
-
-// Value of the previous lane (wave_shr:1); lane 0 gets `first`.
-__device__ __forceinline__ int wave_shift_up(int x, int first) {
-  return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
-}
 
 __device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
@@ -278,20 +240,6 @@ __device__ __forceinline__ void zero_part(uint8_t *__restrict__ out, int64_t lo,
 // ---------------------------------------------------------------------------
 // staging a 128-row strip in LDS
 // ---------------------------------------------------------------------------
-
-// Buffer resource over [base, base + bytes) for raw (unswizzled) buffer loads.
-// A load whose offset lies past `bytes` returns zeros and touches no memory.
-// Base and size are the same for the whole workgroup; reading them from the
-// first lane keeps the descriptor in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const uint8_t *base, uint32_t bytes) {
-  // readfirstlane returns int: each half goes through uint32_t so that the low
-  // half is not sign-extended into the high one
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
-  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))));
-  void *ub = reinterpret_cast<void *>((hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane(int(bytes)), kRawBufferFlags);
-}
 
 template <int POLICY>
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t offset) {

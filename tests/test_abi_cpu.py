@@ -273,3 +273,26 @@ def test_no_reversed_operand_dpp_in_device_code():
     _build.check_device_code()
     assert _build.REVERSED_DPP.search("\tv_subrev_u32_dpp v1, v31, v31 wave_shr:1 row_mask:0xf bank_mask:0xf")
     assert not _build.REVERSED_DPP.search("\tv_sub_u32_dpp v1, v1, v1 row_shr:1\n\tv_mov_b32_dpp v2, v1 wave_shr:1")
+
+
+def test_plain_c_caller_compiles():
+    """The plain C caller of tests/c_abi compiles against include/*.h as C11 (no C++ needed)."""
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    res = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                          "-I", os.path.join(rocm, "include"), "-I", os.path.join(root, "include"),
+                          os.path.join(root, "tests", "c_abi", "abi_check.c")], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr

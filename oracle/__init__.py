@@ -83,6 +83,9 @@ class Oracle:
         lib.oracle_3d_out_bytes.restype = i64
         lib.oracle_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p]
         lib.oracle_3d.restype = ctypes.c_int
+        lib.oracle_quantize_dim1_3d.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        lib.oracle_quantize_dim1_3d.restype = ctypes.c_int
         self.lib = lib
 
     def out_bytes(self, kind, rows, cols, num_groups):
@@ -210,6 +213,30 @@ class Oracle:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return qT, scales
 
+    def quantize_dim1_3d(self, w_bits):
+        """dim1 cast of stacked expert weights: a host (E, K, N) bf16 bit-pattern array (any expert and
+        row strides, unit column stride), blocks of 32 along K.
+
+        Returns (q, blocked): q (E, N, K) uint8 codes (each expert transposed), blocked the
+        out_bytes_3d(E, N, K/32) bytes of per-expert blocked scales.
+        """
+        if w_bits.dtype != np.uint16 or w_bits.ndim != 3:
+            raise ValueError("weights must be a 3-D uint16 (bf16 bit pattern) array")
+        E, K, N = w_bits.shape
+        if E * K * N > 0 and N > 1 and w_bits.strides[2] != 2:
+            raise ValueError("weights must have unit column stride")
+        ld = w_bits.strides[1] // 2 if K > 1 else N
+        es = w_bits.strides[0] // 2 if E > 1 else K * ld
+        q = np.empty((E, N, K), np.uint8)
+        n = self.out_bytes_3d(E, N, K // 32)
+        blocked = np.empty(max(n, 1), np.uint8)
+        ptr = w_bits.__array_interface__["data"][0] if E * K * N > 0 else None
+        rc = self.lib.oracle_quantize_dim1_3d(ptr, E, K, N, es, ld, q.ctypes.data if q.size else None,
+                                              blocked.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the input (status %d)" % rc)
+        return q, blocked[:n]
+
     def scales_dim1(self, x_bits):
         """Only the (N, T/32) E8M0 scale bytes of the dim1 cast of (T, N) bf16 bit patterns."""
         T, N, ld = self._bf16_shape(x_bits)
@@ -329,6 +356,10 @@ def scales_dim0(x_bits):
 
 def quantize_dim1(x_bits):
     return default().quantize_dim1(x_bits)
+
+
+def quantize_dim1_3d(w_bits):
+    return default().quantize_dim1_3d(w_bits)
 
 
 def quantize_dim1_K_groups(x_bits, offs):

@@ -415,6 +415,33 @@ int oracle_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64
     return rc;
 }
 
+/*
+ * The dim1 cast of stacked expert weights ("[mxfp8 moe training] use dim1 cast
+ * cuda kernel for 3d weights by reshaping to 2d", description and Next steps:
+ * cast the 3-D weights along their first matrix dimension and write the codes
+ * directly in per-expert column-major form; Benchmarks tables: B of shape
+ * (E, 8192, 5120)). x holds E matrices of K x N bf16 (expert e at x +
+ * e*expert_stride elements, rows ld elements apart, K a multiple of 32). Each
+ * expert is cast exactly as oracle_quantize_dim1 casts one K x N matrix: its
+ * codes, N x K (feature rows of K codes), go to q + e*N*K; its N x K/32 scale
+ * bytes are laid out as oracle_3d lays out expert e: one blocked matrix of
+ * round_up(N,128) x round_up(K/32,4) bytes at e times that size. blocked
+ * receives oracle_3d_out_bytes(E, N, K/32) bytes.
+ */
+int oracle_quantize_dim1_3d(const uint16_t *x, int64_t E, int64_t K, int64_t N, int64_t expert_stride, int64_t ld,
+                            uint8_t *q, uint8_t *blocked) {
+    if (E < 0 || K < 0 || N < 0 || K % 32 != 0 || ld < N || expert_stride < 0) return ORACLE_EBADSHAPE;
+    int64_t per = N * (K / 32);
+    uint8_t *scales = (uint8_t *)malloc(E * per > 0 ? (size_t)(E * per) : 1);
+    if (!scales) return ORACLE_EBADPTR;
+    int rc = ORACLE_OK;
+    for (int64_t e = 0; e < E && rc == ORACLE_OK; ++e)
+        rc = oracle_quantize_dim1(x + e * expert_stride, K, N, ld, q + e * N * K, scales + e * per);
+    if (rc == ORACLE_OK) rc = oracle_3d(scales, E, N, K / 32, per, K / 32, blocked);
+    free(scales);
+    return rc;
+}
+
 /* The scale bytes alone (N x T/32, row-major) of the dim1 cast. The maximum of
  * each block is accumulated row by row of x (the same maximum, in an order
  * that reads x sequentially). */

@@ -349,6 +349,44 @@ def random_case_3d(rng, max_experts=5, max_rows=300, max_cols=40):
 # deliberately broken copies of the oracle
 # --------------------------------------------------------------------------
 
+def check_dim1_3d(orc, rng):
+    """The dim1 cast of stacked expert weights (E, K, N) equals the dim1 cast of the experts stacked
+    into one (E*K, N) token matrix with E equal token groups: the codes of expert e are the token
+    columns [eK, (e+1)K) of that cast's transposed codes, and the per-expert blocked scales are the
+    first bytes of its K-groups blocked scales (each group one blocked matrix at ru(N,128)*C_g, C_g =
+    e*ru(K/32,4)), the rest of which is zero. Any expert and row strides."""
+    fails = []
+    for E, K, N, ld_pad, es_pad in [(1, 32, 5, 0, 0), (3, 64, 40, 3, 17), (4, 96, 130, 0, 0), (2, 160, 7, 1, 5),
+                                    (5, 32, 129, 2, 0), (0, 64, 8, 0, 0), (3, 0, 8, 0, 0)]:
+        ld = N + ld_pad
+        es = K * ld + es_pad
+        base = random_bf16_rows(rng, max(E * es // max(ld, 1) + 2, 1), ld).reshape(-1)
+        x3 = np.lib.stride_tricks.as_strided(base, shape=(E, K, N), strides=(2 * es, 2 * ld, 2))
+        q, blocked = orc.quantize_dim1_3d(x3)
+        if q.shape != (E, N, K) or blocked.size != orc.out_bytes_3d(E, N, K // 32):
+            fails.append("E=%d K=%d N=%d: shapes %s %d" % (E, K, N, q.shape, blocked.size))
+            continue
+        if E == 0 or K == 0 or N == 0:
+            continue
+        packed = np.ascontiguousarray(x3).reshape(E * K, N)
+        offs = np.arange(1, E + 1, dtype=np.int32) * K
+        qT2, blocked2 = orc.quantize_dim1_K_groups(packed, offs)
+        for e in range(E):
+            if not np.array_equal(q[e], qT2[:, e * K:(e + 1) * K]):
+                fails.append("E=%d K=%d N=%d: codes of expert %d" % (E, K, N, e))
+        if not np.array_equal(blocked2[:blocked.size], blocked) or blocked2[blocked.size:].any():
+            fails.append("E=%d K=%d N=%d: blocked scales" % (E, K, N))
+    # expert stride 0: every expert is the same matrix
+    x = random_bf16_rows(rng, 64, 24)
+    x3 = np.lib.stride_tricks.as_strided(x.reshape(-1), shape=(3, 64, 24), strides=(0, 48, 2))
+    q, blocked = orc.quantize_dim1_3d(x3)
+    one = blocked.size // 3
+    if not (np.array_equal(q[0], q[1]) and np.array_equal(q[0], q[2]) and
+            np.array_equal(blocked[:one], blocked[one:2 * one]) and np.array_equal(blocked[:one], blocked[2 * one:])):
+        fails.append("expert stride 0: experts differ")
+    return fails
+
+
 def with_mutant(old, new, fn):
     """Build a copy of the oracle source with `old` replaced by `new`, call fn(oracle), clean up."""
     import oracle

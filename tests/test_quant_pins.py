@@ -66,6 +66,27 @@ def test_dim1_blocked_scales_layout(orc):
     assert pins.check_dim1_blocked(orc, np.random.default_rng(46)) == []
 
 
+def test_dim1_3d_equals_dim1_of_the_stacked_experts(orc):
+    assert pins.check_dim1_3d(orc, np.random.default_rng(48)) == []
+
+
+DIM1_3D_MUTANTS = {
+    "expert stride ignored": ("rc = oracle_quantize_dim1(x + e * expert_stride, K, N, ld, q + e * N * K",
+                              "rc = oracle_quantize_dim1(x + 0 * expert_stride, K, N, ld, q + e * N * K"),
+    "codes of an expert K bytes apart": ("K, N, ld, q + e * N * K, scales + e * per);",
+                                         "K, N, ld, q + e * K, scales + e * per);"),
+    "every expert gets expert 0's scales": ("oracle_3d(scales, E, N, K / 32, per, K / 32, blocked)",
+                                            "oracle_3d(scales, E, N, K / 32, 0, K / 32, blocked)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DIM1_3D_MUTANTS))
+def test_dim1_3d_planted_mistake_is_caught(name):
+    old, new = DIM1_3D_MUTANTS[name]
+    fails = pins.with_mutant(old, new, lambda mut: pins.check_dim1_3d(mut, np.random.default_rng(48)))
+    assert fails, "planted mistake '%s' passed every pin" % name
+
+
 def test_scales_only_functions_agree(orc):
     rng = np.random.default_rng(47)
     x = pins.random_bf16_rows(rng, 96, 192)

@@ -51,7 +51,8 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rear
                 "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",
                 "pad_m_groups_small": "pad_kernel<true, true, true>", "pad_m_groups": "pad_kernel<true, true, true>",
                 "inverse_m_groups_skinny": "unrearrange_kernel<false, true>",
-                "inverse_k_groups_large": "unrearrange_kernel<true, true>"}
+                "inverse_k_groups_large": "unrearrange_kernel<true, true>",
+                "quant_3d_small": "quantize_dim1_kernel", "quant_3d_e16": "quantize_dim1_kernel"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -94,6 +95,8 @@ def in_bytes_of(w):
         return w.rows * w.cols
     if w.kind in ("quant", "quant_k"):
         return 2 * w.rows * w.K
+    if w.kind == "quant_3d":
+        return 2 * w.experts * w.K * w.N
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
 
 
@@ -113,6 +116,8 @@ def out_bytes_of(lib, w):
         return w.rows * w.K + int(lib.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "quant_k":
         return w.rows * w.K + int(lib.mx_quantize_dim1_K_groups_scale_bytes(w.rows, w.K, w.num_groups))
+    if w.kind == "quant_3d":
+        return w.experts * w.N * w.K + int(lib.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N))
     if w.kind == "3d":
         return int(lib.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
     size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
@@ -140,25 +145,28 @@ class Job:
         self.in_alloc = blocked_bytes_of(lib, w) if w.kind in INVERSE else self.in_bytes
         in_pitch = align_up(self.in_alloc, 256)
         # quant: codes, then the blocked scales from the next 256-byte boundary
-        self.q_pitch = align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k") else 0
+        self.q_pitch = (align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k")
+                        else align_up(w.experts * w.N * w.K, 256) if w.kind == "quant_3d" else 0)
         out_pitch = align_up(self.out_bytes + self.q_pitch, 256)
         dev = torch.device("cuda")
         host = {"quant": lambda: w.x.view(np.uint8), "quant_k": lambda: w.x.view(np.uint8),
                 "pad": lambda: w.data, "inv_M": lambda: w.blocked(self.in_alloc),
+                "quant_3d": lambda: np.ascontiguousarray(w.w).view(np.uint8),
                 "inv_K": lambda: w.blocked(self.in_alloc)}.get(w.kind, lambda: w.scales)()
         src = torch.from_numpy(np.ascontiguousarray(host).reshape(-1)).to(dev)
         self.inp = torch.empty(in_pitch * self.copies, dtype=torch.uint8, device=dev)
         self.outbuf = torch.empty(out_pitch * self.copies, dtype=torch.uint8, device=dev)
         for k in range(self.copies):
             self.inp[k * in_pitch: k * in_pitch + self.in_alloc].copy_(src)
-        self.offs = torch.from_numpy(w.offs).to(dev) if w.kind != "3d" else None
+        self.offs = torch.from_numpy(w.offs).to(dev) if w.kind not in ("3d", "quant_3d") else None
         self.outs = [self.outbuf[k * out_pitch: k * out_pitch + self.out_bytes] for k in range(self.copies)]
         self.in_ptrs = [self.inp.data_ptr() + k * in_pitch for k in range(self.copies)]
         self.out_ptrs = [self.outbuf.data_ptr() + k * out_pitch for k in range(self.copies)]
         self.fn = {"M": lib.mx_block_rearrange_M_groups, "K": lib.mx_block_rearrange_K_groups,
                    "3d": lib.mx_block_rearrange_3d, "quant": lib.mx_quantize_dim0_M_groups,
                    "quant_k": lib.mx_quantize_dim1_K_groups, "pad": lib.mx_pad_M_groups,
-                   "inv_M": lib.mx_block_unrearrange_M_groups, "inv_K": lib.mx_block_unrearrange_K_groups}[w.kind]
+                   "inv_M": lib.mx_block_unrearrange_M_groups, "inv_K": lib.mx_block_unrearrange_K_groups,
+                   "quant_3d": lib.mx_quantize_dim1_3d}[w.kind]
         self.error = gsf.RearrangeError
         torch.cuda.synchronize()
 
@@ -174,6 +182,9 @@ class Job:
         elif w.kind == "pad":
             rc = self.fn(self.in_ptrs[k], w.rows, w.cols, w.cols, self.offs.data_ptr(), w.num_groups,
                          self.out_ptrs[k], stream or None)
+        elif w.kind == "quant_3d":   # experts packed: expert stride K*N, row stride N (elements)
+            rc = self.fn(self.in_ptrs[k], w.experts, w.K, w.N, w.K * w.N, w.N, self.out_ptrs[k],
+                         self.out_ptrs[k] + self.q_pitch, stream or None)
         elif w.kind in INVERSE:   # row-major output with row stride cols
             rc = self.fn(self.in_ptrs[k], w.rows, w.cols, self.offs.data_ptr(), w.num_groups, self.out_ptrs[k],
                          w.cols, stream or None)
@@ -293,6 +304,14 @@ def _oracle_job(w):
         call = lambda: oracle.pad_M_groups(w.data, w.offs)
         return (call, w.data.size + call().size,
                 "the %s workload (%dx%d bytes, %d groups)" % (w.name, w.rows, w.cols, w.num_groups))
+    if w.kind == "quant_3d":
+        cols = min(w.N, 64)
+        x = np.ascontiguousarray(w.w[:1, :, :cols])
+        call = lambda: oracle.quantize_dim1_3d(x)
+        q, blocked = call()
+        return (call, 2 * x.size + q.size + blocked.size,
+                "the first %d of the %d features of expert 0 of the %s workload (K = %d)"
+                % (cols, w.N, w.name, w.K))
     if w.kind in INVERSE:
         kind = w.kind[-1]
         blocked = w.blocked(oracle.out_bytes(kind, w.rows, w.cols, w.num_groups))
@@ -555,7 +574,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (wall / K * 1e6), 3) if pages_us else None,
-        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind in ("quant", "quant_k") else "u8",
+        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind in ("quant", "quant_k", "quant_3d") else "u8",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -563,12 +582,15 @@ def main():
                      "pad": "per-group row padding of MXFP8 data (M groups)",
                      "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales",
                      "inv_M": "inverse rearrangement (blocked -> row-major), M groups",
-                     "inv_K": "inverse rearrangement (blocked -> row-major), K groups"}.get(
+                     "inv_K": "inverse rearrangement (blocked -> row-major), K groups",
+                     "quant_3d": "MXFP8 dim1 cast of stacked expert weights, per-expert codes and blocked scales"}.get(
                 w.kind, "%s-groups" % w.kind),
-            {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape"}.get(w.kind, "scales_shape"):
+            {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape", "quant_3d": "w_shape"}.get(
+                w.kind, "scales_shape"):
                 [w.rows, w.K] if w.kind in ("quant", "quant_k") else (
-                    [w.rows, w.cols] if w.kind in ("pad",) + INVERSE else list(w.scales.shape)),
-            "num_groups": w.experts if w.kind == "3d" else w.num_groups,
+                    [w.experts, w.K, w.N] if w.kind == "quant_3d" else (
+                        [w.rows, w.cols] if w.kind in ("pad",) + INVERSE else list(w.scales.shape))),
+            "num_groups": w.experts if w.kind in ("3d", "quant_3d") else w.num_groups,
             "bytes_per_step": job.bytes_per_step,
             "rotating_copies": job.copies,
             "launch": "eager" if args.eager else "hip_graph",

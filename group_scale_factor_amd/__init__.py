@@ -65,6 +65,10 @@ def _load():
     lib.mx_quantize_dim0_M_groups.restype = ctypes.c_int
     lib.mx_quantize_dim1_K_groups_scale_bytes.argtypes = [i64, i64, i32]
     lib.mx_quantize_dim1_K_groups_scale_bytes.restype = i64
+    lib.mx_quantize_dim1_3d_scale_bytes.argtypes = [i64, i64, i64]
+    lib.mx_quantize_dim1_3d_scale_bytes.restype = i64
+    lib.mx_quantize_dim1_3d.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.mx_quantize_dim1_3d.restype = ctypes.c_int
     lib.mx_quantize_dim1_K_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
     lib.mx_quantize_dim1_K_groups.restype = ctypes.c_int
     lib.mx_pad_M_groups_out_rows.argtypes = [i64, i32]
@@ -360,6 +364,48 @@ def _check_offsets(offs, device):
         raise ValueError("group_end_offsets must be contiguous")
 
 
+def mx_quantize_dim1_3d_scale_bytes(experts, K, N):
+    return int(_load().mx_quantize_dim1_3d_scale_bytes(experts, K, N))
+
+
+def mx_quantize_dim1_3d(w, q=None, scales=None, stream=None):
+    """MXFP8 cast of stacked expert weights along their first matrix dimension, written per expert.
+
+    ``w``: (E, K, N) torch.bfloat16 CUDA tensor (any expert and row strides that are multiples of 8
+    elements, unit column stride), K a multiple of 32. Returns (q, scales): q an (E, N, K) uint8
+    tensor of E4M3 codes (each expert transposed), scales the flat uint8 per-expert blocked E8M0
+    output of E * round_up(N, 128) * round_up(K/32, 4) bytes.
+    """
+    import torch
+
+    lib = _load()
+    if w.dtype != torch.bfloat16 or w.dim() != 3 or not w.is_cuda:
+        raise TypeError("w must be a 3-D torch.bfloat16 GPU tensor")
+    E, K, N = w.shape
+    if E * K * N > 0 and N > 1 and w.stride(2) != 1:
+        raise ValueError("w must have unit column stride")
+    row_stride = w.stride(1) if K > 1 else N
+    expert_stride = w.stride(0) if E > 1 else K * row_stride
+    n = int(lib.mx_quantize_dim1_3d_scale_bytes(E, K, N))
+    if n < 0:
+        raise ValueError("invalid sizes E=%d K=%d N=%d" % (E, K, N))
+    if q is None:
+        q = torch.empty((E, N, K), dtype=torch.uint8, device=w.device)
+    elif q.dtype != torch.uint8 or q.shape != (E, N, K) or not q.is_contiguous() or q.device != w.device:
+        raise ValueError("q must be a contiguous (E, N, K) uint8 tensor on w's device")
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.uint8, device=w.device)
+    elif scales.dtype != torch.uint8 or not scales.is_contiguous() or scales.numel() < n or scales.device != w.device:
+        raise ValueError("scales must be a contiguous uint8 tensor of at least %d bytes on w's device" % n)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    rc = lib.mx_quantize_dim1_3d(w.data_ptr() or None, E, K, N, expert_stride, row_stride, q.data_ptr() or None,
+                                 scales.data_ptr() or None, stream or None)
+    if rc != 0:
+        raise RearrangeError(rc)
+    return q, scales
+
+
 def mx_pad_M_groups(data, group_end_offsets, out=None, stream=None):
     """Pads each token group's rows to a multiple of 128 (zero rows), groups stacked as the M-groups scales.
 
@@ -432,6 +478,8 @@ def mx_unpad_M_groups(padded, rows, group_end_offsets, out=None, stream=None):
 
 
 __all__ = [
+    "mx_quantize_dim1_3d",
+    "mx_quantize_dim1_3d_scale_bytes",
     "mx_block_unrearrange_M_groups",
     "mx_block_unrearrange_K_groups",
     "mx_pad_M_groups",

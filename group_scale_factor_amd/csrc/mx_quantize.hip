@@ -289,11 +289,17 @@ constexpr int kTileDwords = 68 * (kTileTok - 1) + 16 * ((kTileTok - 1) >> 5) + 6
 
 struct Q1Params {
   const uint16_t *x;
-  const int32_t *offs;   // token group ends
+  const int32_t *offs;   // token group ends (unused when group_tokens > 0)
   uint8_t *qT;
   uint8_t *scales;
   int64_t ld;            // row stride of x in elements
   int64_t T;             // tokens (multiple of 32)
+  int64_t q_ld;          // row stride of the codes: T, or group_tokens for per-group code matrices
+  int64_t x_gstride;     // per-group inputs: elements between groups' first rows
+  int64_t q_gstride;     // per-group codes: bytes between groups' code matrices
+  int group_tokens;      // > 0: every group holds exactly this many tokens (stacked expert weights),
+                         // each with its own input matrix and its own N x group_tokens code matrix
+  int diagonal;          // unit order: 0 token chunks fastest, 1 diagonal over feature blocks
   int64_t padded_rows;   // round_up(N, 128)
   int64_t scale_bytes;   // padded_rows * (T/32 + 4G)
   int64_t units;         // chunk_units * nb
@@ -307,7 +313,11 @@ struct Q1Params {
 __device__ __forceinline__ void scan_slice_dim1(const Q1Params &p, int base, int carry_e, int carry_ch, int carry_w,
                                                 int &e, int &cch, int &cw) {
   const int g = base + int(threadIdx.x & (kWave - 1));
-  int64_t et = g < p.groups ? int64_t(p.offs[g]) : 0;
+  int64_t et = 0;
+  if (p.group_tokens > 0)
+    et = g < p.groups ? int64_t(g + 1) * p.group_tokens : 0;
+  else if (g < p.groups)
+    et = p.offs[g];
   et = min(max(et, int64_t(0)), p.T);
   e = max(wave_inclusive_max(int(et / 32)), carry_e);
   const int prev = wave_shift_up(e, carry_e);
@@ -415,11 +425,15 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
   const int64_t n8 = p.units / 8 * 8;
   const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
                                              : int64_t(blockIdx.x);
-  // token chunks vary fastest: units that run together write neighbouring
-  // pieces of the same transposed code rows, which meet in L2 as whole lines
+  // Token chunks vary fastest: units that run together write neighbouring
+  // pieces of the same transposed code rows, which meet in L2 as whole lines.
+  // When every unit writes whole lines (per-group codes, groups of a multiple
+  // of 128 tokens) the diagonal order instead spreads the units that run
+  // together over feature blocks, so their reads of the token rows do not all
+  // fall on the same column slice (4% faster at token rows 16 KB apart).
   const int64_t chunk_units = p.units / p.nb;
-  const int fb = int(u / chunk_units);          // feature block
-  const int64_t ci = u - int64_t(fb) * chunk_units;   // tile column (chunk) index over all groups
+  const int64_t ci = u % chunk_units;           // tile column (chunk) index over all groups
+  const int fb = p.diagonal ? int((u / chunk_units + ci) % p.nb) : int(u / chunk_units);   // feature block
 
   Groups1<SMALL> grp;
   grp.init(p, group_lds);
@@ -429,6 +443,8 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
   int64_t t0 = 0;          // first token of the unit
   int ntok = 0;            // tokens of the unit (multiple of 32, <= 128)
   int64_t tile_off = -1;   // byte offset of the unit's scale tile, -1: no scales
+  int64_t x_row0 = 0;      // element offset of the unit's first input row
+  int64_t q_col0 = 0;      // byte offset of the unit's first code in code row 0
   if (ci < total_chunks) {
     const int g = grp.count_cch_le(ci);
     const int first_chunk = g ? grp.chunks_through(g - 1) : 0;
@@ -440,12 +456,22 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
     t0 = 32 * int64_t(S + 4 * k);
     ntok = 32 * min(4, w - 4 * k);
     tile_off = p.padded_rows * C + (int64_t(fb) * (W / 4) + k) * 512;
+    if (p.group_tokens > 0) {   // group g's own input and code matrices
+      const int64_t tl = t0 - int64_t(g) * p.group_tokens;
+      x_row0 = int64_t(g) * p.x_gstride + tl * p.ld;
+      q_col0 = int64_t(g) * p.q_gstride + tl;
+    } else {
+      x_row0 = t0 * p.ld;
+      q_col0 = t0;
+    }
   } else {
     const int64_t trailing = (cols - last_end + 3) / 4;   // chunks of tokens after the last group
     const int64_t c2 = ci - total_chunks;
-    if (c2 < trailing) {
+    if (c2 < trailing) {   // (never with group_tokens > 0: the groups cover every token)
       t0 = 32 * (last_end + 4 * c2);
       ntok = int(32 * min(int64_t(4), cols - last_end - 4 * c2));
+      x_row0 = t0 * p.ld;
+      q_col0 = t0;
     } else {
       // spare unit: a share of the zero tail of the scale allocation
       const int64_t spare = (p.units / p.nb - total_chunks - trailing) * p.nb;
@@ -468,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
   {
     const int f_base = fb * kTileFeat;
     const __amdgpu_buffer_rsrc_t rsrc =
-        byte_buffer(p.x + t0 * p.ld + f_base, uint32_t(int64_t(ntok) * p.ld * 2));
+        byte_buffer(p.x + x_row0 + f_base, uint32_t(int64_t(ntok) * p.ld * 2));
     uint4 v[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -516,14 +542,14 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
   const int n0 = fb * kTileFeat + 2 * pair;
   if (32 * tb < ntok) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const int64_t col = t0 + 32 * tb;
+    const int64_t col = q_col0 + 32 * tb;
     if (n0 < p.N) {
-      uint8_t *dst = p.qT + int64_t(n0) * p.T + col;
+      uint8_t *dst = p.qT + int64_t(n0) * p.q_ld + col;
       *reinterpret_cast<u32x4 *>(dst) = u32x4{c0[0], c0[1], c0[2], c0[3]};
       *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{c0[4], c0[5], c0[6], c0[7]};
     }
     if (n0 + 1 < p.N) {
-      uint8_t *dst = p.qT + int64_t(n0 + 1) * p.T + col;
+      uint8_t *dst = p.qT + int64_t(n0 + 1) * p.q_ld + col;
       *reinterpret_cast<u32x4 *>(dst) = u32x4{c1[0], c1[1], c1[2], c1[3]};
       *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{c1[4], c1[5], c1[6], c1[7]};
     }
@@ -545,6 +571,26 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Grid and launch of the dim1 cast; p holds the sources, outputs, strides,
+// groups and scale size (validated by the caller, scale_bytes > 0).
+int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  p.N = int(N);
+  p.nb = int((N + kTileFeat - 1) / kTileFeat);
+  p.padded_rows = round_up(N, 128);
+  // tile columns: every group's plus the trailing tokens' plus at least one spare
+  const int64_t chunk_units = (p.T + kTileTok - 1) / kTileTok + p.groups + 1;
+  p.units = chunk_units * p.nb;
+  if (p.units > lim) return MX_REARRANGE_ESHAPE;
+  const bool small = p.groups <= kWave;
+  const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * p.groups * sizeof(int));
+  const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)
+                         : reinterpret_cast<const void *>(&quantize_dim1_kernel<false>);
+  void *args[] = {&p};
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(kThreads), args, lds, stream);
+  return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
+}
 
 }  // namespace
 
@@ -628,22 +674,48 @@ int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t r
   p.scales = blocked_scales;
   p.ld = row_stride;
   p.T = T;
-  p.N = int(N);
-  p.nb = int((N + kTileFeat - 1) / kTileFeat);
+  p.q_ld = T;
   p.groups = num_groups;
-  p.padded_rows = round_up(N, 128);
   p.scale_bytes = scale_bytes;
-  // tile columns: every group's plus the trailing tokens' plus at least one spare
-  const int64_t chunk_units = (T + kTileTok - 1) / kTileTok + num_groups + 1;
-  p.units = chunk_units * p.nb;
-  if (p.units > lim) return MX_REARRANGE_ESHAPE;
-  const bool small = num_groups <= kWave;
-  const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * num_groups * sizeof(int));
-  const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)
-                         : reinterpret_cast<const void *>(&quantize_dim1_kernel<false>);
-  void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(kThreads), args, lds, stream);
-  return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
+  return launch_dim1(p, N, stream);
+}
+
+int64_t mx_quantize_dim1_3d_scale_bytes(int64_t experts, int64_t K, int64_t N) {
+  if (experts < 0 || K < 0 || N < 0 || K % 32 != 0) return -1;
+  return experts * round_up(N, 128) * round_up(K / 32, 4);
+}
+
+int mx_quantize_dim1_3d(const uint16_t *w, int64_t experts, int64_t K, int64_t N, int64_t expert_stride,
+                        int64_t row_stride, uint8_t *q, uint8_t *blocked_scales, hipStream_t stream) {
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (experts < 0 || K < 0 || N < 0 || K % 32 != 0 || row_stride < N || row_stride > kMaxRowStrideDim1 ||
+      expert_stride < 0)
+    return MX_REARRANGE_ESHAPE;
+  if (experts > kMaxGroupsDim1) return MX_REARRANGE_EGROUPS;
+  if (K > lim || N > lim - 128 || (experts > 0 && K > lim / experts)) return MX_REARRANGE_ESHAPE;
+  if (experts > 1 && expert_stride > INT64_MAX / experts) return MX_REARRANGE_ESHAPE;
+  const int64_t scale_bytes = mx_quantize_dim1_3d_scale_bytes(experts, K, N);
+  if (scale_bytes == 0) return MX_REARRANGE_OK;   // no experts, no tokens or no features: nothing to write
+  if (w == nullptr || q == nullptr || blocked_scales == nullptr) return MX_REARRANGE_ENULL;
+  if ((reinterpret_cast<uintptr_t>(w) & 15) || (row_stride & 7) || (expert_stride & 7) ||
+      (reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(blocked_scales) & 15))
+    return MX_REARRANGE_EALIGN;
+
+  Q1Params p = {};
+  p.x = w;
+  p.offs = nullptr;
+  p.qT = q;
+  p.scales = blocked_scales;
+  p.ld = row_stride;
+  p.T = experts * K;
+  p.q_ld = K;
+  p.x_gstride = expert_stride;
+  p.q_gstride = N * K;
+  p.group_tokens = int(K);
+  p.diagonal = K % kTileTok == 0;
+  p.groups = int(experts);
+  p.scale_bytes = scale_bytes;
+  return launch_dim1(p, N, stream);
 }
 
 }  // extern "C"

@@ -132,6 +132,43 @@ int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t r
                               const int32_t *token_group_end_offsets, int32_t num_groups, uint8_t *qT,
                               uint8_t *blocked_scales, hipStream_t stream);
 
+/*
+ * The dim1 cast of stacked expert weights, written per expert ("[mxfp8 moe
+ * training] use dim1 cast cuda kernel for 3d weights by reshaping to 2d":
+ * description and Next steps, a dim1 cast of the 3-D weights that writes each
+ * expert's codes directly in column-major form; Benchmarks tables, weights of
+ * shape (E, 8192, 5120)).
+ *
+ * w holds `experts` matrices of K x N bf16 bit patterns (expert e at
+ * w + e*expert_stride elements, row k of it `row_stride` elements further per
+ * row). Each is cast exactly as mx_quantize_dim1_K_groups casts a K x N
+ * matrix with one group: blocks of 32 along K, codes transposed. Outputs:
+ *   q               E x N x K E4M3 codes: expert e's row n (feature n over all K)
+ *                   at q + e*N*K + n*K.
+ *   blocked_scales  mx_quantize_dim1_3d_scale_bytes(E, K, N) bytes: expert e's
+ *                   N x K/32 scales as one blocked matrix of round_up(N,128) x
+ *                   round_up(K/32,4) bytes at e times that size — the layout
+ *                   mx_block_rearrange_3d writes for (E, N, K/32) scales, and the
+ *                   one mx_quantize_dim1_K_groups writes for the experts stacked
+ *                   into E*K tokens with E equal groups, without its tail.
+ * Arguments:
+ *   experts         0 <= E <= 2048 (E == 0: nothing to do).
+ *   K               a multiple of 32; E*K < 2^31.
+ *   N               N + 128 < 2^31.
+ *   expert_stride   >= 0 elements, a multiple of 8 (16-byte aligned experts; 0
+ *                   repeats one matrix).
+ *   row_stride      N <= row_stride <= 2^23 elements, a multiple of 8.
+ *   w, q, blocked_scales  device, 16-byte aligned; NULL allowed only when
+ *                   there is nothing to write (E, K or N zero).
+ * One kernel on `stream`; nothing allocated; no device memory read during
+ * validation. Status codes as for mx_quantize_dim0_M_groups (MX_REARRANGE_EGROUPS
+ * for E > 2048).
+ */
+int64_t mx_quantize_dim1_3d_scale_bytes(int64_t experts, int64_t K, int64_t N);
+
+int mx_quantize_dim1_3d(const uint16_t *w, int64_t experts, int64_t K, int64_t N, int64_t expert_stride,
+                        int64_t row_stride, uint8_t *q, uint8_t *blocked_scales, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

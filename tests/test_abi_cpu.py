@@ -44,7 +44,8 @@ def test_header_declares_entry_points():
                  "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes",
                  "mx_quantize_dim1_K_groups", "mx_quantize_dim1_K_groups_scale_bytes",
                  "mx_pad_M_groups", "mx_unpad_M_groups", "mx_pad_M_groups_out_rows",
-                 "mx_block_unrearrange_M_groups", "mx_block_unrearrange_K_groups"):
+                 "mx_block_unrearrange_M_groups", "mx_block_unrearrange_K_groups",
+                 "mx_quantize_dim1_3d", "mx_quantize_dim1_3d_scale_bytes"):
         assert want in names
 
 
@@ -192,6 +193,35 @@ def test_quantize_dim1_sizes_and_validation(lib):
     for args, want in cases:
         assert f(*args, None) == want, args
     assert f(None, 64, 0, 0, A, 2, None, None, None) == 0   # N = 0: nothing to write
+
+
+def test_quantize_dim1_3d_sizes_and_validation(lib):
+    import oracle
+
+    for E, K, N in [(0, 64, 8), (1, 32, 1), (16, 5120, 8192), (3, 96, 130), (2, 0, 5), (4, 64, 0)]:
+        assert lib.mx_quantize_dim1_3d_scale_bytes(E, K, N) == oracle.out_bytes_3d(E, N, K // 32)
+    assert lib.mx_quantize_dim1_3d_scale_bytes(2, 48, 4) == -1
+    f = lib.mx_quantize_dim1_3d
+    A = 0x10000
+    cases = [
+        ((None, 2, 64, 8, 512, 8, A, A), -1),          # weights NULL
+        ((A, 2, 64, 8, 512, 8, None, A), -1),          # codes NULL
+        ((A, 2, 64, 8, 512, 8, A, None), -1),          # scales NULL
+        ((A, 2, 48, 8, 512, 8, A, A), -2),             # K not a multiple of 32
+        ((A, 2, 64, 8, 512, 4, A, A), -2),             # row stride below N
+        ((A, 2, 64, 8, -8, 8, A, A), -2),              # negative expert stride
+        ((A, -1, 64, 8, 512, 8, A, A), -2),            # negative experts
+        ((A, 2049, 64, 8, 512, 8, A, A), -3),          # too many experts
+        ((A + 8, 2, 64, 8, 512, 8, A, A), -4),         # weights misaligned
+        ((A, 2, 64, 8, 516, 8, A, A), -4),             # expert stride not a multiple of 8
+        ((A, 2, 64, 8, 512, 12, A, A), -4),            # row stride not a multiple of 8
+        ((A, 2, 64, 8, 512, 8, A + 4, A), -4),         # codes misaligned
+        ((A, 2, 64, 8, 512, 8, A, A + 4), -4),         # scales misaligned
+    ]
+    for args, want in cases:
+        assert f(*args, None) == want, args
+    for args in [(None, 0, 64, 8, 0, 8, None, None), (None, 3, 0, 8, 0, 8, None, None), (None, 3, 64, 0, 0, 0, None, None)]:
+        assert f(*args, None) == 0, args                 # nothing to write
 
 
 def test_pad_sizes_and_validation(lib):

@@ -424,3 +424,103 @@ def test_dim1_bench_launch_configuration(env):
     out = job.outbuf.cpu().numpy()
     _compare("dim1 bench codes", out[: w.rows * w.K], want_q.reshape(-1))
     _compare("dim1 bench scales", out[job.q_pitch: job.q_pitch + want_s.size], want_s)
+
+
+# --------------------------------------------------------------------------
+# dim1 cast of stacked expert weights: per-expert codes and blocked scales
+# --------------------------------------------------------------------------
+
+def device_bf16_3d(torch, w_bits, es, ld):
+    """An (E, K, N) bf16 device view with expert stride es and row stride ld (elements) of host bit patterns."""
+    E, K, N = w_bits.shape
+    n = (E - 1) * es + (K - 1) * ld + N if E * K * N > 0 else 0
+    flat = np.zeros(n + 64, np.uint16)
+    if E * K * N > 0:
+        np.lib.stride_tricks.as_strided(flat, shape=(E, K, N), strides=(2 * es, 2 * ld, 2))[...] = w_bits
+    buf = torch.from_numpy(flat.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.as_strided(buf, (E, K, N), (es, ld, 1))
+
+
+def run_dim1_3d(env, w_bits, es=None, ld=None, label=""):
+    gsf, oracle, torch = env
+    E, K, N = w_bits.shape
+    ld = _ld8(N) if ld is None else ld
+    es = K * ld if es is None else es
+    print("case dim1 3d", label, "E", E, "K", K, "N", N, "ld", ld, "expert stride", es, flush=True)
+    want_q, want_s = oracle.quantize_dim1_3d(w_bits)
+    w = device_bf16_3d(torch, w_bits, es, ld)
+    nq, ns = E * N * K, want_s.size
+    qbuf = torch.full((nq + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((ns + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    gsf.mx_quantize_dim1_3d(w, q=qbuf[:nq].view(E, N, K), scales=sbuf[:ns])
+    torch.cuda.synchronize()
+    gq, gs = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (gq[nq:] == POISON).all(), "%s: bytes past the codes were written" % label
+    assert (gs[ns:] == POISON).all(), "%s: bytes past the scales were written" % label
+    _compare(label + " codes", gq[:nq], want_q.reshape(-1))
+    _compare(label + " scales", gs[:ns], want_s)
+
+
+def test_dim1_3d_workload_small(env):
+    import workloads
+
+    w = workloads.make("quant_3d_small")
+    es, ld = w.w.strides[0] // 2, w.w.strides[1] // 2
+    run_dim1_3d(env, w.w, es=es, ld=ld, label=w.name)
+
+
+def test_dim1_3d_fuzz(env):
+    import pins
+
+    rng = np.random.default_rng(95)
+    for i in range(40):
+        E = int(rng.choice([1, 2, 3, 5, 8]))
+        K = int(rng.choice([32, 64, 96, 128, 160, 256, 320]))   # multiples of 128 take the diagonal unit order
+        N = int(rng.choice([1, 5, 8, 40, 127, 128, 129, 300]))
+        ld = _ld8(N, int(rng.integers(0, 3)))
+        es = 0 if rng.random() < 0.1 else K * ld + 8 * int(rng.integers(0, 4))
+        one = pins.random_bf16_rows(rng, K * (1 if es == 0 else E), N)
+        w = np.broadcast_to(one, (E, K, N)) if es == 0 else one.reshape(E, K, N)
+        run_dim1_3d(env, w, es=es, ld=ld, label="fuzz%d" % i)
+
+
+def test_dim1_3d_many_experts(env):
+    import pins
+
+    rng = np.random.default_rng(96)
+    w = pins.random_bf16_rows(rng, 70 * 32, 40).reshape(70, 32, 40)   # more than 64 groups: table in LDS
+    run_dim1_3d(env, w, label="70 experts")
+    w = pins.random_bf16_rows(rng, 66 * 128, 136).reshape(66, 128, 136)
+    run_dim1_3d(env, w, label="66 experts of 128 tokens")
+
+
+def test_dim1_3d_empty_shapes(env):
+    gsf, oracle, torch = env
+    for E, K, N in [(0, 64, 8), (3, 0, 8), (3, 64, 0)]:
+        print("case dim1 3d empty", E, K, N, flush=True)
+        w = torch.zeros((E, K, N), dtype=torch.bfloat16, device="cuda")
+        q, s = gsf.mx_quantize_dim1_3d(w)
+        torch.cuda.synchronize()
+        assert q.shape == (E, N, K) and s.numel() == oracle.out_bytes_3d(E, N, K // 32)
+
+
+def test_dim1_3d_full_size_and_bench_launch(env):
+    """The launches bench.py times on the (16, 5120, 8192) weights: every scale byte, and the codes of
+    three whole experts, against the oracle."""
+    import bench
+
+    gsf, oracle, torch = env
+    print("case dim1 3d full size quant_3d_e16 (bench launch)", flush=True)
+    job = bench.Job("quant_3d_e16", rotate_bytes=0)
+    job.step(0)
+    torch.cuda.synchronize()
+    w = job.w
+    E, K, N = w.experts, w.K, w.N
+    out = job.outs[0].cpu().numpy()
+    q = out[: E * N * K].reshape(E, N, K)
+    scales = np.stack([oracle.scales_dim1(w.w[e]) for e in range(E)])        # (E, N, K/32)
+    _compare("quant_3d_e16 scales", out[job.q_pitch: job.q_pitch + oracle.out_bytes_3d(E, N, K // 32)],
+             oracle.rearrange_3d(scales))
+    for e in (0, 7, E - 1):
+        want_q, _ = oracle.quantize_dim1(w.w[e])
+        _compare("quant_3d_e16 codes of expert %d" % e, q[e].reshape(-1), want_q.reshape(-1))

@@ -234,6 +234,40 @@ def quant_k_groups(seed=12):
 
 
 @dataclass
+class ExpertQuantWorkload:
+    """Stacked expert weights for the dim1 cast written per expert: E matrices of K x N bf16 bit
+    patterns (blocks of 32 along K), possibly a strided view (expert and row strides multiples of 8)."""
+    name: str
+    experts: int
+    K: int
+    N: int
+    w: np.ndarray        # uint16[E, K, N] view, unit column stride
+    description: str
+    kind: str = "quant_3d"
+
+
+def quant_3d_small(seed=17):
+    """3 experts of (320, 300) bf16, experts 4000 elements apart beyond their size, rows 320 apart."""
+    rng = np.random.default_rng(seed)
+    E, K, N, ld = 3, 320, 300, 320
+    es = K * ld + 4000
+    flat = _bf16_activations(rng, (E * es) // ld + 1, ld, 20, 0.02).reshape(-1)
+    w = np.lib.stride_tricks.as_strided(flat, shape=(E, K, N), strides=(2 * es, 2 * ld, 2))
+    return ExpertQuantWorkload("quant_3d_small", E, K, N, w,
+                               "dim1 cast of 3 experts of (320, 300) bf16, strided experts and rows")
+
+
+def quant_3d_e16(seed=18):
+    """16 experts of (5120, 8192) bf16: the weights B (16, 8192, 5120) of the MoE benchmarks, cast along
+    the 5120-long reduction dimension; scales (16, 8192, 160)."""
+    rng = np.random.default_rng(seed)
+    E, K, N = 16, 5120, 8192
+    w = _bf16_activations_chunked(rng, E * K, N, 8, chunk_rows=2048).reshape(E, K, N)
+    return ExpertQuantWorkload("quant_3d_e16", E, K, N, w,
+                               "dim1 cast of expert weights (16, 5120, 8192) bf16, written per expert")
+
+
+@dataclass
 class PadWorkload:
     """MXFP8 data rows (E4M3 code bytes) and M-group offsets for per-group row padding."""
     name: str
@@ -330,6 +364,12 @@ WORKLOADS_QUANT = {
 }
 
 
+WORKLOADS_QUANT_3D = {
+    "quant_3d_small": quant_3d_small,
+    "quant_3d_e16": quant_3d_e16,
+}
+
+
 WORKLOADS_PAD = {
     "pad_m_groups_small": pad_m_groups_small,
     "pad_m_groups": pad_m_groups,
@@ -345,6 +385,8 @@ WORKLOADS_INVERSE = {
 def make(name: str):
     if name in WORKLOADS_INVERSE:
         return WORKLOADS_INVERSE[name]()
+    if name in WORKLOADS_QUANT_3D:
+        return WORKLOADS_QUANT_3D[name]()
     if name in WORKLOADS_3D:
         return WORKLOADS_3D[name]()
     if name in WORKLOADS_QUANT:

@@ -82,7 +82,7 @@ def test_rearrange_3d(env):
     check_graph(torch, "experts_3d_small", lambda: gsf.mx_block_rearrange_3d(s, out=out), [out])
 
 
-def test_quantize_dim0_and_dim1(env):
+def test_quantize_dim0_dim1_and_experts(env):
     import workloads
 
     gsf, torch = env
@@ -102,6 +102,12 @@ def test_quantize_dim0_and_dim1(env):
                      device="cuda")
     check_graph(torch, "quant_k_groups_small", lambda: gsf.mx_quantize_dim1_K_groups(x, o, qT=qT, scales=sc),
                 [qT, sc])
+
+    w = workloads.make("quant_3d_small")
+    wt = torch.from_numpy(np.ascontiguousarray(w.w).view(np.int16)).cuda().view(torch.bfloat16)
+    q3 = torch.empty((w.experts, w.N, w.K), dtype=torch.uint8, device="cuda")
+    s3 = torch.empty(gsf.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N), dtype=torch.uint8, device="cuda")
+    check_graph(torch, "quant_3d_small", lambda: gsf.mx_quantize_dim1_3d(wt, q=q3, scales=s3), [q3, s3])
 
 
 def test_pad_unpad_and_inverse(env):

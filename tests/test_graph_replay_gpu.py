@@ -104,7 +104,10 @@ def test_quantize_dim0_dim1_and_experts(env):
                 [qT, sc])
 
     w = workloads.make("quant_3d_small")
-    wt = torch.from_numpy(np.ascontiguousarray(w.w).view(np.int16)).cuda().view(torch.bfloat16)
+    ld = (w.N + 7) // 8 * 8                  # rows padded to a multiple of 8 elements (16 bytes)
+    padded = np.zeros((w.experts, w.K, ld), np.uint16)
+    padded[:, :, :w.N] = w.w
+    wt = torch.from_numpy(padded.view(np.int16)).cuda().view(torch.bfloat16)[:, :, :w.N]
     q3 = torch.empty((w.experts, w.N, w.K), dtype=torch.uint8, device="cuda")
     s3 = torch.empty(gsf.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N), dtype=torch.uint8, device="cuda")
     check_graph(torch, "quant_3d_small", lambda: gsf.mx_quantize_dim1_3d(wt, q=q3, scales=s3), [q3, s3])

@@ -45,8 +45,8 @@
  *                      `cols` bytes, row r starting at scales + r*row_stride.
  *                      Any byte alignment. May be NULL when rows*cols == 0.
  *                      Read only.
- *   rows, cols         matrix shape in bytes (scale elements); >= 0, and
- *                      rows, cols + 4*num_groups < 2^31.
+ *   rows, cols         matrix shape in bytes (scale elements); >= 0, with
+ *                      rows + 128*num_groups < 2^31 and cols + 4*num_groups < 2^31.
  *   row_stride         bytes between consecutive rows; cols <= row_stride <= 2^24.
  *                      No alignment requirement.
  *   group_end_offsets  device pointer to int32[num_groups], cumulative

@@ -21,7 +21,9 @@
 // the four words into a row-major LDS strip (odd dword pitch), and after one
 // barrier write the row segments out: 16-byte stores of words realigned with
 // v_alignbyte for every aligned 16-byte chunk inside a segment, at most three
-// dwords and three bytes at either end. Spare units of the same launch write
+// dwords and three bytes at either end. When the unit's output rows are
+// contiguous (row stride == width, whole words) the strip is packed and the
+// unit's rows are stored as one segment. Spare units of the same launch write
 // the zeros.
 
 #include <hip/hip_runtime.h>

@@ -66,19 +66,33 @@ def kernel_source(name):
     return os.path.join(CSRC, "mx_quantize.hip" if name.startswith("quant") else "mx_rearrange.hip")
 
 
-def kernel_source_digest(name):
-    """Digest of the kernel's source file followed by the headers it includes from the same folder."""
+def code_text(text):
+    """Source text with comments removed and whitespace collapsed: what the compiler sees of it."""
     import re
 
+    text = re.sub(rb"/\*.*?\*/", b" ", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b" ", text)
+    return b" ".join(text.split())
+
+
+def kernel_source_digest(name, read=None):
+    """Digest of the code of the kernel's source file followed by the headers it includes from the same
+    folder (comments and whitespace ignored). `read(path)` returns a file's bytes (default: the tree)."""
+    import re
+
+    if read is None:
+        def read(path):
+            with open(path, "rb") as f:
+                return f.read()
     path = kernel_source(name)
-    with open(path, "rb") as f:
-        text = f.read()
-    h = hashlib.sha256(text)
+    text = read(path)
+    h = hashlib.sha256(code_text(text))
     for inc in re.findall(rb'#include "([^"]+)"', text):
         local = os.path.join(os.path.dirname(path), inc.decode())
-        if os.path.exists(local):
-            with open(local, "rb") as f:
-                h.update(f.read())
+        try:
+            h.update(code_text(read(local)))
+        except (OSError, KeyError):
+            pass
     return h.hexdigest()[:16]
 
 

@@ -326,3 +326,19 @@ def test_bench_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_profile_digest_ignores_comments_only():
+    """The kernel digest that ties a committed counter profile to its kernel changes with the code, not with
+    comments or whitespace."""
+    import bench
+
+    src = b"// header\n#include <x>\nint f(int a) { /* sum */ return a + 1; }  // tail\n"
+    assert bench.code_text(src) == bench.code_text(b"#include <x>\nint   f(int a) {\n return a + 1; }\n")
+    assert bench.code_text(src) != bench.code_text(src.replace(b"a + 1", b"a + 2"))
+    files = {bench.kernel_source("m_groups_skinny"): b"int k; // one\n"}
+    d1 = bench.kernel_source_digest("m_groups_skinny", lambda p: files[p])
+    files[bench.kernel_source("m_groups_skinny")] = b"int k; /* two */\n"
+    assert bench.kernel_source_digest("m_groups_skinny", lambda p: files[p]) == d1
+    files[bench.kernel_source("m_groups_skinny")] = b"long k;\n"
+    assert bench.kernel_source_digest("m_groups_skinny", lambda p: files[p]) != d1

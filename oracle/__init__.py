@@ -1,8 +1,12 @@
-"""CPU oracle for the grouped MXFP8 scale-factor rearrangement and the MXFP8 dim0 cast (test infrastructure).
+"""CPU oracle (test infrastructure) for everything the HIP library computes: the grouped MXFP8
+scale-factor rearrangement (M groups, K groups, per-expert 3-D) and its inverse, the MXFP8 casts
+(dim0 with M-groups scales, dim1 with K-groups scales, dim1 of stacked expert weights) and the
+per-group padding of data rows.
 
-Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
-this package. The HIP library and its Python binding never do, and this package
-imports nothing from them.
+Only the tests (including the plain C caller in tests/c_abi, which links the
+compiled oracle), the smoke check and the benchmark's CPU-baseline leg may
+import, link or call it. The HIP library and its Python binding never do, and
+this package imports nothing from them.
 
 The arithmetic lives in ``mx_rearrange_oracle.c``: a plain C loop over groups and
 over every position of each group's padded matrix, and a plain per-block loop for

@@ -15,7 +15,6 @@ const char *mx_rearrange_strerror(int status) {
     case MX_REARRANGE_EGROUPS: return "num_groups out of range (at least 1; the casts also cap it)";
     case MX_REARRANGE_EALIGN: return "a buffer or row stride is not aligned as the entry point requires";
     case MX_REARRANGE_ELAUNCH: return "HIP kernel launch failed";
-    case MX_REARRANGE_EUNAVAILABLE: return "entry point not available in this build";
     default: return "unknown status";
   }
 }

@@ -93,7 +93,6 @@ typedef struct ihipStream_t *hipStream_t;
 #define MX_REARRANGE_EGROUPS (-3)      /* num_groups < 1 (or above the cap of a cast) */
 #define MX_REARRANGE_EALIGN (-4)       /* a buffer (or row stride) not aligned as required */
 #define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
-#define MX_REARRANGE_EUNAVAILABLE (-6) /* the entry point is not available in this build */
 
 /*
  * Output size in bytes for groups along M: (rows + 128*num_groups) *

@@ -258,7 +258,7 @@ def test_unrearrange_validation(lib, fn):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):   # -6 and 7: not a status, "unknown status" text
         s = lib.mx_rearrange_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 

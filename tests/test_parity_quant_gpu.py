@@ -79,14 +79,15 @@ def test_workload_small_bit_exact(env):
     run_quant(env, w.x, w.offs, label=w.name)
 
 
-def test_workload_full_size(env):
-    """(16640, 5120): every scale byte against the oracle; codes on sampled rows (every group's first
-    and last rows and 256 seeded others), computed by the oracle one row at a time."""
+@pytest.mark.parametrize("name", ["quant_m_groups", "quant_m_groups_skinny"])
+def test_workload_full_size(env, name):
+    """(16640, 5120) and (131072, 1408): every scale byte against the oracle; codes on sampled rows (every
+    group's first and last rows and 256 seeded others), computed by the oracle one row at a time."""
     gsf, oracle, torch = env
     import workloads
 
-    w = workloads.make("quant_m_groups")
-    print("case quant_m_groups full size", flush=True)
+    w = workloads.make(name)
+    print("case %s full size" % name, flush=True)
     x = device_bf16(torch, w.x)
     q, s = gsf.mx_quantize_dim0_M_groups(x, torch.from_numpy(w.offs).cuda())
     torch.cuda.synchronize()

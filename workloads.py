@@ -205,6 +205,16 @@ def quant_m_groups(seed=10):
                          "MXFP8 dim0 cast: bf16 (16640, 5120), 16 groups, some empty")
 
 
+def quant_m_groups_skinny(seed=19):
+    """(131072, 1408) bf16 activations with the 8 groups of m_groups_skinny: the data whose block-32 scales
+    are the (131072, 44) M-groups skinny shape (44 scale columns, padded to 48 in the blocked layout)."""
+    rng = np.random.default_rng(seed)
+    f = m_groups_skinny()
+    return QuantWorkload("quant_m_groups_skinny", f.rows, 44 * 32, f.offs,
+                         _bf16_activations_chunked(rng, f.rows, 44 * 32, 8),
+                         "MXFP8 dim0 cast: bf16 (131072, 1408), the 8 groups of the skinny M-groups shape")
+
+
 def _bf16_activations_chunked(rng, rows, K, row_exp, chunk_rows=8192):
     """As _bf16_activations without zero blocks, drawn in row chunks to bound host memory."""
     out = np.empty((rows, K), np.uint16)
@@ -359,6 +369,7 @@ WORKLOADS_3D = {
 WORKLOADS_QUANT = {
     "quant_m_groups_small": quant_m_groups_small,
     "quant_m_groups": quant_m_groups,
+    "quant_m_groups_skinny": quant_m_groups_skinny,
     "quant_k_groups_small": quant_k_groups_small,
     "quant_k_groups": quant_k_groups,
 }

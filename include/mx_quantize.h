@@ -70,6 +70,12 @@ int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t n
  *                    that size is 0.
  * stream             HIP stream for the single kernel (NULL: the default stream).
  *
+ * Stacked expert weights cast along their last dimension (E matrices of N x K)
+ * need no entry point of their own: cast the (E*N) x K view with the E equal
+ * group ends N, 2N, ..., E*N; the first E * round_up(N,128) * round_up(K/32,4)
+ * bytes of blocked_scales are then the per-expert layout of mx_block_rearrange_3d
+ * (the rest is the zero tail of the M-groups allocation).
+ *
  * Ownership: the caller owns every buffer; nothing is allocated or kept.
  * Errors (negative status, nothing enqueued): MX_REARRANGE_ESHAPE for sizes and
  * strides, MX_REARRANGE_EGROUPS for num_groups, MX_REARRANGE_ENULL for a missing

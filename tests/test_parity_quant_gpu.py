@@ -525,3 +525,25 @@ def test_dim1_3d_full_size_and_bench_launch(env):
     for e in (0, 7, E - 1):
         want_q, _ = oracle.quantize_dim1(w.w[e])
         _compare("quant_3d_e16 codes of expert %d" % e, q[e].reshape(-1), want_q.reshape(-1))
+
+
+def test_dim0_cast_of_stacked_experts_gives_the_3d_layout(env):
+    """Expert weights cast along their last dimension through the M-groups cast with equal group ends: the
+    codes are the row-wise cast, the first E*ru(N,128)*ru(K/32,4) scale bytes the per-expert (3-D) layout of
+    the oracle, and the rest of the allocation zero."""
+    gsf, oracle, torch = env
+    import pins
+
+    rng = np.random.default_rng(97)
+    for E, N, K in [(3, 200, 96), (4, 128, 64), (2, 129, 160)]:
+        print("case dim0 stacked experts", E, N, K, flush=True)
+        x = pins.random_bf16_rows(rng, E * N, K)
+        offs = (np.arange(1, E + 1) * N).astype(np.int32)
+        q, s = gsf.mx_quantize_dim0_M_groups(device_bf16(torch, x), torch.from_numpy(offs).cuda())
+        torch.cuda.synchronize()
+        want_q, scales = oracle.quantize_dim0(x)                      # (E*N, K/32) scales
+        want_3d = oracle.rearrange_3d(scales.reshape(E, N, K // 32))
+        got_s = s.cpu().numpy()
+        _compare("stacked experts codes", q.cpu().numpy().reshape(-1), want_q.reshape(-1))
+        _compare("stacked experts 3-D scales", got_s[:want_3d.size], want_3d)
+        assert not got_s[want_3d.size:].any()

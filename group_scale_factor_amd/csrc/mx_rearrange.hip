@@ -17,13 +17,19 @@
 //
 // The work is pure data movement, bound by HBM bandwidth; there is no
 // arithmetic on the scale values. Design:
-//   * One workgroup handles one work unit: 128 rows x a column chunk of one
-//     group, i.e. a run of whole output tiles that are contiguous in the output.
+//   * One workgroup handles one work unit. M groups and per-expert matrices:
+//     128 rows x a column chunk of one group, i.e. a run of whole output tiles
+//     that are contiguous in the output. K groups: 128 rows x a 256-column
+//     window of the input (two 128-byte lines per row when rows are so
+//     aligned), writing the tiles of every group whose tiles start in the
+//     window — one contiguous output run per such group. A K unit's input
+//     thus does not depend on the offsets: its loads are issued before the
+//     offsets are scanned, and the scan runs while they are in flight.
 //   * Group lookup: every wave loads the end offsets, one group per lane,
 //     clamps them into a non-decreasing sequence, and forms the padded sizes
 //     and their prefix sums with DPP scans; a ballot over the cumulative unit
-//     counts names the group of the unit. G > 64 is handled in 64-lane slices
-//     with a carry.
+//     counts (M) or over the groups' column ranges (K) names the group(s) of
+//     the unit. G > 64 is handled in 64-lane slices with a carry.
 //   * Load: the unit's source bytes are fetched as 16-byte aligned pieces
 //     (buffer_load_dwordx4) covering each row segment (or, for packed narrow
 //     rows, the whole strip as one range) and staged in LDS. A 16-byte aligned
@@ -59,6 +65,14 @@ namespace {
 // LDS small (7 workgroups per CU), which measured faster than wider ones.
 constexpr int kMaxUnitCols = 112;
 constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits M row blocks into
+// K groups: input windows of 256 columns (two 128-byte lines per row when rows
+// are line aligned). A group's tile starts 4*k columns after the group's first
+// column and belongs to the window holding that start, so a window's tiles
+// read up to 3 columns past it.
+constexpr int kWinCols = 256;
+constexpr int kWinSpan = kWinCols + 3;
+constexpr int kWinPieces = (kWinSpan + 30) / 16;   // 16-byte pieces covering a window row at any alignment
+constexpr int kTailColsPerUnit = 128;         // K: tail units per row block = ceil(4G / this)
 constexpr int kTargetUnits = 1024;            // M: split row blocks into chunks until this many units
 constexpr int kFlatMaxCols = 60;              // M: widest packed row staged as one flat range
 constexpr int kMaxPieces = (kMaxUnitCols + 30) / 16;   // 16-byte pieces covering one row segment
@@ -68,11 +82,15 @@ constexpr int kLdsSlack = 16;                 // room for the second word of an 
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // keeps a unit's byte span inside 32-bit buffer offsets
 // Cache policy of the staging loads (buffer instruction bit 1: non-temporal).
-// M strips share at most one line with their neighbour, so they stream; the
-// row segments of neighbouring K units share lines, which stay in L2.
+// M strips share at most one line with their neighbour, so they stream. A K
+// window's own lines are read by no other unit when rows are 128-byte aligned
+// and stream too; the piece past the window (and every piece of rows not so
+// aligned, whose lines straddle windows) is shared and keeps the default
+// policy, so the neighbour finds it in L2.
 constexpr int kFlatLoadPolicy = 2;
 constexpr int kMRowsLoadPolicy = 2;
-constexpr int kKRowsLoadPolicy = 0;
+constexpr int kWindowLoadPolicy = 2;
+constexpr int kSharedLoadPolicy = 0;
 constexpr int k3dLoadPolicy = 2;
 
 // Staging modes; each is its own kernel instantiation.
@@ -80,12 +98,14 @@ enum Mode : int {
   kModeMFlat = 0,   // M groups, packed rows of <= 60 bytes, one contiguous range per 128-row strip
   kModeMRows = 1,   // M groups, one row segment at a time
   kModeMRowsNarrow = 3,  // M groups, one row segment of at most kNarrowUnitCols at a time
-  kModeKRows = 2,   // K groups, one row segment at a time
+  kModeKWindows = 2,  // K groups, column windows of rows that start 128-byte aligned
+  kModeKWindowsAny = 6,  // K groups, column windows of rows at any alignment
   kMode3d = 4,      // per-expert matrices, one row segment at a time, no group lookup
   kMode3dWide = 5,  // the same with twice the threads, for grids of several units per CU slot
 };
 
 constexpr bool is_3d(int mode) { return mode == kMode3d || mode == kMode3dWide; }
+constexpr bool is_k(int mode) { return mode == kModeKWindows || mode == kModeKWindowsAny; }
 
 // Narrow M units (small problems split into many column chunks) get their own
 // instantiation sized for them: fewer loads per lane, fewer registers.
@@ -94,21 +114,25 @@ constexpr int kNarrowUnitCols = 48;
 // block-32 scales of K = 5120): one contiguous output run per row block.
 constexpr int k3dMaxUnitCols = 160;
 // Threads per workgroup, measured per mode: 128 for the small per-unit work of
-// flat strips and narrow chunks, 256 elsewhere; per-expert grids of more than
-// k3dWideUnits units run 512 threads (fewer loads per lane, more units in flight).
+// flat strips and narrow chunks, 256 elsewhere; K windows and per-expert grids
+// of more than k3dWideUnits units run 512 threads (fewer loads per lane, more
+// units in flight).
 constexpr int threads_for(int mode) {
-  return mode == kModeMFlat || mode == kModeMRowsNarrow ? 128 : mode == kMode3dWide ? 512 : 256;
+  return mode == kModeMFlat || mode == kModeMRowsNarrow ? 128 : mode == kMode3dWide || is_k(mode) ? 512 : 256;
 }
 constexpr int64_t k3dWideUnits = 2048;
 constexpr int max_unit_cols_for(int mode) {
-  return mode == kModeMRowsNarrow ? kNarrowUnitCols : is_3d(mode) ? k3dMaxUnitCols : kMaxUnitCols;
+  return mode == kModeMRowsNarrow ? kNarrowUnitCols
+         : is_3d(mode)            ? k3dMaxUnitCols
+         : is_k(mode)             ? kWinSpan
+                                  : kMaxUnitCols;
 }
 constexpr int max_pieces_for(int mode) { return (max_unit_cols_for(mode) + 30) / 16; }
 constexpr int load_policy_for(int mode) {
-  return mode == kModeMFlat ? kFlatLoadPolicy
-         : mode == kModeKRows ? kKRowsLoadPolicy
-         : is_3d(mode)        ? k3dLoadPolicy
-                              : kMRowsLoadPolicy;
+  return mode == kModeMFlat    ? kFlatLoadPolicy
+         : is_k(mode)            ? kSharedLoadPolicy
+         : is_3d(mode)           ? k3dLoadPolicy
+                                 : kMRowsLoadPolicy;
 }
 constexpr int load_iters_for(int mode) {
   return ((mode == kModeMFlat ? kMaxFlatPieces : kTileRows * max_pieces_for(mode)) + threads_for(mode) - 1) /
@@ -122,11 +146,14 @@ constexpr int kMinWavesPerEu = 1;
 static_assert(kMaxUnitCols % 4 == 0 && kMinUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kTileRows * kMaxPitch + kLdsSlack <= 64 * 1024, "LDS per workgroup");
 static_assert(kTileRows * (16 * max_pieces_for(kMode3d) + 4) + kLdsSlack <= 64 * 1024, "LDS per workgroup");
-static_assert(load_iters_for(kModeKRows) <= 8 && load_iters_for(kModeMFlat) <= 8 && load_iters_for(kMode3d) <= 8 &&
-                  load_iters_for(kModeMRowsNarrow) <= 8 && load_iters_for(kModeMRows) <= 8,
+static_assert(load_iters_for(kModeKWindowsAny) <= 8 && load_iters_for(kModeMFlat) <= 8 &&
+                  load_iters_for(kMode3d) <= 8 && load_iters_for(kModeMRowsNarrow) <= 8 &&
+                  load_iters_for(kModeMRows) <= 8,
               "staging unrolled to 8");
 static_assert(k3dMaxUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narrow units");
+static_assert(kTileRows * (16 * kWinPieces + 4) + kLdsSlack <= 64 * 1024, "LDS per workgroup");
+static_assert(kWinPieces * 16 >= kWinCols + 16, "a window row and the piece past it fit one LDS row");
 
 struct Params {
   const uint8_t *src;
@@ -147,6 +174,8 @@ struct Params {
   int trash;           // LDS offset of 16 bytes that staging pieces without data are written to
   int64_t expert_stride;  // per-expert matrices: bytes between experts
   int64_t row_blocks;     // per-expert matrices: 128-row blocks per expert
+  int windows;            // K: column windows per row block (the first units of each)
+  int tail_units;         // K: units per row block that zero-fill its slice of the tail
 };
 
 __device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
@@ -155,38 +184,32 @@ __device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgc
 // group scan and lookup
 // ---------------------------------------------------------------------------
 
-// Where a work unit sits among the groups. Group sizes are counted in rows (M)
-// or scale columns (K); "units" are 128-row blocks (M) or unit_cols-column
-// chunks of one 128-row block (K).
+// Where an M output row block sits among the groups: group sizes in rows,
+// units are 128-row blocks.
 struct GroupHit {
-  int group;        // index of the group holding the unit; == groups for the tail
-  int start;        // first input row (M) / column (K) of the group
-  int size;         // rows (M) / columns (K) of the group
-  int first_unit;   // units of all earlier groups (all groups, for the tail)
-  int padded_start; // K: padded columns of all earlier groups (all groups, for the tail)
+  int group;        // index of the group holding the block; == groups for the tail
+  int start;        // first input row of the group
+  int size;         // rows of the group
+  int first_unit;   // row blocks of all earlier groups (all groups, for the tail)
 };
 
 // Scans the cumulative end offsets in 64-lane slices and finds the group that
-// holds unit `target`. limit = rows (M) or cols (K): each end offset is clamped
-// into [previous end, limit], which leaves valid offsets unchanged and keeps
-// every access in bounds for invalid ones. Every lane of the wave must call it.
-template <bool KGROUPS>
-__device__ __forceinline__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int limit,
-                                               int unit_cols, int target) {
+// holds output row block `target`. Each end offset is clamped into
+// [previous end, rows], which leaves valid offsets unchanged and keeps every
+// access in bounds for invalid ones. Every lane of the wave must call it.
+__device__ __forceinline__ GroupHit find_group(const int32_t *__restrict__ offs, int groups, int rows, int target) {
   const int lane = threadIdx.x & (kWave - 1);
-  int carry_end = 0, carry_units = 0, carry_padded = 0;
+  int carry_end = 0, carry_units = 0;
   for (int base = 0; base < groups; base += kWave) {
     const int g = base + lane;
     const bool active = g < groups;
     int end = active ? offs[g] : 0;
-    end = min(max(end, 0), limit);
+    end = min(max(end, 0), rows);
     end = max(wave_inclusive_max(end), carry_end);
     const int prev = wave_shift_up(end, carry_end);
     const int size = end - prev;                       // 0 for lanes past the last group
-    const int padded = KGROUPS ? (size + 3) & ~3 : 0;  // K: width padded to 4 columns
-    const int units = KGROUPS ? (padded + unit_cols - 1) / unit_cols : (size + kTileRows - 1) / kTileRows;
+    const int units = (size + kTileRows - 1) / kTileRows;
     const int cum_units = wave_inclusive_sum(units) + carry_units;
-    const int cum_padded = KGROUPS ? wave_inclusive_sum(padded) + carry_padded : 0;
     const unsigned long long before = __ballot(active && cum_units <= target);
     const int n = __popcll(before);
     if (n < min(kWave, groups - base)) {
@@ -195,20 +218,45 @@ __device__ __forceinline__ GroupHit find_group(const int32_t *__restrict__ offs,
       h.start = lane_value(prev, n);
       h.size = lane_value(size, n);
       h.first_unit = lane_value(cum_units, n) - lane_value(units, n);
-      h.padded_start = KGROUPS ? lane_value(cum_padded, n) - lane_value(padded, n) : 0;
       return h;
     }
     carry_end = lane_value(end, kWave - 1);
     carry_units = lane_value(cum_units, kWave - 1);
-    carry_padded = KGROUPS ? lane_value(cum_padded, kWave - 1) : 0;
   }
   GroupHit h;
   h.group = groups;
   h.start = carry_end;
   h.size = 0;
   h.first_unit = carry_units;
-  h.padded_start = carry_padded;
   return h;
+}
+
+// K groups: one 64-group slice of the group table, per lane (group base +
+// lane): first column, end column, width padded to 4, and the padded widths of
+// all earlier groups. end_raw is the lane's end offset (any value past the last
+// group); the ends are clamped into a non-decreasing sequence in [0, cols].
+struct KSlice {
+  int start, end, width, before;
+};
+
+__device__ __forceinline__ KSlice k_slice(int end_raw, int base, int groups, int cols, int carry_end,
+                                          int carry_width) {
+  const bool active = base + int(threadIdx.x & (kWave - 1)) < groups;
+  int e = active ? min(max(end_raw, 0), cols) : 0;
+  e = max(wave_inclusive_max(e), carry_end);
+  KSlice s;
+  s.start = wave_shift_up(e, carry_end);
+  s.end = e;
+  s.width = active ? (e - s.start + 3) & ~3 : 0;
+  s.before = wave_inclusive_sum(s.width) + carry_width - s.width;
+  return s;
+}
+
+// End offset g through a buffer resource over the G offsets: 0 past the last
+// group, by the buffer's range check rather than a branch (a load under a
+// branch is waited for where the branch ends, not where it is used).
+__device__ __forceinline__ int end_offset(__amdgpu_buffer_rsrc_t offs, int g) {
+  return __builtin_amdgcn_raw_buffer_load_b32(offs, 4 * g, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -352,13 +400,57 @@ __device__ __forceinline__ void stage_flat(uint8_t *__restrict__ lds, int trash,
   stage_flat_upto<NT, ITERS, POLICY>((n + NT - 1) / NT, lds, trash, rsrc, n);
 }
 
+// Window staging for rows that start 128-byte aligned: LDS row r gets bytes
+// [0, kWinCols) of the window row, lines no other unit reads, loaded with
+// POLICY, and, when `extra`, bytes [kWinCols, kWinCols + 16), the first
+// columns of the next window, loaded first and with the shared policy. Rows
+// past nrows load zeros. `between` runs once every load is issued and before
+// any is waited for.
+template <int NT, int POLICY, typename F>
+__device__ __forceinline__ void stage_window(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
+                                             int64_t ld, int nrows, bool extra, int pitch, F &&between) {
+  constexpr int kPieces = kWinCols / 16;
+  constexpr int kMain = kTileRows * kPieces / NT;
+  static_assert(kTileRows * kPieces % NT == 0 && NT >= kTileRows, "window staging covers 128 rows");
+  const int re = int(threadIdx.x);
+  const uint4 x = load16<kSharedLoadPolicy>(
+      rsrc, extra && re < nrows ? uint32_t(re) * uint32_t(ld) + kWinCols : kOutOfRange);
+  uint4 v[kMain];
+#pragma unroll
+  for (int it = 0; it < kMain; ++it) {
+    const int q = int(threadIdx.x) + NT * it;
+    const int r = q / kPieces, k = q % kPieces;
+    v[it] = load16<POLICY>(rsrc, r < nrows ? uint32_t(r) * uint32_t(ld) + 16 * k : kOutOfRange);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before `between` starts
+  between();
+  // every piece is written (the piece past the window, when there is none, to
+  // the trash bytes), see stage_rows_n; LDS rows are 4-byte aligned
+  uint32_t *d = reinterpret_cast<uint32_t *>(lds + (extra && re < kTileRows ? re * pitch + kWinCols : trash));
+  d[0] = x.x;
+  d[1] = x.y;
+  d[2] = x.z;
+  d[3] = x.w;
+#pragma unroll
+  for (int it = 0; it < kMain; ++it) {
+    const int q = int(threadIdx.x) + NT * it;
+    d = reinterpret_cast<uint32_t *>(lds + (q / kPieces) * pitch + 16 * (q % kPieces));
+    d[0] = v[it].x;
+    d[1] = v[it].y;
+    d[2] = v[it].z;
+    d[3] = v[it].w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // emitting tiles from LDS
 // ---------------------------------------------------------------------------
 
 // Writes `tile_cols` tiles (128 rows x 4 columns each) contiguously at dst.
 // Row r, column c of the unit is LDS byte row_off(r) + c with
-// row_off(r) = first + r*row_step (FLAT) or r*row_step + (addr + r*ld) mod 16.
+// row_off(r) = first + r*row_step (FLAT) or first + r*row_step + (addr + r*ld)
+// mod 16 (per-row staging, where `first` is the unit's column in the staged
+// segment).
 // Rows >= nrows and columns >= ncols are written as zero.
 template <int NT, bool FLAT, bool ALIGNED>
 __device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__restrict__ dst,
@@ -377,11 +469,8 @@ __device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ lds, uint
       const int r = i + 32 * q;
       uint32_t x = 0;
       if (r < nrows) {
-        int b = r * row_step + 4 * tc;
-        if (FLAT)
-          b += first;
-        else
-          b += int((uint32_t(addr) + uint32_t(r) * uint32_t(ld)) & 15u);  // (addr + r*ld) mod 16
+        int b = first + r * row_step + 4 * tc;
+        if (!FLAT) b += int((uint32_t(addr) + uint32_t(r) * uint32_t(ld)) & 15u);  // (addr + r*ld) mod 16
         if (ALIGNED) {
           x = w32[b >> 2];
         } else {
@@ -421,6 +510,66 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
     emit_tiles<NT, FLAT, false>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
 }
 
+// K groups: the unit of 128-row block `block` and input window `slot` (columns
+// [W*slot, W*slot + W) with W = kWinCols, plus up to 3 past it). The window's
+// loads go out first; the first 64 end offsets (end_raw, loaded before them)
+// are scanned while they are in flight. Then, for every group with a tile
+// starting in the window, the run of those tiles is written at the group's
+// place: group g's blocked matrix starts at byte padded_rows * (padded widths
+// before g), its row block `block` 128 * width_g bytes further per block, tile
+// k 512*k on.
+template <int NT, bool LINE_ALIGNED>
+__device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Params &p, int64_t block, int slot,
+                                            __amdgpu_buffer_rsrc_t offs, int end_raw, int64_t padded_rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c_lo = slot * kWinCols;                     // < cols
+  const int64_t c_hi = int64_t(c_lo) + kWinCols;
+  const int nrows = min(kTileRows, p.rows - kTileRows * int(block));
+  const int seg = int(std::min<int64_t>(kWinSpan, int64_t(p.cols) - c_lo));
+  const uint8_t *row_base = p.src + block * kTileRows * p.ld + c_lo;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row_base);
+  KSlice first;
+  auto scan = [&] { first = k_slice(end_raw, 0, p.groups, p.cols, 0, 0); };
+  if constexpr (LINE_ALIGNED) {
+    const uint32_t span = uint32_t((int64_t(nrows - 1) * p.ld + seg + 15) & ~int64_t(15));
+    stage_window<NT, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > kWinCols,
+                                        p.pitch, scan);
+  } else {
+    scan();
+    stage_rows<NT, load_iters_for(kModeKWindowsAny), kSharedLoadPolicy>(lds, p.trash, row_base, p.ld, nrows, seg,
+                                                                        p.pitch, p.pieces);
+  }
+  __syncthreads();
+  const bool aligned = ((a | uintptr_t(p.ld)) & 3) == 0;
+  int carry_end = 0, carry_width = 0;
+  for (int base = 0; base < p.groups; base += kWave) {
+    const KSlice sl = base == 0 ? first
+                                : k_slice(end_offset(offs, base + lane), base, p.groups, p.cols, carry_end,
+                                          carry_width);
+    // a group has a tile starting in the window iff its first tile starts
+    // before the window ends and its last tile (at start + width - 4) does
+    // not start before the window
+    const bool hit = base + lane < p.groups && sl.width > 0 && sl.start < c_hi &&
+                     sl.start + sl.width - 4 >= c_lo;
+    for (unsigned long long m = __ballot(hit); m != 0; m &= m - 1) {
+      const int n = __builtin_ctzll(m);
+      const int gs = lane_value(sl.start, n), ge = lane_value(sl.end, n);
+      const int gw = lane_value(sl.width, n), gb = lane_value(sl.before, n);
+      const int k_lo = gs >= c_lo ? 0 : (c_lo - gs + 3) >> 2;
+      const int k_hi = int(std::min<int64_t>(gw >> 2, (c_hi - gs + 3) >> 2));
+      const int col0 = gs + 4 * k_lo;                   // first column of the run, in the window
+      uint8_t *dst = p.out + padded_rows * gb + block * kTileRows * gw + int64_t(512) * k_lo;
+      if (aligned && ((col0 - c_lo) & 3) == 0)
+        emit_tiles<NT, false, true>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
+      else
+        emit_tiles<NT, false, false>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
+    }
+    carry_end = lane_value(sl.end, kWave - 1);
+    carry_width = lane_value(sl.before + sl.width, kWave - 1);
+    if (carry_end >= c_hi) break;  // later groups start past the window
+  }
+}
+
 // ---------------------------------------------------------------------------
 // the kernel: one work unit per workgroup (a grid-stride loop only when the
 // grid is capped). A workgroup ends as soon as its stores are issued, so the
@@ -431,7 +580,7 @@ template <int MODE>
 __global__ __launch_bounds__(threads_for(MODE)) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu)))
 void rearrange_kernel(Params p) {
   constexpr int NT = threads_for(MODE);
-  constexpr bool KGROUPS = MODE == kModeKRows;
+  constexpr bool KGROUPS = is_k(MODE);
   extern __shared__ __align__(16) uint8_t lds[];
   bool first_iter = true;
   for (int64_t vb = blockIdx.x; vb < p.vunits; vb += gridDim.x) {
@@ -459,7 +608,7 @@ void rearrange_kernel(Params p) {
         copy_unit<MODE>(lds, p, p.src + e * p.expert_stride + int64_t(kTileRows) * rb * p.ld + c0, nrows, ncols,
                         tile_cols, dst);
     } else if constexpr (!KGROUPS) {
-      const GroupHit h = find_group<false>(p.offs, p.groups, p.rows, p.unit_cols, int(block));
+      const GroupHit h = find_group(p.offs, p.groups, p.rows, int(block));
       const int64_t row_block_bytes = int64_t(kTileRows) * p.padded_cols;
       if (h.group < p.groups) {
         const int k = int(block) - h.first_unit;
@@ -480,27 +629,28 @@ void rearrange_kernel(Params p) {
         zero_part<NT>(p.out, int64_t(h.first_unit) * row_block_bytes, p.out_bytes, tail_index, tail_units);
       }
     } else {
-      const GroupHit h = find_group<true>(p.offs, p.groups, p.cols, p.unit_cols, slot);
+      // the end offsets of the first 64 groups are loaded ahead of everything
+      // else, so that waiting for them does not wait for the strip loads
+      const __amdgpu_buffer_rsrc_t offs = byte_buffer(p.offs, 4 * uint32_t(p.groups));
+      const int end_raw = end_offset(offs, int(threadIdx.x & (kWave - 1)));
+      __builtin_amdgcn_sched_barrier(0);
       const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
-      if (h.group < p.groups) {
-        const int chunk = slot - h.first_unit;
-        const int padded_width = (h.size + 3) & ~3;
-        const int c0 = h.start + chunk * p.unit_cols;
-        const int nrows = min(kTileRows, p.rows - kTileRows * int(block));
-        // the min() with cols - c0 only restates what a correct scan guarantees
-        const int ncols = min(min(p.unit_cols, h.size - chunk * p.unit_cols), p.cols - c0);
-        const int tile_cols = min(p.unit_cols, padded_width - chunk * p.unit_cols) >> 2;
-        uint8_t *dst = p.out + padded_rows * h.padded_start + block * kTileRows * padded_width +
-                       int64_t(chunk) * p.unit_cols * kTileRows;
-        // the last condition, too, holds for every unit of a correct scan
-        if (nrows > 0 && ncols > 0 && padded_rows * (h.padded_start + padded_width) <= p.out_bytes)
-          copy_unit<MODE>(lds, p, p.src + block * kTileRows * p.ld + c0, nrows, ncols, tile_cols, dst);
+      if (slot < p.windows) {
+        window_unit<NT, MODE == kModeKWindows>(lds, p, block, slot, offs, end_raw, padded_rows);
       } else {
         // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
         // 128 * (cols + 4G - padded total) slice per 128-row block
-        const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - h.padded_start;
-        const int64_t lo = padded_rows * h.padded_start + block * kTileRows * tail_cols;
-        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, slot - h.first_unit, p.per_row - h.first_unit);
+        const int lane = threadIdx.x & (kWave - 1);
+        int carry_end = 0, carry_width = 0;
+        for (int base = 0; base < p.groups; base += kWave) {
+          const KSlice sl = k_slice(base == 0 ? end_raw : end_offset(offs, base + lane), base, p.groups, p.cols,
+                                    carry_end, carry_width);
+          carry_end = lane_value(sl.end, kWave - 1);
+          carry_width = lane_value(sl.before + sl.width, kWave - 1);
+        }
+        const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - carry_width;
+        const int64_t lo = padded_rows * carry_width + block * kTileRows * tail_cols;
+        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, slot - p.windows, p.tail_units);
       }
     }
   }
@@ -559,10 +709,13 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
     p.per_row = (p.padded_cols + p.unit_cols - 1) / p.unit_cols;
     units = blocks * p.per_row;
   } else {
-    mode = kModeKRows;
-    p.unit_cols = kMaxUnitCols;
-    // units per 128-row block: every group's chunks plus at least one of tail
-    p.per_row = int((cols + 4 * int64_t(groups) + p.unit_cols - 1) / p.unit_cols + groups);
+    // windows stream their own lines when every row starts on a 128-byte line
+    mode = ((reinterpret_cast<uintptr_t>(scales) | uintptr_t(ld)) & 127) == 0 ? kModeKWindows : kModeKWindowsAny;
+    p.unit_cols = kWinCols;
+    // units per 128-row block: its input windows, then the tail units
+    p.windows = int((cols + kWinCols - 1) / kWinCols);
+    p.tail_units = int((4 * int64_t(groups) + kTailColsPerUnit - 1) / kTailColsPerUnit);
+    p.per_row = p.windows + p.tail_units;
     units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
   return dispatch(p, mode, units, stream);
@@ -604,7 +757,9 @@ int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
 }
 
 int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
-  const int64_t seg = std::min<int64_t>(p.cols, p.unit_cols);   // widest row segment of a unit
+  // widest row segment of a unit; K windows always get room for a whole
+  // window row and the piece past it
+  const int64_t seg = is_k(mode) ? kWinSpan : std::min<int64_t>(p.cols, p.unit_cols);
   p.pieces = std::max<int>(1, int((seg + 30) / 16));
   p.pitch = 16 * p.pieces + 4;
   p.units = units;
@@ -621,7 +776,8 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
                    : mode == kModeMRowsNarrow ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow>)
                    : mode == kMode3d    ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3d>)
                    : mode == kMode3dWide ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3dWide>)
-                                        : reinterpret_cast<const void *>(&rearrange_kernel<kModeKRows>);
+                   : mode == kModeKWindows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows>)
+                                        : reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsAny>);
   const int threads = threads_for(mode);
   // one workgroup per unit; the grid is a multiple of 8, so a workgroup that
   // loops (only past kMaxGrid units) stays on its XCD

@@ -141,6 +141,23 @@ def test_fuzz_K(env):
     _fuzz(env, "K", 32, 120)
 
 
+def test_fuzz_K_line_aligned_rows(env):
+    """K groups over rows that start on 128-byte lines (the streaming window path): widths spanning
+    several column windows, group starts at any column (tiles straddling window edges), up to 130 groups."""
+    import workloads
+
+    rng = np.random.default_rng(34)
+    for i in range(60):
+        rows = int(rng.choice([1, 5, 127, 128, 129, 300, 1000]))
+        cols = int(rng.choice([3, 100, 255, 256, 257, 259, 300, 513, 768, 1031, 2000, 4097]))
+        ld = (cols + 127) // 128 * 128 + 128 * int(rng.choice([0, 0, 1, 7]))
+        G = int(rng.choice([1, 2, 3, 8, 16, 64, 65, 130]))
+        offs = workloads.random_offsets(rng, cols, G, p_empty=float(rng.choice([0.0, 0.3])),
+                                        short_total=bool(rng.random() < 0.2))
+        A = workloads.random_scales(rng, rows, cols, ld)
+        run_case(env, "K", A, offs, misalign=0, label="fuzzK-lines-%d" % i)
+
+
 @pytest.mark.parametrize("kind", ["M", "K"])
 def test_wide_and_odd_shapes(env, kind):
     rng = np.random.default_rng(33)

@@ -41,8 +41,9 @@ DEFAULT_WORKLOAD = "m_groups_skinny"
 # input doesn't meet 2d TMA constraints", Benchmarks table). GPU not named on the page.
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
 # kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
-# 3 = M narrow row segments, 2 = K row segments
-# 4 = per-expert row segments, 5 = the same with 512 threads (grids of more than 2048 units)
+# 3 = M narrow row segments, 2 = K column windows of rows on 128-byte lines (6: rows at
+# any other alignment), 4 = per-expert row segments, 5 = the same with 512 threads (grids
+# of more than 2048 units)
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
                 "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",

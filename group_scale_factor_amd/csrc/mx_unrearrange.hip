@@ -183,7 +183,9 @@ __device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const ui
 
 // Writes rows [0, nrows) x bytes [skip, skip + ncols) of the LDS strip (row r
 // from lds + r*pitch words) to dst, row r at dst + r*ld (ld unused when nrows
-// is 1). Called by the whole workgroup.
+// is 1). Called by the whole workgroup. NT: the 16-byte chunk stores are
+// non-temporal (measured faster for M units, slower for K units).
+template <bool NT>
 __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int skip, int nrows, int ncols,
                                            uint8_t *dst, int64_t ld) {
   // Store. Split each row segment by its alignment: up to 3 single bytes, up
@@ -211,7 +213,10 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
     } else {
       v = u32x4{w[0], w[1], w[2], w[3]};
     }
-    *reinterpret_cast<u32x4 *>(row_ptr + lo) = v;
+    if (NT)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(row_ptr + lo));
+    else
+      *reinterpret_cast<u32x4 *>(row_ptr + lo) = v;
   }
   if ((dst_bits & 15) != 0 || (ncols & 15) != 0) {
     for (int s = threadIdx.x; s < nrows * 6; s += kUThreads) {
@@ -242,14 +247,15 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
 // ncols) to dst, row r at dst + r*ld. When the rows are contiguous (ld ==
 // ncols) and whole words, the strip is packed with pitch ncols/4 and the unit's
 // output is stored as one segment of nrows*ncols bytes.
+template <bool NT>
 __device__ __forceinline__ void unit_out(uint32_t *lds, const uint4 (&v)[kULoads], int skip, int tile_cols, int nrows,
                                          int ncols, uint8_t *dst, int64_t ld) {
   if (skip == 0 && ld == ncols && (ncols & 3) == 0) {
     scatter_strip(lds, ncols >> 2, v, tile_cols);
-    store_rows(lds, 0, 0, 1, nrows * ncols, dst, 0);
+    store_rows<NT>(lds, 0, 0, 1, nrows * ncols, dst, 0);
   } else {
     scatter_strip(lds, kUPitch, v, tile_cols);
-    store_rows(lds, kUPitch, skip, nrows, ncols, dst, ld);
+    store_rows<NT>(lds, kUPitch, skip, nrows, ncols, dst, ld);
   }
 }
 
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       uint4 v[kULoads];
       issue_loads(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
                   uint32_t(tile_cols) * 512u);
-      unit_out(strip, v, 0, tile_cols, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
+      unit_out<true>(strip, v, 0, tile_cols, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
     } else {
       // spare units: zero the rows after the last group
       const int64_t first_spare = grp.pend_at(p.groups - 1) / kTileRows;
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       const int tile_cols = ((lc & 3) + ncols + 3) >> 2;
       uint4 v[kULoads];
       issue_loads(v, src, tile_cols, uint32_t(tile_cols) * 512u);
-      unit_out(strip, v, lc & 3, tile_cols, nrows, ncols, p.out + rb * kTileRows * p.ld + a, p.ld);
+      unit_out<false>(strip, v, lc & 3, tile_cols, nrows, ncols, p.out + rb * kTileRows * p.ld + a, p.ld);
     } else {
       // spare slots of this row block: zero its rows' columns after the last group
       zero_region(p.out, p.ld, rb * kTileRows, rb * kTileRows + nrows, grp.end(p.groups - 1), p.cols,

@@ -53,6 +53,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "group_table.h"
 #include "mx_rearrange.h"
@@ -70,8 +71,7 @@ constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits
 // column and belongs to the window holding that start, so a window's tiles
 // read up to 3 columns past it.
 constexpr int kWinCols = 256;
-constexpr int kWinSpan = kWinCols + 3;
-constexpr int kWinPieces = (kWinSpan + 30) / 16;   // 16-byte pieces covering a window row at any alignment
+constexpr int kWinColsAny = 128;              // windows of rows that do not start on 128-byte lines
 constexpr int kTailColsPerUnit = 128;         // K: tail units per row block = ceil(4G / this)
 constexpr int kTargetUnits = 1024;            // M: split row blocks into chunks until this many units
 constexpr int kFlatMaxCols = 60;              // M: widest packed row staged as one flat range
@@ -106,6 +106,10 @@ enum Mode : int {
 
 constexpr bool is_3d(int mode) { return mode == kMode3d || mode == kMode3dWide; }
 constexpr bool is_k(int mode) { return mode == kModeKWindows || mode == kModeKWindowsAny; }
+constexpr int win_cols_for(int mode) { return mode == kModeKWindows ? kWinCols : kWinColsAny; }
+constexpr int win_span_for(int mode) { return win_cols_for(mode) + 3; }
+// 16-byte pieces covering a window row (and the 3 columns past it) at any alignment
+constexpr int win_pieces_for(int mode) { return (win_span_for(mode) + 30) / 16; }
 
 // Narrow M units (small problems split into many column chunks) get their own
 // instantiation sized for them: fewer loads per lane, fewer registers.
@@ -114,17 +118,19 @@ constexpr int kNarrowUnitCols = 48;
 // block-32 scales of K = 5120): one contiguous output run per row block.
 constexpr int k3dMaxUnitCols = 160;
 // Threads per workgroup, measured per mode: 128 for the small per-unit work of
-// flat strips and narrow chunks, 256 elsewhere; K windows and per-expert grids
-// of more than k3dWideUnits units run 512 threads (fewer loads per lane, more
-// units in flight).
+// flat strips and narrow chunks, 256 elsewhere; K windows of line-aligned rows
+// and per-expert grids of more than k3dWideUnits units run 512 threads (fewer
+// loads per lane, more units in flight).
 constexpr int threads_for(int mode) {
-  return mode == kModeMFlat || mode == kModeMRowsNarrow ? 128 : mode == kMode3dWide || is_k(mode) ? 512 : 256;
+  return mode == kModeMFlat || mode == kModeMRowsNarrow       ? 128
+         : mode == kMode3dWide || mode == kModeKWindows ? 512
+                                                        : 256;
 }
 constexpr int64_t k3dWideUnits = 2048;
 constexpr int max_unit_cols_for(int mode) {
   return mode == kModeMRowsNarrow ? kNarrowUnitCols
          : is_3d(mode)            ? k3dMaxUnitCols
-         : is_k(mode)             ? kWinSpan
+         : is_k(mode)             ? win_span_for(mode)
                                   : kMaxUnitCols;
 }
 constexpr int max_pieces_for(int mode) { return (max_unit_cols_for(mode) + 30) / 16; }
@@ -152,8 +158,11 @@ static_assert(load_iters_for(kModeKWindowsAny) <= 8 && load_iters_for(kModeMFlat
               "staging unrolled to 8");
 static_assert(k3dMaxUnitCols % 4 == 0, "units are whole tile columns");
 static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narrow units");
-static_assert(kTileRows * (16 * kWinPieces + 4) + kLdsSlack <= 64 * 1024, "LDS per workgroup");
-static_assert(kWinPieces * 16 >= kWinCols + 16, "a window row and the piece past it fit one LDS row");
+static_assert(kTileRows * (16 * win_pieces_for(kModeKWindows) + 4) + kLdsSlack <= 64 * 1024 &&
+                  kTileRows * (16 * win_pieces_for(kModeKWindowsAny) + 4) + kLdsSlack <= 64 * 1024,
+              "LDS per workgroup");
+static_assert(win_pieces_for(kModeKWindows) * 16 >= kWinCols + 16,
+              "a window row and the piece past it fit one LDS row");
 
 struct Params {
   const uint8_t *src;
@@ -299,10 +308,16 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t of
 // fetched as the 16-byte pieces covering it into LDS row r (pitch bytes); its
 // first byte then sits at r*pitch + (a mod 16). Piece slot s = r*pieces + k
 // goes to lane s mod NT; each lane issues exactly N loads back to back (N =
-// slots per lane of this unit) before it waits for any of them.
-template <int NT, int N, int POLICY>
+// slots per lane of this unit) before it waits for any of them. `between`
+// runs once they are issued, before the first wait.
+struct Nothing {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <int NT, int N, int POLICY, typename F>
 __device__ __forceinline__ void stage_rows_n(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
-                                             uint32_t lead, int64_t ld, int nrows, int seg, int pitch, int pieces) {
+                                             uint32_t lead, int64_t ld, int nrows, int seg, int pitch, int pieces,
+                                             F &between) {
   const int step_r = NT / pieces, step_k = NT % pieces;
   const int r0 = threadIdx.x / pieces, k0 = threadIdx.x % pieces;
   uint4 v[N];
@@ -316,6 +331,10 @@ __device__ __forceinline__ void stage_rows_n(uint8_t *__restrict__ lds, int tras
     r += step_r;
     k += step_k;
     if (k >= pieces) { k -= pieces; ++r; }
+  }
+  if constexpr (!std::is_same<F, Nothing>::value) {
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before `between` starts
+    between();
   }
   // The same walk again (cheaper than keeping N offsets live across the
   // loads). Every piece is written, slots without data to the trash bytes at
@@ -340,28 +359,28 @@ __device__ __forceinline__ void stage_rows_n(uint8_t *__restrict__ lds, int tras
 }
 
 // Runs stage_rows_n with the smallest N >= n (n uniform, 1 <= n <= N).
-template <int NT, int N, int POLICY>
+template <int NT, int N, int POLICY, typename F>
 __device__ __forceinline__ void stage_rows_upto(int n, uint8_t *__restrict__ lds, int trash,
                                                 __amdgpu_buffer_rsrc_t rsrc, uint32_t lead, int64_t ld, int nrows,
-                                                int seg, int pitch, int pieces) {
+                                                int seg, int pitch, int pieces, F &between) {
   if constexpr (N > 1) {
     if (n < N) {
-      stage_rows_upto<NT, N - 1, POLICY>(n, lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces);
+      stage_rows_upto<NT, N - 1, POLICY>(n, lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces, between);
       return;
     }
   }
-  stage_rows_n<NT, N, POLICY>(lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces);
+  stage_rows_n<NT, N, POLICY>(lds, trash, rsrc, lead, ld, nrows, seg, pitch, pieces, between);
 }
 
-template <int NT, int ITERS, int POLICY>
+template <int NT, int ITERS, int POLICY, typename F = Nothing>
 __device__ __forceinline__ void stage_rows(uint8_t *__restrict__ lds, int trash, const uint8_t *row_base, int64_t ld,
-                                           int nrows, int seg, int pitch, int pieces) {
+                                           int nrows, int seg, int pitch, int pieces, F &&between = F()) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(row_base) & 15);
   const uint8_t *base = row_base - lead;  // 16-byte aligned
   const uint32_t span = uint32_t((lead + int64_t(nrows - 1) * ld + seg + 15) & ~int64_t(15));
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(base, span);
   stage_rows_upto<NT, ITERS, POLICY>((nrows * pieces + NT - 1) / NT, lds, trash, rsrc, lead, ld, nrows, seg, pitch,
-                                     pieces);
+                                     pieces, between);
 }
 
 // Flat staging: the strip is one contiguous range [a, a + len); its 16-byte
@@ -372,7 +391,8 @@ __device__ __forceinline__ void stage_flat_n(uint8_t *__restrict__ lds, int tras
   const int t = threadIdx.x;
   uint4 v[N];
 #pragma unroll
-  for (int it = 0; it < N; ++it) v[it] = load16<POLICY>(rsrc, t + it * NT < n ? uint32_t(16 * (t + it * NT)) : kOutOfRange);
+  for (int it = 0; it < N; ++it)
+    v[it] = load16<POLICY>(rsrc, t + it * NT < n ? uint32_t(16 * (t + it * NT)) : kOutOfRange);
   // every piece is written (past the strip: to the trash bytes), see stage_rows_n
 #pragma unroll
   for (int it = 0; it < N; ++it)
@@ -511,33 +531,34 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
 }
 
 // K groups: the unit of 128-row block `block` and input window `slot` (columns
-// [W*slot, W*slot + W) with W = kWinCols, plus up to 3 past it). The window's
-// loads go out first; the first 64 end offsets (end_raw, loaded before them)
-// are scanned while they are in flight. Then, for every group with a tile
-// starting in the window, the run of those tiles is written at the group's
-// place: group g's blocked matrix starts at byte padded_rows * (padded widths
-// before g), its row block `block` 128 * width_g bytes further per block, tile
-// k 512*k on.
-template <int NT, bool LINE_ALIGNED>
+// [W*slot, W*slot + W) with W the mode's window width, plus up to 3 past it).
+// The window's loads go out first; the first 64 end offsets (end_raw, loaded
+// before them) are scanned while they are in flight. Then, for every group with
+// a tile starting in the window, the run of those tiles is written at the
+// group's place: group g's blocked matrix starts at byte padded_rows * (padded
+// widths before g), its row block `block` 128 * width_g bytes further per
+// block, tile k 512*k on.
+template <int NT, int MODE>
 __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Params &p, int64_t block, int slot,
                                             __amdgpu_buffer_rsrc_t offs, int end_raw, int64_t padded_rows) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int c_lo = slot * kWinCols;                     // < cols
-  const int64_t c_hi = int64_t(c_lo) + kWinCols;
+  constexpr bool LINE_ALIGNED = MODE == kModeKWindows;
+  constexpr int W = win_cols_for(MODE);
+  const int c_lo = slot * W;                            // < cols
+  const int64_t c_hi = int64_t(c_lo) + W;
   const int nrows = min(kTileRows, p.rows - kTileRows * int(block));
-  const int seg = int(std::min<int64_t>(kWinSpan, int64_t(p.cols) - c_lo));
+  const int seg = int(std::min<int64_t>(win_span_for(MODE), int64_t(p.cols) - c_lo));
   const uint8_t *row_base = p.src + block * kTileRows * p.ld + c_lo;
   const uintptr_t a = reinterpret_cast<uintptr_t>(row_base);
   KSlice first;
   auto scan = [&] { first = k_slice(end_raw, 0, p.groups, p.cols, 0, 0); };
   if constexpr (LINE_ALIGNED) {
     const uint32_t span = uint32_t((int64_t(nrows - 1) * p.ld + seg + 15) & ~int64_t(15));
-    stage_window<NT, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > kWinCols,
+    stage_window<NT, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > W,
                                         p.pitch, scan);
   } else {
-    scan();
-    stage_rows<NT, load_iters_for(kModeKWindowsAny), kSharedLoadPolicy>(lds, p.trash, row_base, p.ld, nrows, seg,
-                                                                        p.pitch, p.pieces);
+    stage_rows<NT, load_iters_for(MODE), kSharedLoadPolicy>(lds, p.trash, row_base, p.ld, nrows, seg, p.pitch,
+                                                            p.pieces, scan);
   }
   __syncthreads();
   const bool aligned = ((a | uintptr_t(p.ld)) & 3) == 0;
@@ -636,7 +657,7 @@ void rearrange_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
       if (slot < p.windows) {
-        window_unit<NT, MODE == kModeKWindows>(lds, p, block, slot, offs, end_raw, padded_rows);
+        window_unit<NT, MODE>(lds, p, block, slot, offs, end_raw, padded_rows);
       } else {
         // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
         // 128 * (cols + 4G - padded total) slice per 128-row block
@@ -711,9 +732,9 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   } else {
     // windows stream their own lines when every row starts on a 128-byte line
     mode = ((reinterpret_cast<uintptr_t>(scales) | uintptr_t(ld)) & 127) == 0 ? kModeKWindows : kModeKWindowsAny;
-    p.unit_cols = kWinCols;
+    p.unit_cols = mode == kModeKWindows ? win_cols_for(kModeKWindows) : win_cols_for(kModeKWindowsAny);
     // units per 128-row block: its input windows, then the tail units
-    p.windows = int((cols + kWinCols - 1) / kWinCols);
+    p.windows = int((cols + p.unit_cols - 1) / p.unit_cols);
     p.tail_units = int((4 * int64_t(groups) + kTailColsPerUnit - 1) / kTailColsPerUnit);
     p.per_row = p.windows + p.tail_units;
     units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
@@ -759,7 +780,7 @@ int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
 int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
   // widest row segment of a unit; K windows always get room for a whole
   // window row and the piece past it
-  const int64_t seg = is_k(mode) ? kWinSpan : std::min<int64_t>(p.cols, p.unit_cols);
+  const int64_t seg = is_k(mode) ? p.unit_cols + 3 : std::min<int64_t>(p.cols, p.unit_cols);
   p.pieces = std::max<int>(1, int((seg + 30) / 16));
   p.pitch = 16 * p.pieces + 4;
   p.units = units;

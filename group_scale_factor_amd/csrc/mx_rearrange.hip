@@ -60,10 +60,11 @@
 
 namespace {
 
-// Widest column chunk of a unit: 112 columns are covered by at most 8 aligned
-// 16-byte pieces per row at any alignment, so a 128-row unit is at most 1024
-// pieces, 4 per lane of a 256-thread workgroup. Narrow units keep registers and
-// LDS small (7 workgroups per CU), which measured faster than wider ones.
+// Widest column chunk of an M unit: 112 columns are covered by at most 8
+// aligned 16-byte pieces per row at any alignment, so a 128-row unit is at most
+// 1024 pieces, 4 per lane of a 256-thread workgroup. Narrow units keep
+// registers and LDS small (7 workgroups per CU), which measured faster than
+// wider ones.
 constexpr int kMaxUnitCols = 112;
 constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits M row blocks into
 // K groups: input windows of 256 columns (two 128-byte lines per row when rows
@@ -557,8 +558,8 @@ __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Par
     stage_window<NT, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > W,
                                         p.pitch, scan);
   } else {
-    stage_rows<NT, load_iters_for(MODE), kSharedLoadPolicy>(lds, p.trash, row_base, p.ld, nrows, seg, p.pitch,
-                                                            p.pieces, scan);
+    stage_rows<NT, load_iters_for(MODE), load_policy_for(MODE)>(lds, p.trash, row_base, p.ld, nrows, seg, p.pitch,
+                                                                p.pieces, scan);
   }
   __syncthreads();
   const bool aligned = ((a | uintptr_t(p.ld)) & 3) == 0;

@@ -158,6 +158,29 @@ def test_fuzz_K_line_aligned_rows(env):
         run_case(env, "K", A, offs, misalign=0, label="fuzzK-lines-%d" % i)
 
 
+@pytest.mark.parametrize("line_aligned", [True, False])
+def test_k_window_edges(env, line_aligned):
+    """K groups at the edges of the column windows, on rows that start on 128-byte lines and on rows that do
+    not: a tile straddling a window edge, more than 64 groups inside one window, group starts on both sides of
+    window boundaries, and windows that hold no group (offsets ending before the last column)."""
+    import workloads
+
+    rng = np.random.default_rng(35)
+    cases = [
+        (129, 259, [253, 259]),                                   # tile 253..256 straddles the first edge
+        (130, 512, list(range(1, 201)) + [512]),                  # 200 one-column groups in the first window
+        (128, 1000, [255, 256, 257, 511, 513, 1000]),             # starts on either side of 256 and 512
+        (200, 700, [3, 3, 3, 130]),                               # windows past the last group
+        (1, 300, [0, 0, 299]),                                    # one row, empty leading groups
+        (257, 2049, [1, 2049]),                                   # every tile of the big group misaligned by 1
+    ]
+    for rows, cols, offs in cases:
+        ld = ((cols + 127) // 128 * 128) if line_aligned else cols + 5
+        A = workloads.random_scales(rng, rows, cols, ld)
+        run_case(env, "K", A, np.array(offs, np.int32), misalign=0 if line_aligned else 3,
+                 label="k-window-edges-%s" % ("lines" if line_aligned else "any"))
+
+
 @pytest.mark.parametrize("kind", ["M", "K"])
 def test_wide_and_odd_shapes(env, kind):
     rng = np.random.default_rng(33)

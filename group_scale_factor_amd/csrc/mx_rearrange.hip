@@ -32,7 +32,8 @@
 //     the unit. G > 64 is handled in 64-lane slices with a carry.
 //   * Load: the unit's source bytes are fetched as 16-byte aligned pieces
 //     (buffer_load_dwordx4) covering each row segment (or, for packed narrow
-//     rows, the whole strip as one range) and staged in LDS. A 16-byte aligned
+//     rows, the whole strip as one range, loaded straight into LDS) and staged
+//     in LDS. A 16-byte aligned
 //     piece that contains at least one byte of the matrix lies inside the same
 //     memory page as that byte, so the cover never touches a page the matrix
 //     does not; the extra bytes are never emitted.
@@ -385,40 +386,44 @@ __device__ __forceinline__ void stage_rows(uint8_t *__restrict__ lds, int trash,
 }
 
 // Flat staging: the strip is one contiguous range [a, a + len); its 16-byte
-// cover goes to LDS from offset 0, so byte a sits at LDS (a mod 16).
+// cover goes to LDS from offset 0, so byte a sits at LDS (a mod 16). The
+// pieces go straight into LDS: a buffer load with the LDS flag writes lane l's
+// 16 bytes at the wave's LDS base (m0) + 16*l, which with the wave's base at
+// its first piece is LDS offset 16*(piece index). Lanes past the cover load
+// nothing.
+typedef __attribute__((address_space(3))) void LdsVoid;   // an LDS address, as the LDS-load builtin takes it
+
 template <int NT, int N, int POLICY>
-__device__ __forceinline__ void stage_flat_n(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
-                                             int n) {
+__device__ __forceinline__ void stage_flat_n(uint8_t *__restrict__ lds, __amdgpu_buffer_rsrc_t rsrc, int n) {
   const int t = threadIdx.x;
-  uint4 v[N];
+  const int wave_first = t & ~(kWave - 1);   // piece of the wave's lane 0 in the first round
 #pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = load16<POLICY>(rsrc, t + it * NT < n ? uint32_t(16 * (t + it * NT)) : kOutOfRange);
-  // every piece is written (past the strip: to the trash bytes), see stage_rows_n
-#pragma unroll
-  for (int it = 0; it < N; ++it)
-    *reinterpret_cast<uint4 *>(lds + (t + it * NT < n ? 16 * (t + it * NT) : trash)) = v[it];
+  for (int it = 0; it < N; ++it) {
+    if (t + it * NT < n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LdsVoid *)(lds + 16 * (wave_first + it * NT)), 16,
+                                               16 * (t + it * NT), 0, 0, POLICY);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every piece has landed in LDS
 }
 
 // Runs stage_flat_n with the smallest N >= m (m uniform, 1 <= m <= N).
 template <int NT, int N, int POLICY>
-__device__ __forceinline__ void stage_flat_upto(int m, uint8_t *__restrict__ lds, int trash,
-                                                __amdgpu_buffer_rsrc_t rsrc, int n) {
+__device__ __forceinline__ void stage_flat_upto(int m, uint8_t *__restrict__ lds, __amdgpu_buffer_rsrc_t rsrc, int n) {
   if constexpr (N > 1) {
     if (m < N) {
-      stage_flat_upto<NT, N - 1, POLICY>(m, lds, trash, rsrc, n);
+      stage_flat_upto<NT, N - 1, POLICY>(m, lds, rsrc, n);
       return;
     }
   }
-  stage_flat_n<NT, N, POLICY>(lds, trash, rsrc, n);
+  stage_flat_n<NT, N, POLICY>(lds, rsrc, n);
 }
 
 template <int NT, int ITERS, int POLICY>
-__device__ __forceinline__ void stage_flat(uint8_t *__restrict__ lds, int trash, const uint8_t *start, int len) {
+__device__ __forceinline__ void stage_flat(uint8_t *__restrict__ lds, const uint8_t *start, int len) {
   const uint32_t lead = uint32_t(reinterpret_cast<uintptr_t>(start) & 15);
   const int n = int((lead + len + 15) >> 4);
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(start - lead, uint32_t(16 * n));
-  stage_flat_upto<NT, ITERS, POLICY>((n + NT - 1) / NT, lds, trash, rsrc, n);
+  stage_flat_upto<NT, ITERS, POLICY>((n + NT - 1) / NT, lds, rsrc, n);
 }
 
 // Window staging for rows that start 128-byte aligned: LDS row r gets bytes
@@ -515,7 +520,7 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
   const uintptr_t a = reinterpret_cast<uintptr_t>(row_base);
   bool aligned;
   if (FLAT) {
-    stage_flat<NT, load_iters_for(MODE), kFlatLoadPolicy>(lds, p.trash, row_base, nrows * ncols);
+    stage_flat<NT, load_iters_for(MODE), kFlatLoadPolicy>(lds, row_base, nrows * ncols);
     aligned = ((a & 3) == 0) && ((ncols & 3) == 0);
   } else {
     stage_rows<NT, load_iters_for(MODE), load_policy_for(MODE)>(lds, p.trash, row_base, p.ld, nrows, ncols,

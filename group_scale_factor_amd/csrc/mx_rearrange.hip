@@ -33,10 +33,9 @@
 //   * Load: the unit's source bytes are fetched as 16-byte aligned pieces
 //     (buffer_load_dwordx4) covering each row segment (or, for packed narrow
 //     rows, the whole strip as one range, loaded straight into LDS) and staged
-//     in LDS. A 16-byte aligned
-//     piece that contains at least one byte of the matrix lies inside the same
-//     memory page as that byte, so the cover never touches a page the matrix
-//     does not; the extra bytes are never emitted.
+//     in LDS. A 16-byte aligned piece that contains at least one byte of the
+//     matrix lies inside the same memory page as that byte, so the cover never
+//     touches a page the matrix does not; the extra bytes are never emitted.
 //   * Interleave: after one barrier each lane assembles one 16-byte output
 //     unit — the same 4-byte column word of rows i, i+32, i+64, i+96 of the
 //     tile — from LDS. When the source is not 4-byte aligned each word is

@@ -87,6 +87,8 @@ def test_thousands_of_groups(env):
 def test_very_wide_k_rows(env):
     rng = np.random.default_rng(103)
     rearrange_case(env, "K", strided(rng, 129, 65537, 65541), [1, 30001, 30001, 65537], "K 65537 columns")
+    # rows on 128-byte lines (the streaming window path): 257 windows per row block
+    rearrange_case(env, "K", strided(rng, 129, 65539, 65664), [1, 30001, 30002, 65539], "K 65539 columns, lines")
 
 
 def test_inverse_and_pad_largest_strides(env):

@@ -12,6 +12,7 @@ fails loudly when the library has not been built.
     out = mx_block_rearrange_3d(expert_scales)
     q, blocked_scales = mx_quantize_dim0_M_groups(x_bf16, group_end_offsets)
     qT, blocked_scales = mx_quantize_dim1_K_groups(x_bf16, token_group_end_offsets)
+    q, blocked_scales = mx_quantize_dim1_3d(w_bf16)          # (E, K, N) expert weights, cast along K
     padded = mx_pad_M_groups(data, group_end_offsets)
     scales = mx_block_unrearrange_M_groups(blocked, rows, cols, group_end_offsets)   # and _K_groups
     data = mx_unpad_M_groups(padded, rows, group_end_offsets)

@@ -158,6 +158,44 @@ def test_fuzz_K_line_aligned_rows(env):
         run_case(env, "K", A, offs, misalign=0, label="fuzzK-lines-%d" % i)
 
 
+def test_wide_random_sweep(env):
+    """Thousands of random M and K cases (MX_SWEEP_CASES, default 2000): rows up to 3000, widths up to 2049,
+    half of them on rows that start on 128-byte lines and half at any stride and base alignment, up to 300
+    groups with empty groups and short totals; every byte and the guard bytes checked."""
+    import workloads
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(2026)
+    cases = int(os.environ.get("MX_SWEEP_CASES", "2000"))
+    print("case sweep of", cases, "random cases, seed 2026", flush=True)
+    for i in range(cases):
+        kind = "K" if i % 3 else "M"
+        rows = int(rng.choice([1, 2, 63, 127, 128, 129, 255, 256, 300, 700, 1300, 3000]))
+        if rng.random() < 0.7:
+            cols = int(rng.integers(1, 1200))
+        else:
+            cols = int(rng.choice([255, 256, 257, 259, 511, 512, 513, 1024, 2049]))
+        if rng.random() < 0.5:
+            ld, misalign = (cols + 127) // 128 * 128 + 128 * int(rng.integers(0, 3)), 0
+        else:
+            ld, misalign = cols + int(rng.integers(0, 40)), int(rng.integers(0, 16))
+        G = int(rng.choice([1, 2, 3, 5, 8, 16, 33, 64, 65, 100, 300]))
+        offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G,
+                                        p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        A = workloads.random_scales(rng, rows, cols, ld)
+        want = oracle.rearrange(kind, A, offs)
+        n = want.size
+        dev = _device_scales(torch, A, misalign)
+        buf = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+        fn = gsf.mx_block_rearrange_M_groups if kind == "M" else gsf.mx_block_rearrange_K_groups
+        fn(dev, torch.from_numpy(offs).cuda(), out=buf[:n])
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        assert (got[n:] == POISON).all() and np.array_equal(got[:n], want), \
+            "sweep case %d: %s rows %d cols %d ld %d misalign %d G %d" % (i, kind, rows, cols, ld, misalign, G)
+
+
 @pytest.mark.parametrize("line_aligned", [True, False])
 def test_k_window_edges(env, line_aligned):
     """K groups at the edges of the column windows, on rows that start on 128-byte lines and on rows that do

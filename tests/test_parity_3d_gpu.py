@@ -104,6 +104,20 @@ def test_fuzz_strides_and_alignment(env):
         run_3d(env, A, misalign=int(rng.integers(0, 16)), label="fuzz%d" % it)
 
 
+def test_random_sweep(env):
+    """Random per-expert cases (a fifth of MX_SWEEP_CASES, default 400): up to 9 experts, rows up to 1300,
+    widths up to 700, padded row and expert strides, base alignments 0..15."""
+    rng = np.random.default_rng(2028)
+    for it in range(int(os.environ.get("MX_SWEEP_CASES", "2000")) // 5):
+        E = int(rng.integers(1, 10))
+        rows = int(rng.choice([1, 2, 127, 128, 129, 300, 1300]))
+        cols = int(rng.integers(1, 700))
+        ld = cols + int(rng.choice([0, 0, 1, 3, 13, 64]))
+        es = rows * ld + int(rng.choice([0, 0, 5, 64, 1000]))
+        A = host_experts(rng, E, rows, cols, ld, es)
+        run_3d(env, A, misalign=int(rng.integers(0, 16)), label="sweep%d" % it)
+
+
 def test_wide_rows_and_many_experts(env):
     rng = np.random.default_rng(33)
     # the last two run more than 2048 units (the 512-thread instantiation), with ragged rows in the last

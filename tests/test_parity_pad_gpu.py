@@ -111,6 +111,25 @@ def test_fuzz_aligned_and_unaligned(env):
         run_pad(env, data, offs, ld=ld, misalign=misalign, label="fuzz%d" % i)
 
 
+def test_random_sweep(env):
+    """Random pad/unpad cases (a fifth of MX_SWEEP_CASES, default 400): rows up to 3000, widths up to
+    5120, 16-byte aligned and unaligned strides and bases, up to 300 groups, empty groups, short totals."""
+    import workloads
+
+    rng = np.random.default_rng(2029)
+    for i in range(int(os.environ.get("MX_SWEEP_CASES", "2000")) // 5):
+        rows = int(rng.choice([0, 1, 2, 127, 128, 129, 300, 700, 3000]))
+        cols = int(rng.integers(1, 5121)) if rng.random() < 0.5 else int(rng.choice([16, 48, 1024, 5120]))
+        aligned = rng.random() < 0.5
+        ld = (cols + 15) // 16 * 16 + 16 * int(rng.integers(0, 3)) if aligned else cols + int(rng.integers(0, 5))
+        misalign = 0 if aligned else int(rng.integers(0, 16))
+        G = int(rng.choice([1, 2, 3, 8, 16, 64, 65, 300]))
+        offs = workloads.random_offsets(rng, rows, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.3))
+        data = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        run_pad(env, data, offs, ld=ld, misalign=misalign, label="sweep%d" % i)
+
+
 def test_invalid_offsets_are_clamped(env):
     gsf, oracle, torch = env
     rng = np.random.default_rng(81)

@@ -172,6 +172,37 @@ def test_fuzz(env):
         run_quant(env, x, offs, ld=ld, label="fuzz%d" % i)
 
 
+def test_random_sweep(env):
+    """Random dim0 and dim1 casts (a tenth of MX_SWEEP_CASES each, default 200): rows/tokens up to 700,
+    K/N up to 1600 and 1300, padded strides, up to 200 groups, empty groups, short totals (dim1: ends at any
+    token, not only multiples of 32), sprinkled non-finite values."""
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(2030)
+    n = int(os.environ.get("MX_SWEEP_CASES", "2000")) // 10
+    for i in range(n):
+        rows = int(rng.choice([1, 2, 31, 127, 128, 129, 300, 700]))
+        K = 32 * int(rng.integers(1, 51))
+        G = int(rng.choice([1, 2, 3, 8, 16, 64, 65, 200]))
+        offs = workloads.random_offsets(rng, rows, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        x = pins.random_bf16_rows(rng, rows, K)
+        if rng.random() < 0.3:
+            x[rng.integers(0, rows), rng.integers(0, K)] = rng.choice([0x7F80, 0xFF80, 0x7FC0])
+        run_quant(env, x, offs, ld=K + 8 * int(rng.choice([0, 0, 1, 9])), label="sweep dim0 %d" % i)
+    for i in range(n):
+        T = 32 * int(rng.choice([1, 2, 3, 4, 5, 8, 13, 21]))
+        N = int(rng.integers(1, 1300))
+        G = int(rng.choice([1, 2, 3, 8, 16, 64, 65, 200]))
+        offs = workloads.random_offsets(rng, T, G, p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        x = pins.random_bf16_rows(rng, T, N)
+        if rng.random() < 0.3:
+            x[rng.integers(0, T), rng.integers(0, N)] = rng.choice([0x7F80, 0xFF80, 0x7FC0])
+        run_dim1(env, x, offs, ld=_ld8(N, int(rng.choice([0, 0, 1, 5]))), label="sweep dim1 %d" % i)
+
+
 def test_many_groups(env):
     import pins
     import workloads

@@ -156,6 +156,27 @@ def test_fuzz_K(env):
     _fuzz(env, "K", 63, 100)
 
 
+def test_random_sweep(env):
+    """Random inverse cases (half of MX_SWEEP_CASES, default 1000): both groupings, rows up to 3000, widths
+    up to 1300, output strides and base alignments of every kind, up to 300 groups, empty groups and short
+    totals; every output byte and the poisoned bytes around the output rows checked."""
+    import workloads
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(2027)
+    for i in range(int(os.environ.get("MX_SWEEP_CASES", "2000")) // 2):
+        kind = "K" if i % 2 else "M"
+        rows = int(rng.choice([1, 2, 63, 127, 128, 129, 300, 700, 3000]))
+        cols = int(rng.integers(1, 1300))
+        ld = cols + int(rng.choice([0, 0, 1, 3, 16, 128 - cols % 128]))
+        G = int(rng.choice([1, 2, 3, 8, 16, 64, 65, 300]))
+        offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G,
+                                        p_empty=float(rng.choice([0.0, 0.3, 0.7])),
+                                        short_total=bool(rng.random() < 0.2))
+        run_inverse(env, kind, random_blocked(rng, oracle, kind, rows, cols, G), rows, cols, offs, ld=ld,
+                    misalign=int(rng.integers(0, 16)) if rng.random() < 0.5 else 0, label="sweep%d" % i)
+
+
 def test_brute_force_tiny(env):
     import itertools
 

@@ -143,3 +143,31 @@ def test_cast_group_limits(env):
     with pytest.raises(gsf.RearrangeError) as e:
         gsf.mx_quantize_dim1_K_groups(xd, too_many)
     assert e.value.status == -3
+
+
+def test_grid_stride_loop(env):
+    """More than 2^20 work units: the grid is capped and each workgroup loops over several units (with a
+    barrier between them). One-column matrices keep the bytes modest: M groups (flat strips), K groups (the
+    window path) and per-expert matrices, each checked byte for byte."""
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(106)
+    # M: ceil(rows/128) + G row blocks = 1048582 units
+    rows = 128 * (1 << 20) + 300
+    scales = rng.integers(1, 256, size=(rows, 1), dtype=np.uint8)
+    rearrange_case(env, "M", (scales.reshape(-1), scales), [1000, 70000000, rows], "M grid-stride")
+    del scales
+    # K: 524289 row blocks x (1 window + 1 tail unit) = 1048578 units
+    rows = (1 << 26) + 7
+    scales = rng.integers(1, 256, size=(rows, 2), dtype=np.uint8)
+    rearrange_case(env, "K", (scales.reshape(-1), scales), [1, 2], "K grid-stride")
+    del scales
+    # per-expert: one expert of 1048577 row blocks
+    rows = 128 * (1 << 20) + 3
+    A = rng.integers(1, 256, size=(1, rows, 1), dtype=np.uint8)
+    print("case limits 3-D grid-stride rows", rows, flush=True)
+    want = oracle.rearrange_3d(A)
+    buf = torch.full((want.size + GUARD,), POISON, dtype=torch.uint8, device="cuda")
+    gsf.mx_block_rearrange_3d(torch.from_numpy(A).cuda(), out=buf[:want.size])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert (got[want.size:] == POISON).all() and np.array_equal(got[:want.size], want), "3-D grid-stride"

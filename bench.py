@@ -229,6 +229,31 @@ def capture(job, first, count):
     return g
 
 
+def launch_floor_us(count=500):
+    """Graph-replay cost of an empty launch on this GPU (torch's spin kernel told to spin 0 cycles),
+    timed like the workload's launches; None when torch offers no such kernel."""
+    import torch
+
+    if not hasattr(torch.cuda, "_sleep"):
+        return None
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(count):
+                torch.cuda._sleep(0)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
 def capture_same(job, count):
     """A HIP graph of `count` launches that all use input/output copy 0 (cache-resident when it fits)."""
     torch = job.torch
@@ -572,6 +597,9 @@ def main():
         warm = {"us_per_launch": round(warm_us, 3), "GBps": round(job.bytes_per_step / warm_us / 1e3, 2),
                 "launches": n_warm, "note": "one input/output copy reused: cache-resident when it fits, "
                                             "not an HBM figure"}
+    # the fixed cost of one graph-replayed launch, and the fraction of peak one launch of these bytes could
+    # reach even if it moved them at the full peak rate (outside the timed region; skipped when profiling)
+    floor = launch_floor_us() if not args.eager and not args.no_warm and K > 0 else None
     us_per_launch = gpu_s / K * 1e6
     value = job.bytes_per_step * K / wall / 1e9
     achieved = job.bytes_per_step / (gpu_s / K) / 1e9
@@ -621,6 +649,10 @@ def main():
             "traffic": hbm_traffic(args.workload, w.kind),
             "kernel": KERNEL_NAMES.get(args.workload),
             "avg_launch_us": round(us_per_launch, 3),
+            "launch_floor_us": round(floor, 3) if floor is not None else None,
+            "frac_ceiling": (round((job.bytes_per_step / HBM_PEAK_GBPS / 1e3) /
+                                   (floor + job.bytes_per_step / HBM_PEAK_GBPS / 1e3), 4)
+                             if floor is not None else None),
         },
         "warm": warm,
         "cpu_baseline": None,

@@ -523,7 +523,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the rearrangement has no multi-GPU path in this build "
+        print("bench.py measures one GPU: the rearrangement has no multi-GPU path "
               "(each GPU converts its own groups independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -13,18 +13,21 @@
 // where no group holds data (rows past the last end for M, columns past the
 // last end for K).
 //
-// A unit is 128 rows of one group within one 128-column window of the output
-// row (one 128-byte line of each row when the rows are so aligned), so units
-// never share output lines except where groups meet; its tiles are contiguous
-// in the blocked input (for K groups the first may start 1-3 columns early). Lanes
-// load 16-byte tile rows (the column word of rows i, i+32, i+64, i+96), scatter
-// the four words into a row-major LDS strip (odd dword pitch), and after one
-// barrier write the row segments out: 16-byte stores of words realigned with
-// v_alignbyte for every aligned 16-byte chunk inside a segment, at most three
-// dwords and three bytes at either end. When the unit's output rows are
-// contiguous (row stride == width, whole words) the strip is packed and the
-// unit's rows are stored as one segment. Spare units of the same launch write
-// the zeros.
+// M groups: a unit is 128 rows of one group within one 128-column window of
+// the output row (one 128-byte line of each row when the rows are so aligned);
+// its tiles are contiguous in the blocked input. K groups: a unit is 128 rows
+// x one 128-column window of the output, holding the tiles of every group that
+// has columns in the window (read one group after another), so no two units
+// write the same output line. Lanes load 16-byte tile rows (the column word of
+// rows i, i+32, i+64, i+96) and place the four words in a row-major LDS strip
+// (odd dword pitch) — as words, or byte by byte where a K group's columns are
+// not word-aligned in the window — and after one barrier write the row
+// segments out: 16-byte stores of words realigned with v_alignbyte for every
+// aligned 16-byte chunk inside a segment, at most three dwords and three bytes
+// at either end. When the unit's output rows are contiguous (row stride ==
+// width, whole words) the strip is packed and the unit's rows are stored as one
+// segment. Rows (M) past the last group are zeroed by spare units of the same
+// launch; K windows zero their own columns past the last group.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,19 +58,16 @@ struct UParams {
   int per_row;           // M: units per output row block; K: units per 128-row block
 };
 
-// K groups: clamped cumulative ends e (scale columns), cumulative unit counts
-// cch (a group's units are the 128-column windows of the output row its
-// columns touch) and cumulative padded widths cw.
+// K groups: clamped cumulative ends e (scale columns) and cumulative padded
+// widths cw.
 __device__ __forceinline__ void scan_slice_k(const int32_t *__restrict__ offs, int groups, int cols, int base,
-                                             int carry_e, int carry_ch, int carry_w, int &e, int &cch, int &cw) {
+                                             int carry_e, int carry_w, int &e, int &cw) {
   const int g = base + int(threadIdx.x & (kWave - 1));
   e = g < groups ? offs[g] : 0;
   e = min(max(e, 0), cols);
   e = max(wave_inclusive_max(e), carry_e);
   const int prev = wave_shift_up(e, carry_e);
   const int W = g < groups ? (e - prev + 3) & ~3 : 0;
-  const int windows = g < groups && e > prev ? (e - 1) / kUCols - prev / kUCols + 1 : 0;
-  cch = wave_inclusive_sum(windows) + carry_ch;
   cw = wave_inclusive_sum(W) + carry_w;
 }
 
@@ -76,59 +76,54 @@ struct KGroups;
 
 template <>
 struct KGroups<true> {
-  int groups, e, cch, cw;
+  int groups, e, cw;
   __device__ __forceinline__ void init(const UParams &p, int *) {
     groups = p.groups;
-    scan_slice_k(p.offs, p.groups, p.cols, 0, 0, 0, 0, e, cch, cw);
+    scan_slice_k(p.offs, p.groups, p.cols, 0, 0, 0, e, cw);
   }
-  __device__ __forceinline__ int count_cch_le(int64_t key) const {
-    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(cch) <= key));
+  __device__ __forceinline__ int count_ends_le(int64_t key) const {
+    return __popcll(__ballot(int(threadIdx.x & (kWave - 1)) < groups && int64_t(e) <= key));
   }
   __device__ __forceinline__ int end(int g) const { return __builtin_amdgcn_readlane(e, g); }
-  __device__ __forceinline__ int chunks_through(int g) const { return __builtin_amdgcn_readlane(cch, g); }
   __device__ __forceinline__ int width_through(int g) const { return __builtin_amdgcn_readlane(cw, g); }
 };
 
 template <>
 struct KGroups<false> {
   int groups;
-  const int *es, *cchs, *cws;
+  const int *es, *cws;
   __device__ __forceinline__ void init(const UParams &p, int *lds) {
     groups = p.groups;
-    int *e_out = lds, *ch_out = lds + p.groups, *w_out = lds + 2 * p.groups;
+    int *e_out = lds, *w_out = lds + p.groups;
     if (threadIdx.x < kWave) {
-      int ce = 0, cc = 0, cwd = 0;
+      int ce = 0, cwd = 0;
       for (int base = 0; base < p.groups; base += kWave) {
-        int e, cch, cw;
-        scan_slice_k(p.offs, p.groups, p.cols, base, ce, cc, cwd, e, cch, cw);
+        int e, cw;
+        scan_slice_k(p.offs, p.groups, p.cols, base, ce, cwd, e, cw);
         const int g = base + int(threadIdx.x);
         if (g < p.groups) {
           e_out[g] = e;
-          ch_out[g] = cch;
           w_out[g] = cw;
         }
         ce = __builtin_amdgcn_readlane(e, kWave - 1);
-        cc = __builtin_amdgcn_readlane(cch, kWave - 1);
         cwd = __builtin_amdgcn_readlane(cw, kWave - 1);
       }
     }
     __syncthreads();
     es = e_out;
-    cchs = ch_out;
     cws = w_out;
   }
-  __device__ __forceinline__ int count_cch_le(int64_t key) const {
+  __device__ __forceinline__ int count_ends_le(int64_t key) const {
     const int lane = threadIdx.x & (kWave - 1);
     int n = 0;
     for (int base = 0; base < groups; base += kWave) {
-      const int c = __popcll(__ballot(base + lane < groups && int64_t(cchs[base + lane]) <= key));
+      const int c = __popcll(__ballot(base + lane < groups && int64_t(es[base + lane]) <= key));
       n += c;
       if (c < kWave) break;
     }
     return n;
   }
   __device__ __forceinline__ int end(int g) const { return es[g]; }
-  __device__ __forceinline__ int chunks_through(int g) const { return cchs[g]; }
   __device__ __forceinline__ int width_through(int g) const { return cws[g]; }
 };
 
@@ -179,6 +174,39 @@ __device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const ui
     }
   }
   __syncthreads();
+}
+
+// K windows: places ntiles loaded tiles of one group in the window's LDS strip
+// (row r at lds + r*kUPitch words). The first byte of tile tc's words belongs
+// at window column col0 + 4*tc; only bytes at window columns [lo, hi), the
+// group's part of the window, are written. Word-aligned tiles inside the range
+// are written as words, the others byte by byte. Groups place disjoint column
+// ranges, so no barrier is needed between them.
+__device__ __forceinline__ void scatter_window(uint32_t *lds, const uint4 (&v)[kULoads], int ntiles, int col0,
+                                               int lo, int hi) {
+  uint8_t *lb = reinterpret_cast<uint8_t *>(lds);
+#pragma unroll
+  for (int it = 0; it < kULoads; ++it) {
+    const int s = int(threadIdx.x) + it * kUThreads;
+    if (s < ntiles * 32) {
+      const int i = s & 31;
+      const int col = col0 + 4 * (s >> 5);
+      const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+      if ((col & 3) == 0 && col >= lo && col + 4 <= hi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lds[(i + 32 * q) * kUPitch + (col >> 2)] = w[q];
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = col + b;
+          if (c >= lo && c < hi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lb[(i + 32 * q) * kUPitch * 4 + c] = uint8_t(w[q] >> (8 * b));
+          }
+        }
+      }
+    }
+  }
 }
 
 // Writes rows [0, nrows) x bytes [skip, skip + ncols) of the LDS strip (row r
@@ -313,34 +341,38 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
     grp.init(p, group_lds);
     if (u >= p.units) return;
     const int64_t rb = u / p.per_row;                  // 128-row block
-    const int slot = int(u - rb * p.per_row);
-    const int total_chunks = grp.chunks_through(p.groups - 1);
+    const int c_lo = int(u - rb * p.per_row) * kUCols; // output window [c_lo, c_hi)
+    const int c_hi = min(c_lo + kUCols, p.cols);
     const int nrows = min(kTileRows, p.rows - int(rb) * kTileRows);
     const int64_t padded_rows = int64_t((p.rows + kTileRows - 1) / kTileRows) * kTileRows;
-    if (slot < total_chunks) {
-      const int g = grp.count_cch_le(slot);
-      const int first = g ? grp.chunks_through(g - 1) : 0;
-      const int k = slot - first;
+    // the groups cover [0, last end) without gaps: a window reaching past it starts from zeros
+    if (c_hi > grp.end(p.groups - 1)) {
+      for (int d = threadIdx.x; d < kTileRows * kUPitch; d += kUThreads) strip[d] = 0u;
+      __syncthreads();
+    }
+    // every group with columns in the window, from the first whose end lies past c_lo
+    for (int g = grp.count_ends_le(c_lo); g < p.groups; ++g) {
       const int start = g ? grp.end(g - 1) : 0;
+      if (start >= c_hi) break;
       const int end = grp.end(g);
+      if (end <= start) continue;
+      const int lo = max(c_lo, start), hi = min(c_hi, end);   // the group's columns in the window
+      const int t0 = (lo - start) >> 2;                        // its first tile there
+      const int ntiles = ((hi - 1 - start) >> 2) - t0 + 1;
       const int W = (end - start + 3) & ~3;
       const int C = g ? grp.width_through(g - 1) : 0;
-      // output columns [a, b): the group's part of the 128-column window start/128 + k
-      const int win = start / kUCols + k;
-      const int a = max(start, win * kUCols), b = min(end, (win + 1) * kUCols);
-      const int lc = a - start;                          // first local column
-      const int ncols = b - a;
-      if (nrows <= 0 || ncols <= 0) return;
-      const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(lc >> 2) * 512;
-      const int tile_cols = ((lc & 3) + ncols + 3) >> 2;
+      const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(t0) * 512;
       uint4 v[kULoads];
-      issue_loads(v, src, tile_cols, uint32_t(tile_cols) * 512u);
-      unit_out<false>(strip, v, lc & 3, tile_cols, nrows, ncols, p.out + rb * kTileRows * p.ld + a, p.ld);
-    } else {
-      // spare slots of this row block: zero its rows' columns after the last group
-      zero_region(p.out, p.ld, rb * kTileRows, rb * kTileRows + nrows, grp.end(p.groups - 1), p.cols,
-                  slot - total_chunks, p.per_row - total_chunks);
+      issue_loads(v, src, ntiles, uint32_t(ntiles) * 512u);
+      scatter_window(strip, v, ntiles, start + 4 * t0 - c_lo, lo - c_lo, hi - c_lo);
     }
+    __syncthreads();
+    // no other unit writes these lines: stream them when every row starts on a 128-byte line
+    uint8_t *dst = p.out + rb * kTileRows * p.ld + c_lo;
+    if (((reinterpret_cast<uintptr_t>(p.out) | uintptr_t(p.ld)) & 127) == 0)
+      store_rows<true>(strip, kUPitch, 0, nrows, c_hi - c_lo, dst, p.ld);
+    else
+      store_rows<false>(strip, kUPitch, 0, nrows, c_hi - c_lo, dst, p.ld);
   }
 }
 
@@ -370,13 +402,13 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
     p.per_row = (p.padded_cols + kUCols - 1) / kUCols;
     p.units = ((rows + kTileRows - 1) / kTileRows + groups) * p.per_row;
   } else {
-    // a group's windows number at most its width / 128 + 2 (floored sums), plus one spare slot
-    p.per_row = int(cols / kUCols + 2 * int64_t(groups) + 1);
+    // one unit per (128-row block, output window)
+    p.per_row = int((cols + kUCols - 1) / kUCols);
     p.units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
   if (p.units > lim) return MX_REARRANGE_ESHAPE;
   const bool small = groups <= kWave;
-  const size_t lds = size_t(kTileRows) * kUPitch * 4 + (small ? 0 : size_t(kgroups ? 3 : 2) * groups * sizeof(int));
+  const size_t lds = size_t(kTileRows) * kUPitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
   const void *fn = kgroups ? (small ? reinterpret_cast<const void *>(&unrearrange_kernel<true, true>)
                                     : reinterpret_cast<const void *>(&unrearrange_kernel<true, false>))
                            : (small ? reinterpret_cast<const void *>(&unrearrange_kernel<false, true>)

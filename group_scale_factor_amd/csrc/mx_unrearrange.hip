@@ -16,7 +16,8 @@
 // M groups: a unit is 128 rows of one group within one 128-column window of
 // the output row (one 128-byte line of each row when the rows are so aligned);
 // its tiles are contiguous in the blocked input. K groups: a unit is 128 rows
-// x one 128-column window of the output, holding the tiles of every group that
+// x one 256-column window of the output (128 columns above 64 groups, whose
+// table takes LDS), holding the tiles of every group that
 // has columns in the window (read one group after another), so no two units
 // write the same output line. Lanes load 16-byte tile rows (the column word of
 // rows i, i+32, i+64, i+96) and place the four words in a row-major LDS strip
@@ -24,7 +25,7 @@
 // not word-aligned in the window — and after one barrier write the row
 // segments out: 16-byte stores of words realigned with v_alignbyte for every
 // aligned 16-byte chunk inside a segment, at most three dwords and three bytes
-// at either end. When the unit's output rows are contiguous (row stride ==
+// at either end. When an M unit's output rows are contiguous (row stride ==
 // width, whole words) the strip is packed and the unit's rows are stored as one
 // segment. Rows (M) past the last group are zeroed by spare units of the same
 // launch; K windows zero their own columns past the last group.
@@ -37,13 +38,25 @@
 
 namespace {
 
-constexpr int kUThreads = 256;
-constexpr int kUCols = 128;                        // output columns per unit: one 128-byte line of a row
-constexpr int kUMaxTiles = kUCols / 4 + 1;         // a K unit may start up to 3 columns into a tile
-constexpr int kUPitch = kUMaxTiles + 2;            // LDS dwords per strip row (odd)
-constexpr int kULoads = (kUMaxTiles * 32 + kUThreads - 1) / kUThreads;
+// Unit geometry. M units, and K windows when the group table lives in LDS
+// (more than 64 groups): 128 output columns (one 128-byte line of each row)
+// and 256 threads. K windows with at most 64 groups: 256 output columns (two
+// lines of each row) and 512 threads, measured faster on the large K shapes;
+// 256-column M units were slower on the skinny M shape.
+template <bool WIDE>
+struct UGeom {
+  static constexpr int threads = WIDE ? 512 : 256;
+  static constexpr int cols = WIDE ? 256 : 128;
+  static constexpr int max_tiles = cols / 4 + 1;   // a K window may start up to 3 columns into a tile
+  static constexpr int pitch = max_tiles + 2;      // LDS dwords per strip row (odd)
+  static constexpr int loads = (max_tiles * 32 + threads - 1) / threads;
+};
+using GM = UGeom<false>;
 constexpr int kUMaxGroups = 4096;
 constexpr int64_t kUMaxRowStride = int64_t(1) << 30;
+static_assert(kTileRows * UGeom<true>::pitch * 4 <= 64 * 1024 &&
+                  kTileRows * UGeom<false>::pitch * 4 + 2 * kUMaxGroups * 4 <= 64 * 1024,
+              "LDS per workgroup: the strip, and the group table of more than 64 groups");
 
 struct UParams {
   const uint8_t *blocked;
@@ -147,11 +160,12 @@ struct RowSplit {
 
 // Issues the loads of tile_cols contiguous tiles at src (16-byte aligned); at
 // most `bytes` of them are read, pieces past that load as zeros.
-__device__ __forceinline__ void issue_loads(uint4 (&v)[kULoads], const uint8_t *src, int tile_cols, uint32_t bytes) {
+template <class G>
+__device__ __forceinline__ void issue_loads(uint4 (&v)[G::loads], const uint8_t *src, int tile_cols, uint32_t bytes) {
   const __amdgpu_buffer_rsrc_t rsrc = byte_buffer(src, bytes);
 #pragma unroll
-  for (int it = 0; it < kULoads; ++it) {
-    const int s = int(threadIdx.x) + it * kUThreads;
+  for (int it = 0; it < G::loads; ++it) {
+    const int s = int(threadIdx.x) + it * G::threads;
     const uint32_t off = s < tile_cols * 32 ? uint32_t(16 * s) : kOutOfRange;
     const auto t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(off), 0, 2);
     v[it] = make_uint4(t[0], t[1], t[2], t[3]);
@@ -160,11 +174,11 @@ __device__ __forceinline__ void issue_loads(uint4 (&v)[kULoads], const uint8_t *
 
 // Scatters the loaded tiles into the LDS strip, row r's column word c at
 // lds[r*pitch + c]. Called by the whole workgroup; ends with a barrier.
-__device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const uint4 (&v)[kULoads], int tile_cols) {
+__device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const uint4 (&v)[GM::loads], int tile_cols) {
   // piece s = 32*tile + i holds the words of rows i, i+32, i+64, i+96 in column word `tile`
 #pragma unroll
-  for (int it = 0; it < kULoads; ++it) {
-    const int s = int(threadIdx.x) + it * kUThreads;
+  for (int it = 0; it < GM::loads; ++it) {
+    const int s = int(threadIdx.x) + it * GM::threads;
     if (s < tile_cols * 32) {
       const int tc = s >> 5, i = s & 31;
       lds[(i + 0) * pitch + tc] = v[it].x;
@@ -177,31 +191,32 @@ __device__ __forceinline__ void scatter_strip(uint32_t *lds, int pitch, const ui
 }
 
 // K windows: places ntiles loaded tiles of one group in the window's LDS strip
-// (row r at lds + r*kUPitch words). The first byte of tile tc's words belongs
+// (row r at lds + r*G::pitch words). The first byte of tile tc's words belongs
 // at window column col0 + 4*tc; only bytes at window columns [lo, hi), the
 // group's part of the window, are written. Word-aligned tiles inside the range
 // are written as words, the others byte by byte. Groups place disjoint column
 // ranges, so no barrier is needed between them.
-__device__ __forceinline__ void scatter_window(uint32_t *lds, const uint4 (&v)[kULoads], int ntiles, int col0,
+template <class G>
+__device__ __forceinline__ void scatter_window(uint32_t *lds, const uint4 (&v)[G::loads], int ntiles, int col0,
                                                int lo, int hi) {
   uint8_t *lb = reinterpret_cast<uint8_t *>(lds);
 #pragma unroll
-  for (int it = 0; it < kULoads; ++it) {
-    const int s = int(threadIdx.x) + it * kUThreads;
+  for (int it = 0; it < G::loads; ++it) {
+    const int s = int(threadIdx.x) + it * G::threads;
     if (s < ntiles * 32) {
       const int i = s & 31;
       const int col = col0 + 4 * (s >> 5);
       const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
       if ((col & 3) == 0 && col >= lo && col + 4 <= hi) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lds[(i + 32 * q) * kUPitch + (col >> 2)] = w[q];
+        for (int q = 0; q < 4; ++q) lds[(i + 32 * q) * G::pitch + (col >> 2)] = w[q];
       } else {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int c = col + b;
           if (c >= lo && c < hi) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) lb[(i + 32 * q) * kUPitch * 4 + c] = uint8_t(w[q] >> (8 * b));
+            for (int q = 0; q < 4; ++q) lb[(i + 32 * q) * G::pitch * 4 + c] = uint8_t(w[q] >> (8 * b));
           }
         }
       }
@@ -213,7 +228,7 @@ __device__ __forceinline__ void scatter_window(uint32_t *lds, const uint4 (&v)[k
 // from lds + r*pitch words) to dst, row r at dst + r*ld (ld unused when nrows
 // is 1). Called by the whole workgroup. NT: the 16-byte chunk stores are
 // non-temporal (measured faster for M units, slower for K units).
-template <bool NT>
+template <bool NT, int THREADS>
 __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int skip, int nrows, int ncols,
                                            uint8_t *dst, int64_t ld) {
   // Store. Split each row segment by its alignment: up to 3 single bytes, up
@@ -225,7 +240,7 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const uintptr_t dst_bits = reinterpret_cast<uintptr_t>(dst) | uintptr_t(nrows > 1 ? ld : 0);
   const int max_chunks = ncols >> 4;
-  for (int s = threadIdx.x; s < nrows * max_chunks; s += kUThreads) {
+  for (int s = threadIdx.x; s < nrows * max_chunks; s += THREADS) {
     const int r = s / max_chunks, q = s - r * max_chunks;
     uint8_t *row_ptr = dst + int64_t(r) * ld;
     const RowSplit sp(row_ptr, ncols);
@@ -247,7 +262,7 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
       *reinterpret_cast<u32x4 *>(row_ptr + lo) = v;
   }
   if ((dst_bits & 15) != 0 || (ncols & 15) != 0) {
-    for (int s = threadIdx.x; s < nrows * 6; s += kUThreads) {
+    for (int s = threadIdx.x; s < nrows * 6; s += THREADS) {
       const int r = s / 6, k = s - r * 6;
       uint8_t *row_ptr = dst + int64_t(r) * ld;
       const RowSplit sp(row_ptr, ncols);
@@ -260,7 +275,7 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
     }
   }
   if ((dst_bits & 3) != 0 || (ncols & 3) != 0) {
-    for (int s = threadIdx.x; s < nrows * 6; s += kUThreads) {
+    for (int s = threadIdx.x; s < nrows * 6; s += THREADS) {
       const int r = s / 6, k = s - r * 6;
       uint8_t *row_ptr = dst + int64_t(r) * ld;
       const RowSplit sp(row_ptr, ncols);
@@ -276,14 +291,14 @@ __device__ __forceinline__ void store_rows(const uint32_t *lds, int pitch, int s
 // ncols) and whole words, the strip is packed with pitch ncols/4 and the unit's
 // output is stored as one segment of nrows*ncols bytes.
 template <bool NT>
-__device__ __forceinline__ void unit_out(uint32_t *lds, const uint4 (&v)[kULoads], int skip, int tile_cols, int nrows,
+__device__ __forceinline__ void unit_out(uint32_t *lds, const uint4 (&v)[GM::loads], int skip, int tile_cols, int nrows,
                                          int ncols, uint8_t *dst, int64_t ld) {
   if (skip == 0 && ld == ncols && (ncols & 3) == 0) {
     scatter_strip(lds, ncols >> 2, v, tile_cols);
-    store_rows<NT>(lds, 0, 0, 1, nrows * ncols, dst, 0);
+    store_rows<NT, GM::threads>(lds, 0, 0, 1, nrows * ncols, dst, 0);
   } else {
-    scatter_strip(lds, kUPitch, v, tile_cols);
-    store_rows<NT>(lds, kUPitch, skip, nrows, ncols, dst, ld);
+    scatter_strip(lds, GM::pitch, v, tile_cols);
+    store_rows<NT, GM::threads>(lds, GM::pitch, skip, nrows, ncols, dst, ld);
   }
 }
 
@@ -295,17 +310,18 @@ __device__ __forceinline__ void zero_region(uint8_t *out, int64_t ld, int64_t r0
   if (total <= 0 || parts <= 0) return;
   const int64_t per = (total + parts - 1) / parts;
   const int64_t b = min(per * part, total), e = min(per * (part + 1), total);
-  for (int64_t s = b + threadIdx.x; s < e; s += kUThreads) {
+  for (int64_t s = b + threadIdx.x; s < e; s += GM::threads) {
     const int64_t r = s / w;
     out[(r0 + r) * ld + c0 + (s - r * w)] = 0;
   }
 }
 
 template <bool KGROUPS, bool SMALL>
-__global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
+__global__ __launch_bounds__(UGeom<KGROUPS && SMALL>::threads) void unrearrange_kernel(UParams p) {
+  using GK = UGeom<KGROUPS && SMALL>;   // K window geometry
   extern __shared__ __align__(16) int ulds[];
   uint32_t *strip = reinterpret_cast<uint32_t *>(ulds);
-  int *group_lds = ulds + kTileRows * kUPitch;
+  int *group_lds = ulds + kTileRows * GK::pitch;
   const int64_t n8 = int64_t(gridDim.x) / 8 * 8;
   const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
                                              : int64_t(blockIdx.x);
@@ -315,8 +331,8 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
     if (u >= p.units) return;
     const int64_t ob = u / p.per_row;                  // output row block of the blocked layout
     const int cc = int(u - ob * p.per_row);
-    const int c0 = cc * kUCols;
-    const int ncols = min(kUCols, p.cols - c0);
+    const int c0 = cc * GM::cols;
+    const int ncols = min(GM::cols, p.cols - c0);
     const int tile_cols = (ncols + 3) >> 2;
     const int g = grp.count_pends_le(ob * kTileRows);
     if (g < p.groups) {
@@ -326,8 +342,8 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       const int row0 = start + int(k) * kTileRows;
       const int nrows = int(min(int64_t(kTileRows), int64_t(grp.end(g) - start) - k * kTileRows));
       if (nrows <= 0 || ncols <= 0) return;
-      uint4 v[kULoads];
-      issue_loads(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
+      uint4 v[GM::loads];
+      issue_loads<GM>(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
                   uint32_t(tile_cols) * 512u);
       unit_out<true>(strip, v, 0, tile_cols, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
     } else {
@@ -341,13 +357,13 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
     grp.init(p, group_lds);
     if (u >= p.units) return;
     const int64_t rb = u / p.per_row;                  // 128-row block
-    const int c_lo = int(u - rb * p.per_row) * kUCols; // output window [c_lo, c_hi)
-    const int c_hi = min(c_lo + kUCols, p.cols);
+    const int c_lo = int(u - rb * p.per_row) * GK::cols; // output window [c_lo, c_hi)
+    const int c_hi = min(c_lo + GK::cols, p.cols);
     const int nrows = min(kTileRows, p.rows - int(rb) * kTileRows);
     const int64_t padded_rows = int64_t((p.rows + kTileRows - 1) / kTileRows) * kTileRows;
     // the groups cover [0, last end) without gaps: a window reaching past it starts from zeros
     if (c_hi > grp.end(p.groups - 1)) {
-      for (int d = threadIdx.x; d < kTileRows * kUPitch; d += kUThreads) strip[d] = 0u;
+      for (int d = threadIdx.x; d < kTileRows * GK::pitch; d += GK::threads) strip[d] = 0u;
       __syncthreads();
     }
     // every group with columns in the window, from the first whose end lies past c_lo
@@ -362,17 +378,17 @@ __global__ __launch_bounds__(kUThreads) void unrearrange_kernel(UParams p) {
       const int W = (end - start + 3) & ~3;
       const int C = g ? grp.width_through(g - 1) : 0;
       const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(t0) * 512;
-      uint4 v[kULoads];
-      issue_loads(v, src, ntiles, uint32_t(ntiles) * 512u);
-      scatter_window(strip, v, ntiles, start + 4 * t0 - c_lo, lo - c_lo, hi - c_lo);
+      uint4 v[GK::loads];
+      issue_loads<GK>(v, src, ntiles, uint32_t(ntiles) * 512u);
+      scatter_window<GK>(strip, v, ntiles, start + 4 * t0 - c_lo, lo - c_lo, hi - c_lo);
     }
     __syncthreads();
     // no other unit writes these lines: stream them when every row starts on a 128-byte line
     uint8_t *dst = p.out + rb * kTileRows * p.ld + c_lo;
     if (((reinterpret_cast<uintptr_t>(p.out) | uintptr_t(p.ld)) & 127) == 0)
-      store_rows<true>(strip, kUPitch, 0, nrows, c_hi - c_lo, dst, p.ld);
+      store_rows<true, GK::threads>(strip, GK::pitch, 0, nrows, c_hi - c_lo, dst, p.ld);
     else
-      store_rows<false>(strip, kUPitch, 0, nrows, c_hi - c_lo, dst, p.ld);
+      store_rows<false, GK::threads>(strip, GK::pitch, 0, nrows, c_hi - c_lo, dst, p.ld);
   }
 }
 
@@ -398,23 +414,27 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
   p.cols = int(cols);
   p.groups = groups;
   p.padded_cols = int(round_up(cols, 4));
+  const bool small = groups <= kWave;   // group table in registers, else in LDS
+  const bool wide = kgroups && small;   // 256-column K windows
+  const int unit_cols = wide ? UGeom<true>::cols : GM::cols;
   if (!kgroups) {
-    p.per_row = (p.padded_cols + kUCols - 1) / kUCols;
+    p.per_row = (p.padded_cols + unit_cols - 1) / unit_cols;
     p.units = ((rows + kTileRows - 1) / kTileRows + groups) * p.per_row;
   } else {
     // one unit per (128-row block, output window)
-    p.per_row = int((cols + kUCols - 1) / kUCols);
+    p.per_row = int((cols + unit_cols - 1) / unit_cols);
     p.units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
   if (p.units > lim) return MX_REARRANGE_ESHAPE;
-  const bool small = groups <= kWave;
-  const size_t lds = size_t(kTileRows) * kUPitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
+  const int pitch = wide ? UGeom<true>::pitch : GM::pitch;
+  const int threads = wide ? UGeom<true>::threads : GM::threads;
+  const size_t lds = size_t(kTileRows) * pitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
   const void *fn = kgroups ? (small ? reinterpret_cast<const void *>(&unrearrange_kernel<true, true>)
                                     : reinterpret_cast<const void *>(&unrearrange_kernel<true, false>))
                            : (small ? reinterpret_cast<const void *>(&unrearrange_kernel<false, true>)
                                     : reinterpret_cast<const void *>(&unrearrange_kernel<false, false>));
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(kUThreads), args, lds, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(threads), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

@@ -91,6 +91,24 @@ def test_very_wide_k_rows(env):
     rearrange_case(env, "K", strided(rng, 129, 65539, 65664), [1, 30001, 30002, 65539], "K 65539 columns, lines")
 
 
+def test_inverse_most_groups(env):
+    """The inverse calls at their group limit (4096): the scanned table of more than 64 groups sits in LDS
+    beside the strip, and most groups are empty."""
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(105)
+    for kind, rows, cols in (("M", 3000, 13), ("K", 130, 6000)):
+        n = rows if kind == "M" else cols
+        ends = np.sort(rng.integers(0, n + 1, size=4096)).astype(np.int32)
+        ends[-1] = n
+        blocked = rng.integers(0, 256, size=oracle.out_bytes(kind, rows, cols, 4096), dtype=np.uint8)
+        want = oracle.unrearrange(kind, blocked, rows, cols, ends)
+        print("case limits inverse", kind, "4096 groups", flush=True)
+        fn = gsf.mx_block_unrearrange_M_groups if kind == "M" else gsf.mx_block_unrearrange_K_groups
+        got = fn(torch.from_numpy(blocked).cuda(), rows, cols, torch.from_numpy(ends).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), want), kind
+
+
 def test_inverse_and_pad_largest_strides(env):
     gsf, oracle, torch = env
     rng = np.random.default_rng(104)

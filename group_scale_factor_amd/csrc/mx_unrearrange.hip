@@ -33,29 +33,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "group_table.h"
 #include "mx_rearrange.h"
 
 namespace {
 
-// Unit geometry. M units, and K windows when the group table lives in LDS
-// (more than 64 groups): 128 output columns (one 128-byte line of each row)
-// and 256 threads. K windows with at most 64 groups: 256 output columns (two
-// lines of each row) and 512 threads, measured faster on the large K shapes;
-// 256-column M units were slower on the skinny M shape.
-template <bool WIDE>
+// Unit geometry (threads, output columns). M units: 128 columns (one
+// 128-byte line of each row), 128 threads. K windows with at most 64 groups:
+// 256 columns (two lines of each row), 512 threads, measured faster on the
+// large K shapes (256-column M units were slower on the skinny M shape). K
+// windows of more than 64 groups, whose table takes LDS: 128 columns, 256
+// threads.
+template <int THREADS, int COLS>
 struct UGeom {
-  static constexpr int threads = WIDE ? 512 : 256;
-  static constexpr int cols = WIDE ? 256 : 128;
+  static constexpr int threads = THREADS;
+  static constexpr int cols = COLS;
   static constexpr int max_tiles = cols / 4 + 1;   // a K window may start up to 3 columns into a tile
   static constexpr int pitch = max_tiles + 2;      // LDS dwords per strip row (odd)
   static constexpr int loads = (max_tiles * 32 + threads - 1) / threads;
 };
-using GM = UGeom<false>;
+using GM = UGeom<128, 128>;
+using GKWide = UGeom<512, 256>;
+using GKNarrow = UGeom<256, 128>;
+template <bool KGROUPS, bool SMALL>
+using UnitGeom = typename std::conditional<KGROUPS, typename std::conditional<SMALL, GKWide, GKNarrow>::type, GM>::type;
 constexpr int kUMaxGroups = 4096;
 constexpr int64_t kUMaxRowStride = int64_t(1) << 30;
-static_assert(kTileRows * UGeom<true>::pitch * 4 <= 64 * 1024 &&
-                  kTileRows * UGeom<false>::pitch * 4 + 2 * kUMaxGroups * 4 <= 64 * 1024,
+static_assert(kTileRows * GKWide::pitch * 4 <= 64 * 1024 &&
+                  kTileRows * GKNarrow::pitch * 4 + 2 * kUMaxGroups * 4 <= 64 * 1024 &&
+                  kTileRows * GM::pitch * 4 + 2 * kUMaxGroups * 4 <= 64 * 1024,
               "LDS per workgroup: the strip, and the group table of more than 64 groups");
 
 struct UParams {
@@ -317,11 +325,11 @@ __device__ __forceinline__ void zero_region(uint8_t *out, int64_t ld, int64_t r0
 }
 
 template <bool KGROUPS, bool SMALL>
-__global__ __launch_bounds__(UGeom<KGROUPS && SMALL>::threads) void unrearrange_kernel(UParams p) {
-  using GK = UGeom<KGROUPS && SMALL>;   // K window geometry
+__global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearrange_kernel(UParams p) {
+  using GK = typename std::conditional<SMALL, GKWide, GKNarrow>::type;   // K window geometry
   extern __shared__ __align__(16) int ulds[];
   uint32_t *strip = reinterpret_cast<uint32_t *>(ulds);
-  int *group_lds = ulds + kTileRows * GK::pitch;
+  int *group_lds = ulds + kTileRows * UnitGeom<KGROUPS, SMALL>::pitch;
   const int64_t n8 = int64_t(gridDim.x) / 8 * 8;
   const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
                                              : int64_t(blockIdx.x);
@@ -416,7 +424,7 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
   p.padded_cols = int(round_up(cols, 4));
   const bool small = groups <= kWave;   // group table in registers, else in LDS
   const bool wide = kgroups && small;   // 256-column K windows
-  const int unit_cols = wide ? UGeom<true>::cols : GM::cols;
+  const int unit_cols = wide ? GKWide::cols : kgroups ? GKNarrow::cols : GM::cols;
   if (!kgroups) {
     p.per_row = (p.padded_cols + unit_cols - 1) / unit_cols;
     p.units = ((rows + kTileRows - 1) / kTileRows + groups) * p.per_row;
@@ -426,8 +434,8 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
     p.units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
   if (p.units > lim) return MX_REARRANGE_ESHAPE;
-  const int pitch = wide ? UGeom<true>::pitch : GM::pitch;
-  const int threads = wide ? UGeom<true>::threads : GM::threads;
+  const int pitch = wide ? GKWide::pitch : kgroups ? GKNarrow::pitch : GM::pitch;
+  const int threads = wide ? GKWide::threads : kgroups ? GKNarrow::threads : GM::threads;
   const size_t lds = size_t(kTileRows) * pitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
   const void *fn = kgroups ? (small ? reinterpret_cast<const void *>(&unrearrange_kernel<true, true>)
                                     : reinterpret_cast<const void *>(&unrearrange_kernel<true, false>))

@@ -26,8 +26,9 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 
 def compile_library(src, dst, verbose=False):
-    """Compile one oracle source file into a shared library (plain gcc -O2, one thread)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", dst + ".tmp", src, "-lm"]
+    """Compile one oracle source file into a shared library (plain gcc -O2)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-pthread", "-o", dst + ".tmp", src,
+           "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -53,6 +54,11 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        for name in ("oracle_M_groups_threads", "oracle_K_groups_threads"):
+            fn = getattr(lib, name, None)
+            if fn is not None:   # absent from the planted-mistake copies of older sources
+                fn.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, i32, ctypes.c_void_p, ctypes.c_int]
+                fn.restype = ctypes.c_int
         lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -96,13 +102,15 @@ class Oracle:
         fn = self.lib.oracle_M_groups_out_bytes if kind == "M" else self.lib.oracle_K_groups_out_bytes
         return int(fn(rows, cols, num_groups))
 
-    def rearrange(self, kind, scales, offs, out=None):
+    def rearrange(self, kind, scales, offs, out=None, threads=None):
         """Run the oracle on a host (rows, cols) uint8 array with unit column stride.
 
         ``scales`` may have any row stride >= cols (a strided numpy view); ``offs``
         holds the cumulative int32 group end offsets. Returns the flat uint8
         output of out_bytes(...) bytes. Raises ValueError when the oracle rejects
-        the input.
+        the input. ``threads`` (an int) shares the one call among that many host
+        threads (the same bytes; a CPU baseline spread over cores); None runs the
+        single-threaded definition.
         """
         if scales.dtype != np.uint8 or scales.ndim != 2:
             raise ValueError("scales must be a 2-D uint8 array")
@@ -117,10 +125,14 @@ class Oracle:
             out = np.empty(max(n, 0), dtype=np.uint8)
         elif out.dtype != np.uint8 or out.size < n or not out.flags.c_contiguous:
             raise ValueError("out must be a contiguous uint8 array of at least %d bytes" % n)
-        fn = self.lib.oracle_M_groups if kind == "M" else self.lib.oracle_K_groups
         sp = scales.__array_interface__["data"][0] if rows * cols > 0 else None
-        rc = fn(sp, rows, cols, ld, offs.ctypes.data if G > 0 else None, G,
-                out.ctypes.data if out.size > 0 else None)
+        args = [sp, rows, cols, ld, offs.ctypes.data if G > 0 else None, G, out.ctypes.data if out.size > 0 else None]
+        if threads is None:
+            fn = self.lib.oracle_M_groups if kind == "M" else self.lib.oracle_K_groups
+        else:
+            fn = self.lib.oracle_M_groups_threads if kind == "M" else self.lib.oracle_K_groups_threads
+            args.append(int(threads))
+        rc = fn(*args)
         if rc != 0:
             raise ValueError("oracle rejected the input (status %d)" % rc)
         return out[:n]
@@ -334,8 +346,8 @@ def out_bytes(kind, rows, cols, num_groups):
     return default().out_bytes(kind, rows, cols, num_groups)
 
 
-def rearrange(kind, scales, offs, out=None):
-    return default().rearrange(kind, scales, offs, out)
+def rearrange(kind, scales, offs, out=None, threads=None):
+    return default().rearrange(kind, scales, offs, out, threads)
 
 
 def out_bytes_3d(experts, rows, cols):

@@ -48,6 +48,7 @@
 
 #include <stdint.h>
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -160,6 +161,146 @@ int oracle_K_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t l
         group_start = offs[g];
     }
     return ORACLE_OK;
+}
+
+/*
+ * The same two definitions, one call shared among `threads` POSIX threads: the
+ * CPU baseline of one conversion spread over the host's cores. The work is
+ * split into pieces of (group, 128-row block) — for K groups a row block of one
+ * group's matrix, for M groups a row block of one group's padded rows — and
+ * each piece runs exactly the loop body of oracle_M_groups / oracle_K_groups
+ * over its own positions; pieces are handed out one at a time from a shared
+ * counter. The zero-fill of the whole output before the copy is split into
+ * equal ranges the same way, and all of it ends (the threads are joined)
+ * before the first piece is copied. Nothing else differs: the same positions receive
+ * the same bytes, in another order.
+ */
+
+struct piece_job {
+    int kgroups;
+    const uint8_t *scales;
+    int64_t rows, cols, ld;
+    const int32_t *offs;
+    int32_t num_groups;
+    uint8_t *out;
+    int64_t total;
+    const int64_t *first_piece; /* pieces of groups before g; num_groups + 1 entries */
+    const int64_t *group_start; /* first input row (M) or column (K) of group g */
+    const int64_t *group_base;  /* output row (M) or padded column (K) where group g starts */
+    int64_t zero_parts;
+    int64_t next;               /* shared counter: next zero range, then next piece */
+};
+
+static int64_t take(struct piece_job *job) { return __atomic_fetch_add(&job->next, 1, __ATOMIC_RELAXED); }
+
+static void run_piece(const struct piece_job *job, int64_t p) {
+    int32_t g = 0;
+    while (job->first_piece[g + 1] <= p) ++g;
+    int64_t i0 = 128 * (p - job->first_piece[g]);
+    int64_t start = job->group_start[g];
+    int64_t size = job->offs[g] - start;
+    if (!job->kgroups) {
+        int64_t padded_cols = round_up(job->cols, 4);
+        int64_t out_row = job->group_base[g];
+        for (int64_t i = i0; i < i0 + 128; ++i) {
+            for (int64_t j = 0; j < padded_cols; ++j) {
+                uint8_t v = 0;
+                if (i < size && j < job->cols) v = job->scales[(start + i) * job->ld + j];
+                job->out[blocked_byte(padded_cols, out_row + i, j)] = v;
+            }
+        }
+    } else {
+        int64_t padded_rows = round_up(job->rows, 128);
+        int64_t padded_width = round_up(size, 4);
+        uint8_t *dst = job->out + padded_rows * job->group_base[g];
+        for (int64_t i = i0; i < i0 + 128; ++i) {
+            for (int64_t j = 0; j < padded_width; ++j) {
+                uint8_t v = 0;
+                if (i < job->rows && j < size) v = job->scales[i * job->ld + start + j];
+                dst[blocked_byte(padded_width, i, j)] = v;
+            }
+        }
+    }
+}
+
+static void *zero_worker(void *arg) {
+    struct piece_job *job = (struct piece_job *)arg;
+    for (;;) {
+        int64_t z = take(job);
+        if (z >= job->zero_parts) break;
+        int64_t per = (job->total + job->zero_parts - 1) / job->zero_parts;
+        int64_t lo = z * per, hi = lo + per < job->total ? lo + per : job->total;
+        if (lo < hi) memset(job->out + lo, 0, (size_t)(hi - lo));
+    }
+    return 0;
+}
+
+static void *copy_worker(void *arg) {
+    struct piece_job *job = (struct piece_job *)arg;
+    int64_t pieces = job->first_piece[job->num_groups];
+    for (;;) {
+        int64_t p = take(job);
+        if (p >= pieces) break;
+        run_piece(job, p);
+    }
+    return 0;
+}
+
+/* Runs fn on `threads` threads (this one included) and joins them. */
+static void run_workers(void *(*fn)(void *), struct piece_job *job, int threads) {
+    pthread_t tid[256];
+    int n = threads < 1 ? 1 : (threads > 256 ? 256 : threads), started = 0;
+    for (; started < n - 1; ++started)
+        if (pthread_create(&tid[started], 0, fn, job) != 0) break;
+    fn(job);
+    for (int t = 0; t < started; ++t) pthread_join(tid[t], 0);
+}
+
+static int grouped_threads(int kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                           const int32_t *offs, int32_t num_groups, uint8_t *out, int threads) {
+    int64_t total = kgroups ? oracle_K_groups_out_bytes(rows, cols, num_groups)
+                            : oracle_M_groups_out_bytes(rows, cols, num_groups);
+    int rc = check_args(scales, rows, cols, ld, offs, num_groups, out, total, kgroups ? cols : rows);
+    if (rc != ORACLE_OK) return rc;
+    if (total == 0) return ORACLE_OK;
+    int64_t *first_piece = (int64_t *)malloc(3 * ((size_t)num_groups + 1) * sizeof(int64_t));
+    if (!first_piece) return ORACLE_EBADPTR;
+    int64_t *group_start = first_piece + num_groups + 1, *group_base = group_start + num_groups + 1;
+    int64_t start = 0, base = 0, pieces = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t size = offs[g] - start;
+        first_piece[g] = pieces;
+        group_start[g] = start;
+        group_base[g] = base;
+        if (kgroups) {
+            /* an empty group has no matrix and no piece */
+            pieces += size > 0 ? round_up(rows, 128) / 128 : 0;
+            base += round_up(size, 4);
+        } else {
+            pieces += round_up(size, 128) / 128;
+            base += round_up(size, 128);
+        }
+        start = offs[g];
+    }
+    first_piece[num_groups] = pieces;
+    struct piece_job job = {kgroups, scales, rows, cols, ld, offs, num_groups, out, total,
+                            first_piece, group_start, group_base, 0, 0};
+    job.zero_parts = 4 * (int64_t)(threads < 1 ? 1 : threads);
+    run_workers(zero_worker, &job, threads); /* every zero store lands before any copy starts */
+    job.next = 0;
+    run_workers(copy_worker, &job, threads);
+    free(first_piece);
+    return ORACLE_OK;
+}
+
+int oracle_M_groups_threads(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                            const int32_t *offs, int32_t num_groups, uint8_t *out, int threads) {
+    return grouped_threads(0, scales, rows, cols, ld, offs, num_groups, out, threads);
+}
+
+int oracle_K_groups_threads(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
+                            const int32_t *offs, int32_t num_groups, uint8_t *out, int threads) {
+    return grouped_threads(1, scales, rows, cols, ld, offs, num_groups, out, threads);
 }
 
 /*

@@ -23,6 +23,10 @@ int oracle_M_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t l
                     int32_t num_groups, uint8_t *out);
 int oracle_K_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld, const int32_t *offs,
                     int32_t num_groups, uint8_t *out);
+int oracle_M_groups_threads(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld, const int32_t *offs,
+                            int32_t num_groups, uint8_t *out, int threads);
+int oracle_K_groups_threads(const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld, const int32_t *offs,
+                            int32_t num_groups, uint8_t *out, int threads);
 int64_t oracle_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols);
 int oracle_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols, int64_t expert_stride, int64_t ld,
               uint8_t *out);
@@ -126,6 +130,15 @@ static void rearrange_cases(void) {
                                        : oracle_K_groups(in, rows, cols, ld, offs, G, out);
                     CHECK(rc == 0, "%s rearrange rows %lld cols %lld G %d: rc %d", kind ? "K" : "M",
                           (long long)rows, (long long)cols, G, rc);
+                    /* the same call shared among threads writes the same bytes */
+                    uint8_t *par = exact(n_out);
+                    int threads = 1 + (int)below(5);
+                    rc = kind == 0 ? oracle_M_groups_threads(in, rows, cols, ld, offs, G, par, threads)
+                                   : oracle_K_groups_threads(in, rows, cols, ld, offs, G, par, threads);
+                    CHECK(rc == 0 && (n_out == 0 || memcmp(par, out, (size_t)n_out) == 0),
+                          "%s threaded rearrange rows %lld cols %lld G %d threads %d: rc %d", kind ? "K" : "M",
+                          (long long)rows, (long long)cols, G, threads, rc);
+                    free(par);
                     /* the inverse restores every byte that lies in a group; the rest comes back zero */
                     uint8_t *back = exact(rows * cols);
                     rc = kind == 0 ? oracle_unrearrange_M_groups(out, rows, cols, offs, G, back, cols)

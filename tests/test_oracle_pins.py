@@ -304,3 +304,20 @@ def test_unrearrange_planted_mistake_is_caught(name):
         return fails
 
     assert pins.with_mutant(old, new, all_pins), "mutant '%s' passed every pin" % name
+
+
+@pytest.mark.parametrize("kind", ["M", "K"])
+def test_threaded_call_equals_the_definition(orc, kind):
+    # the CPU baseline's all-core form of one call: the same bytes as the single-threaded definition
+    # (itself pinned above), on random shapes, strides, empty groups and short totals, for several
+    # thread counts, and on the large named workload of each kind
+    rng = np.random.default_rng(300 if kind == "M" else 400)
+    for _ in range(40):
+        rows, cols, ld, offs = pins.random_case(rng, kind)
+        buf = rng.integers(0, 256, size=max(rows * ld, 1), dtype=np.uint8)
+        A = np.lib.stride_tricks.as_strided(buf, shape=(rows, cols), strides=(ld, 1))
+        want = orc.rearrange(kind, A, offs)
+        for threads in (1, 2, 3, 8):
+            assert np.array_equal(orc.rearrange(kind, A, offs, threads=threads), want), (rows, cols, ld, offs)
+    w = workloads.make("m_groups_skinny" if kind == "M" else "k_groups")
+    assert np.array_equal(orc.rearrange(kind, w.scales, w.offs, threads=8), orc.rearrange(kind, w.scales, w.offs))

@@ -48,32 +48,18 @@ def _load():
             "HIP library %s is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)" % LIBRARY)
     lib = ctypes.CDLL(LIBRARY)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
-    for name in ("mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes"):
-        fn = getattr(lib, name)
-        fn.argtypes = [i64, i64, i32]
-        fn.restype = i64
     for name in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp]
         fn.restype = ctypes.c_int
-    lib.mx_rearrange_3d_out_bytes.argtypes = [i64, i64, i64]
-    lib.mx_rearrange_3d_out_bytes.restype = i64
     lib.mx_block_rearrange_3d.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp]
     lib.mx_block_rearrange_3d.restype = ctypes.c_int
-    lib.mx_quantize_dim0_M_groups_scale_bytes.argtypes = [i64, i64, i32]
-    lib.mx_quantize_dim0_M_groups_scale_bytes.restype = i64
     lib.mx_quantize_dim0_M_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
     lib.mx_quantize_dim0_M_groups.restype = ctypes.c_int
-    lib.mx_quantize_dim1_K_groups_scale_bytes.argtypes = [i64, i64, i32]
-    lib.mx_quantize_dim1_K_groups_scale_bytes.restype = i64
-    lib.mx_quantize_dim1_3d_scale_bytes.argtypes = [i64, i64, i64]
-    lib.mx_quantize_dim1_3d_scale_bytes.restype = i64
     lib.mx_quantize_dim1_3d.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.mx_quantize_dim1_3d.restype = ctypes.c_int
     lib.mx_quantize_dim1_K_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp]
     lib.mx_quantize_dim1_K_groups.restype = ctypes.c_int
-    lib.mx_pad_M_groups_out_rows.argtypes = [i64, i32]
-    lib.mx_pad_M_groups_out_rows.restype = i64
     lib.mx_pad_M_groups.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp]
     lib.mx_pad_M_groups.restype = ctypes.c_int
     lib.mx_unpad_M_groups.argtypes = [vp, i64, i64, vp, i32, vp, i64, vp]
@@ -82,8 +68,6 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, i64, i64, vp, i32, vp, i64, vp]
         fn.restype = ctypes.c_int
-    lib.mx_rearrange_strerror.argtypes = [ctypes.c_int]
-    lib.mx_rearrange_strerror.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -93,23 +77,86 @@ def library():
     return _load()
 
 
+# Output sizes and status texts. The C headers define these as static inline functions (the library
+# exports only the entry points); the same formulas are restated here to size the outputs torch allocates.
+# A CPU test compiles the headers and checks every function below against them.
+
+def _round_up(x, m):
+    return (x + m - 1) // m * m
+
+
 def mx_rearrange_M_groups_out_bytes(rows, cols, num_groups):
-    return int(_load().mx_rearrange_M_groups_out_bytes(rows, cols, num_groups))
+    """(rows + 128*G) * round_up(cols, 4); -1 for invalid sizes (include/mx_rearrange.h)."""
+    if rows < 0 or cols < 0 or num_groups < 1:
+        return -1
+    return (rows + 128 * num_groups) * _round_up(cols, 4)
 
 
 def mx_rearrange_K_groups_out_bytes(rows, cols, num_groups):
-    return int(_load().mx_rearrange_K_groups_out_bytes(rows, cols, num_groups))
+    """round_up(rows, 128) * (cols + 4*G); -1 for invalid sizes (include/mx_rearrange.h)."""
+    if rows < 0 or cols < 0 or num_groups < 1:
+        return -1
+    return _round_up(rows, 128) * (cols + 4 * num_groups)
 
 
 def mx_rearrange_3d_out_bytes(experts, rows, cols):
-    return int(_load().mx_rearrange_3d_out_bytes(experts, rows, cols))
+    """E * round_up(rows, 128) * round_up(cols, 4); -1 for invalid sizes (include/mx_rearrange.h)."""
+    lim = (1 << 31) - 128
+    if experts < 0 or rows < 0 or cols < 0 or rows >= lim or cols >= lim:
+        return -1
+    per_expert = _round_up(rows, 128) * _round_up(cols, 4)
+    if per_expert > 0 and experts > ((1 << 63) - 1) // per_expert:
+        return -1
+    return experts * per_expert
+
+
+def mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups):
+    """(rows + 128*G) * round_up(K/32, 4); -1 for invalid sizes (include/mx_quantize.h)."""
+    if rows < 0 or K < 0 or K % 32 != 0 or num_groups < 1:
+        return -1
+    return (rows + 128 * num_groups) * _round_up(K // 32, 4)
+
+
+def mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups):
+    """round_up(N, 128) * (T/32 + 4*G); -1 for invalid sizes (include/mx_quantize.h)."""
+    if T < 0 or N < 0 or T % 32 != 0 or num_groups < 1:
+        return -1
+    return _round_up(N, 128) * (T // 32 + 4 * num_groups)
+
+
+def mx_quantize_dim1_3d_scale_bytes(experts, K, N):
+    """E * round_up(N, 128) * round_up(K/32, 4); -1 for invalid sizes (include/mx_quantize.h)."""
+    if experts < 0 or K < 0 or N < 0 or K % 32 != 0:
+        return -1
+    return experts * _round_up(N, 128) * _round_up(K // 32, 4)
+
+
+def mx_pad_M_groups_out_rows(rows, num_groups):
+    """rows + 128*G; -1 for invalid sizes (include/mx_pad.h)."""
+    if rows < 0 or num_groups < 1:
+        return -1
+    return rows + 128 * num_groups
+
+
+STATUS_TEXT = {
+    0: "success",
+    -1: "a required pointer is NULL",
+    -2: "invalid shape or stride: negative, too large, or a row stride out of its range",
+    -3: "num_groups out of range (at least 1; the casts and the inverse also cap it)",
+    -4: "a buffer or row stride is not aligned as the entry point requires",
+    -5: "HIP kernel launch failed",
+}
+
+
+def mx_rearrange_strerror(status):
+    """Text of a status code (include/mx_rearrange.h)."""
+    return STATUS_TEXT.get(status, "unknown status")
 
 
 class RearrangeError(RuntimeError):
     def __init__(self, status):
         self.status = status
-        super().__init__("mx_block_rearrange failed (%d): %s"
-                         % (status, _load().mx_rearrange_strerror(status).decode()))
+        super().__init__("mx_block_rearrange failed (%d): %s" % (status, mx_rearrange_strerror(status)))
 
 
 def _call(kind, scales, group_end_offsets, out, stream):
@@ -131,8 +178,8 @@ def _call(kind, scales, group_end_offsets, out, stream):
         raise ValueError("scales must have unit column stride (row-major rows)")
     row_stride = scales.stride(0) if rows > 1 else cols
     G = group_end_offsets.numel()
-    size_fn = lib.mx_rearrange_M_groups_out_bytes if kind == "M" else lib.mx_rearrange_K_groups_out_bytes
-    n = int(size_fn(rows, cols, G))
+    size_fn = mx_rearrange_M_groups_out_bytes if kind == "M" else mx_rearrange_K_groups_out_bytes
+    n = size_fn(rows, cols, G)
     if n < 0:
         raise ValueError("invalid sizes rows=%d cols=%d num_groups=%d" % (rows, cols, G))
     if out is None:
@@ -191,7 +238,7 @@ def mx_block_rearrange_3d(scales, out=None, stream=None):
         raise ValueError("scales must have unit column stride")
     row_stride = scales.stride(1) if rows > 1 else cols
     expert_stride = scales.stride(0) if E > 1 else rows * row_stride
-    n = int(lib.mx_rearrange_3d_out_bytes(E, rows, cols))
+    n = mx_rearrange_3d_out_bytes(E, rows, cols)
     if n < 0:
         raise ValueError("invalid sizes experts=%d rows=%d cols=%d" % (E, rows, cols))
     if out is None:
@@ -218,8 +265,8 @@ def _unrearrange(kind, blocked, rows, cols, group_end_offsets, out, stream):
         raise TypeError("blocked must be a contiguous torch.uint8 GPU tensor")
     _check_offsets(group_end_offsets, blocked.device)
     G = group_end_offsets.numel()
-    size_fn = lib.mx_rearrange_M_groups_out_bytes if kind == "M" else lib.mx_rearrange_K_groups_out_bytes
-    n = int(size_fn(rows, cols, G))
+    size_fn = mx_rearrange_M_groups_out_bytes if kind == "M" else mx_rearrange_K_groups_out_bytes
+    n = size_fn(rows, cols, G)
     if n < 0 or blocked.numel() < n:
         raise ValueError("blocked must hold the %d bytes of the forward output" % max(n, 0))
     if out is None:
@@ -248,10 +295,6 @@ def mx_block_unrearrange_K_groups(blocked, rows, cols, group_end_offsets, out=No
     return _unrearrange("K", blocked, rows, cols, group_end_offsets, out, stream)
 
 
-def mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups):
-    return int(_load().mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups))
-
-
 def mx_quantize_dim0_M_groups(x, group_end_offsets, q=None, scales=None, stream=None):
     """MXFP8 cast along rows (blocks of 32) with the scales placed in the M-groups blocked layout.
 
@@ -276,7 +319,7 @@ def mx_quantize_dim0_M_groups(x, group_end_offsets, q=None, scales=None, stream=
         raise ValueError("x must have unit column stride")
     row_stride = x.stride(0) if rows > 1 else K
     G = group_end_offsets.numel()
-    n = int(lib.mx_quantize_dim0_M_groups_scale_bytes(rows, K, G))
+    n = mx_quantize_dim0_M_groups_scale_bytes(rows, K, G)
     if n < 0:
         raise ValueError("invalid sizes rows=%d K=%d num_groups=%d" % (rows, K, G))
     if q is None:
@@ -295,10 +338,6 @@ def mx_quantize_dim0_M_groups(x, group_end_offsets, q=None, scales=None, stream=
     if rc != 0:
         raise RearrangeError(rc)
     return q, scales
-
-
-def mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups):
-    return int(_load().mx_quantize_dim1_K_groups_scale_bytes(T, N, num_groups))
 
 
 def mx_quantize_dim1_K_groups(x, token_group_end_offsets, qT=None, scales=None, stream=None):
@@ -326,7 +365,7 @@ def mx_quantize_dim1_K_groups(x, token_group_end_offsets, qT=None, scales=None, 
         raise ValueError("x must have unit column stride")
     row_stride = x.stride(0) if T > 1 else N
     G = offs.numel()
-    n = int(lib.mx_quantize_dim1_K_groups_scale_bytes(T, N, G))
+    n = mx_quantize_dim1_K_groups_scale_bytes(T, N, G)
     if n < 0:
         raise ValueError("invalid sizes T=%d N=%d num_groups=%d" % (T, N, G))
     if qT is None:
@@ -365,10 +404,6 @@ def _check_offsets(offs, device):
         raise ValueError("group_end_offsets must be contiguous")
 
 
-def mx_quantize_dim1_3d_scale_bytes(experts, K, N):
-    return int(_load().mx_quantize_dim1_3d_scale_bytes(experts, K, N))
-
-
 def mx_quantize_dim1_3d(w, q=None, scales=None, stream=None):
     """MXFP8 cast of stacked expert weights along their first matrix dimension, written per expert.
 
@@ -387,7 +422,7 @@ def mx_quantize_dim1_3d(w, q=None, scales=None, stream=None):
         raise ValueError("w must have unit column stride")
     row_stride = w.stride(1) if K > 1 else N
     expert_stride = w.stride(0) if E > 1 else K * row_stride
-    n = int(lib.mx_quantize_dim1_3d_scale_bytes(E, K, N))
+    n = mx_quantize_dim1_3d_scale_bytes(E, K, N)
     if n < 0:
         raise ValueError("invalid sizes E=%d K=%d N=%d" % (E, K, N))
     if q is None:
@@ -428,7 +463,7 @@ def mx_pad_M_groups(data, group_end_offsets, out=None, stream=None):
         raise ValueError("data must have unit column stride")
     row_stride = d.stride(0) if rows > 1 else cols
     G = group_end_offsets.numel()
-    out_rows = int(lib.mx_pad_M_groups_out_rows(rows, G))
+    out_rows = mx_pad_M_groups_out_rows(rows, G)
     if out_rows < 0:
         raise ValueError("invalid sizes rows=%d num_groups=%d" % (rows, G))
     if out is None:
@@ -461,7 +496,7 @@ def mx_unpad_M_groups(padded, rows, group_end_offsets, out=None, stream=None):
     _check_offsets(group_end_offsets, src.device)
     G = group_end_offsets.numel()
     cols = src.shape[1]
-    if src.shape[0] != int(lib.mx_pad_M_groups_out_rows(rows, G)):
+    if src.shape[0] != mx_pad_M_groups_out_rows(rows, G):
         raise ValueError("padded must have rows + 128*G rows")
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
@@ -495,6 +530,8 @@ __all__ = [
     "mx_block_rearrange_K_groups",
     "mx_rearrange_M_groups_out_bytes",
     "mx_rearrange_K_groups_out_bytes",
+    "mx_pad_M_groups_out_rows",
+    "mx_rearrange_strerror",
     "RearrangeError",
     "library",
 ]

@@ -8,7 +8,7 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", name)
-           for name in ("mx_rearrange.hip", "mx_unrearrange.hip", "mx_quantize.hip", "mx_pad.hip", "mx_status.hip")]
+           for name in ("mx_rearrange.hip", "mx_unrearrange.hip", "mx_quantize.hip", "mx_pad.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmxrearrange.so")
 ARCH = "gfx950"

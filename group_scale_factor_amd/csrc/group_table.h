@@ -20,6 +20,11 @@ constexpr int kTileRows = 128;
 constexpr int kRawBufferFlags = 0x00020000;       // buffer descriptor word 3: 32-bit raw data
 constexpr uint32_t kOutOfRange = 0xfffffff0u;     // buffer offset past any range: the load returns 0
 
+// Largest grid of `threads`-thread workgroups one launch may have: the runtime
+// limits gridDim.x * blockDim.x to below 2^32 work-items. Entry points whose
+// grid would exceed it return MX_REARRANGE_ESHAPE (outputs of over 100 GB).
+constexpr int64_t max_grid(int threads) { return ((int64_t(1) << 32) - 1) / threads; }
+
 template <int CTRL>
 __device__ __forceinline__ int dpp(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);  // lanes without a source read 0

@@ -23,6 +23,7 @@
 #include "group_table.h"
 #include "mx_pad.h"
 #include "mx_rearrange.h"
+#include "write_ranges.h"
 
 namespace {
 
@@ -48,23 +49,27 @@ struct PadParams {
   int groups;
 };
 
-// Source row of destination row R, or -1 for a row of zeros.
-template <bool PAD, class GROUPS>
-__device__ __forceinline__ int64_t source_row(const GROUPS &grp, int groups, int64_t R) {
+// Source row of destination row R, or -1 for a row of zeros. A source row
+// outside the source matrix (src_rows rows), which only a wrong group table
+// could give, is -1 as well: the kernel then reads nothing outside its input.
+template <bool PAD, class TABLE>
+__host__ __device__ inline int64_t source_row(const TABLE &grp, int groups, int64_t R, int64_t src_rows) {
+  int64_t s = -1;
   if (PAD) {
     const int g = grp.count_pends_le(R);
     if (g >= groups) return -1;                       // tail past the last group's padded rows
     const int start = g ? grp.end(g - 1) : 0;
     const int pstart = g ? grp.pend_at(g - 1) : 0;
     const int64_t local = R - pstart;
-    return local < grp.end(g) - start ? start + local : -1;   // past the group's rows: padding
+    s = local < grp.end(g) - start ? start + local : -1;   // past the group's rows: padding
   } else {
     const int g = grp.count_ends_le(R);
     if (g >= groups) return -1;                       // rows past the last end
     const int start = g ? grp.end(g - 1) : 0;
     const int pstart = g ? grp.pend_at(g - 1) : 0;
-    return int64_t(pstart) + (R - start);
+    s = int64_t(pstart) + (R - start);
   }
+  return s >= 0 && s < src_rows ? s : -1;
 }
 
 template <bool PAD, bool SMALL, bool VEC>
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(kPadThreads) void pad_kernel(PadParams p) {
     const bool valid = u0 + i < p.units;
     if (valid && R != looked_up) {
       looked_up = R;
-      s_row = source_row<PAD>(grp, p.groups, R);
+      s_row = source_row<PAD>(grp, p.groups, R, PAD ? int64_t(p.rows) : p.rows + 128 * int64_t(p.groups));
     }
     src_row[i] = valid ? s_row : -1;
     dst_row[i] = valid ? R : -1;
@@ -173,7 +178,7 @@ int launch_pad(bool pad, const uint8_t *src, int64_t rows, int64_t cols, int64_t
                    (reinterpret_cast<uintptr_t>(src) % 16) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0;
   const int64_t waves = (p.units + kPadUnroll - 1) / kPadUnroll;
   const int64_t grid = (waves + kPadWaves - 1) / kPadWaves;
-  if (grid > lim) return MX_REARRANGE_ESHAPE;
+  if (grid > max_grid(kPadThreads)) return MX_REARRANGE_ESHAPE;
   const bool small = num_groups <= kWave;
   const size_t lds = small ? 0 : size_t(2) * num_groups * sizeof(int);
   const void *fn;
@@ -195,11 +200,6 @@ int launch_pad(bool pad, const uint8_t *src, int64_t rows, int64_t cols, int64_t
 }  // namespace
 
 extern "C" {
-
-int64_t mx_pad_M_groups_out_rows(int64_t rows, int32_t num_groups) {
-  if (rows < 0 || num_groups < 1) return -1;
-  return rows + 128 * int64_t(num_groups);
-}
 
 int mx_pad_M_groups(const uint8_t *data, int64_t rows, int64_t cols, int64_t row_stride,
                     const int32_t *group_end_offsets, int32_t num_groups, uint8_t *padded, hipStream_t stream) {

@@ -48,6 +48,7 @@
 #include "group_table.h"
 #include "mx_quantize.h"
 #include "mx_rearrange.h"
+#include "write_ranges.h"
 
 namespace {
 
@@ -98,7 +99,7 @@ __device__ __forceinline__ void store8_nt(uint8_t *dst, uint32_t a, uint32_t b) 
 }
 
 // Byte offset of scale row R, tile column tc inside the blocked matrix of tile_cols tile columns.
-__device__ __forceinline__ int64_t scale_word_offset(int64_t R, int tc, int tile_cols) {
+__host__ __device__ inline int64_t scale_word_offset(int64_t R, int tc, int tile_cols) {
   const int64_t tile = (R / kTileRows) * tile_cols + tc;
   const int r = int(R % kTileRows);
   return tile * 512 + (r % 32) * 16 + (r / 32) * 4;
@@ -174,18 +175,12 @@ __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, con
       word |= dpp<0x118>(word);   // row_shr:8
       if (r != looked_up) {
         looked_up = r;
-        const int g = grp.count_ends_le(r);
-        scale_row = -1;
-        if (g < p.groups) {
-          const int start = g ? grp.end(g - 1) : 0;
-          const int pstart = g ? grp.pend_at(g - 1) : 0;
-          scale_row = int64_t(pstart) + (r - start);
-        }
+        scale_row = dim0_scale_row(grp, p.groups, r);
       }
       const int tc = 4 * c + (lane >> 4);
       if ((lane & 15) == 12 && scale_row >= 0 && tc < p.tile_cols) {
         const int64_t off = scale_word_offset(scale_row, tc, p.tile_cols);
-        *reinterpret_cast<uint32_t *>(p.scales + off) = uint32_t(word);
+        if (fits(off, 4, p.scale_bytes)) *reinterpret_cast<uint32_t *>(p.scales + off) = uint32_t(word);
       }
     }
     if (++c == p.chunks) {
@@ -195,10 +190,33 @@ __device__ __forceinline__ void quantize_units(const QParams &p, int64_t u0, con
   }
 }
 
-// Zero-fill of output row block ob of the blocked scales: the padding rows of
-// the group it belongs to, or all of it past the last group.
-template <class GROUPS>
-__device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const GROUPS &grp) {
+// Row of input row r inside the blocked scales (its group's padded start plus
+// its place in the group), or -1 when r lies in no group. count_ends_le(key):
+// groups whose clamped end is <= key; end(g), pend_at(g): clamped cumulative
+// end and padded cumulative end of group g.
+template <class TABLE>
+__host__ __device__ inline int64_t dim0_scale_row(const TABLE &grp, int groups, int64_t r) {
+  const int g = grp.count_ends_le(r);
+  if (g < 0 || g >= groups) return -1;
+  const int start = g ? grp.end(g - 1) : 0;
+  const int pstart = g ? grp.pend_at(g - 1) : 0;
+  return int64_t(pstart) + (r - start);
+}
+
+// Zero-fill of output row block ob of the blocked scales: the padding rows
+// [valid, 128) of the group the block belongs to, or (past the last group)
+// the byte range `tail` of the block. Both stay inside the scale allocation:
+// valid is clamped into [0, 128], every padding-row word is checked with
+// fits(), and the tail is clamped by zero_share.
+struct Dim0ZeroBlock {
+  bool in_group;
+  int valid;
+  ZeroSpan tail;
+};
+
+template <class TABLE>
+__host__ __device__ inline Dim0ZeroBlock dim0_zero_block(const QParams &p, const TABLE &grp, int64_t ob) {
+  Dim0ZeroBlock z = {false, kTileRows, {0, 0, 0}};
   const int64_t block_bytes = int64_t(kTileRows) * p.tile_cols * 4;
   const int g = grp.count_pends_le(ob * kTileRows);
   if (g < p.groups) {
@@ -206,27 +224,53 @@ __device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const G
     const int pstart = g ? grp.pend_at(g - 1) : 0;
     const int size = grp.end(g) - start;
     const int64_t k = ob - pstart / kTileRows;
-    const int valid = int(min(int64_t(kTileRows), int64_t(size) - kTileRows * k));
-    const int pad_rows = kTileRows - valid;
-    const int n = pad_rows * p.tile_cols;
+    z.in_group = true;
+    z.valid = int(clamp64(int64_t(size) - kTileRows * k, 0, kTileRows));
+  } else {
+    const int64_t lo = ob * block_bytes > int64_t(grp.pend_at(p.groups - 1)) * p.tile_cols * 4
+                           ? ob * block_bytes
+                           : int64_t(grp.pend_at(p.groups - 1)) * p.tile_cols * 4;
+    z.tail = zero_share(lo, (ob + 1) * block_bytes, p.scale_bytes, 0, 1);
+  }
+  return z;
+}
+
+template <class GROUPS>
+__device__ __forceinline__ void zero_block(const QParams &p, int64_t ob, const GROUPS &grp) {
+  const Dim0ZeroBlock z = dim0_zero_block(p, grp, ob);
+  if (z.in_group) {
+    const int n = (kTileRows - z.valid) * p.tile_cols;
     for (int t = threadIdx.x; t < n; t += kThreads) {
-      const int rr = valid + t / p.tile_cols;
+      const int rr = z.valid + t / p.tile_cols;
       const int tc = t % p.tile_cols;
       const int64_t off = scale_word_offset(ob * kTileRows + rr, tc, p.tile_cols);
-      if (off + 4 <= p.scale_bytes) *reinterpret_cast<uint32_t *>(p.scales + off) = 0u;
+      if (fits(off, 4, p.scale_bytes)) *reinterpret_cast<uint32_t *>(p.scales + off) = 0u;
     }
   } else {
-    const int64_t lo = max(ob * block_bytes, int64_t(grp.pend_at(p.groups - 1)) * p.tile_cols * 4);
-    const int64_t hi = min((ob + 1) * block_bytes, p.scale_bytes);
-    if (lo >= hi) return;
-    // lo is a multiple of 512 (a row block boundary); hi a multiple of 4
-    const int64_t full = lo + ((hi - lo) & ~int64_t(15));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t a = lo + 16 * threadIdx.x; a < full; a += 16 * kThreads)
-      *reinterpret_cast<u32x4 *>(p.scales + a) = z;
-    for (int64_t a = full + 4 * threadIdx.x; a < hi; a += 4 * kThreads) *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int64_t a = z.tail.begin + 16 * threadIdx.x; a < z.tail.full; a += 16 * kThreads)
+      *reinterpret_cast<u32x4 *>(p.scales + a) = zero;
+    for (int64_t a = z.tail.full + 4 * threadIdx.x; a < z.tail.end; a += 4 * kThreads)
+      *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
   }
+}
+
+// Shape, units and grid of the dim0 cast (sizes validated by the caller);
+// returns the grid: the quantising workgroups, then one zero-fill workgroup
+// per output row block.
+int64_t dim0_geometry(QParams &p, int64_t rows, int64_t K, int32_t num_groups) {
+  p.rows = int(rows);
+  p.K = int(K);
+  p.chunks = int((K + kUnitElems - 1) / kUnitElems);
+  p.groups = num_groups;
+  p.tile_cols = int((K / 32 + 3) / 4);
+  p.units = rows * p.chunks;
+  p.scale_bytes = mx_quantize_dim0_M_groups_scale_bytes(rows, K, num_groups);
+  const int64_t waves = (p.units + kUnroll - 1) / kUnroll;
+  p.data_groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  p.pad_blocks = (rows + kTileRows - 1) / kTileRows + num_groups;
+  return p.data_groups + p.pad_blocks;
 }
 
 template <bool SMALL>
@@ -388,6 +432,76 @@ struct Groups1<false> {
   __device__ __forceinline__ int width_through(int g) const { return cws[g]; }
 };
 
+// What one unit of the dim1 cast reads and writes, decoded from its tile
+// column ci and feature block fb and the scanned group table (end(g): clamped
+// cumulative end in scale columns; chunks_through(g), width_through(g):
+// cumulative tile columns and padded widths; count_cch_le(key): groups whose
+// cumulative tile columns are <= key). Token runs are clamped into their token
+// range and the scale tile into the scale allocation (write_ranges.h), so a
+// wrong table can give a wrong output but no access outside the buffers.
+struct Dim1Unit {
+  int64_t t0;         // first token of the unit (over all tokens)
+  int ntok;           // tokens of the unit: a multiple of 32, <= 128
+  int64_t x_row0;     // element offset of the unit's first input row
+  int64_t q_col0;     // byte offset of the unit's first code in code row 0
+  int64_t tile_off;   // byte offset of the unit's 512-byte scale tile, -1: no scales
+  bool spare;         // a unit past the data: zero its share of the scale tail
+  ZeroSpan zero;      // that share
+};
+
+template <class TABLE>
+__host__ __device__ inline Dim1Unit dim1_unit(const Q1Params &p, const TABLE &grp, int64_t ci, int fb) {
+  Dim1Unit un = {0, 0, 0, 0, -1, false, {0, 0, 0}};
+  const int total_chunks = grp.chunks_through(p.groups - 1);
+  const int last_end = grp.end(p.groups - 1);   // scale columns covered by groups
+  const int64_t cols = p.T / 32;
+  if (ci < total_chunks) {
+    const int g = int(clamp64(grp.count_cch_le(ci), 0, p.groups - 1));
+    const int first_chunk = g ? grp.chunks_through(g - 1) : 0;
+    const int64_t k = ci - first_chunk;
+    const int S = g ? grp.end(g - 1) : 0;
+    const int w = grp.end(g) - S;
+    const int C = g ? grp.width_through(g - 1) : 0;
+    const int W = (w + 3) & ~3;
+    const int64_t t0 = 32 * (int64_t(S) + 4 * k);
+    const int64_t n = 32 * (int64_t(w) - 4 * k < 4 ? int64_t(w) - 4 * k : int64_t(4));
+    un.tile_off = p.padded_rows * C + (int64_t(fb) * (W / 4) + k) * 512;
+    if (!fits(un.tile_off, 512, p.scale_bytes)) un.tile_off = -1;
+    if (p.group_tokens > 0) {   // group g's own input and code matrices
+      const Run tl = clamp_run(t0 - int64_t(g) * p.group_tokens, n, p.group_tokens);
+      un.t0 = int64_t(g) * p.group_tokens + tl.first;
+      un.ntok = int(tl.n);
+      un.x_row0 = int64_t(g) * p.x_gstride + tl.first * p.ld;
+      un.q_col0 = int64_t(g) * p.q_gstride + tl.first;
+    } else {
+      const Run t = clamp_run(t0, n, p.T);
+      un.t0 = t.first;
+      un.ntok = int(t.n);
+      un.x_row0 = t.first * p.ld;
+      un.q_col0 = t.first;
+    }
+  } else {
+    // chunks of tokens after the last group (none with group_tokens > 0: the groups cover every token)
+    const int64_t trailing = p.group_tokens > 0 ? 0 : (cols - last_end + 3) / 4;
+    const int64_t c2 = ci - total_chunks;
+    if (c2 < trailing) {
+      const int64_t left = cols - last_end - 4 * c2;
+      const Run t = clamp_run(32 * (last_end + 4 * c2), 32 * (left < 4 ? left : 4), p.T);
+      un.t0 = t.first;
+      un.ntok = int(t.n);
+      un.x_row0 = t.first * p.ld;
+      un.q_col0 = t.first;
+    } else {
+      // spare unit: a share of the zero tail of the scale allocation
+      un.spare = true;
+      const int64_t spare = (p.units / p.nb - total_chunks - trailing) * p.nb;
+      const int64_t part = (c2 - trailing) * p.nb + fb;
+      un.zero = zero_share(p.padded_rows * grp.width_through(p.groups - 1), p.scale_bytes, p.scale_bytes, part, spare);
+    }
+  }
+  return un;
+}
+
 // 8 bf16 of a staged piece with the features at or past N zeroed (f0 = feature of the first).
 __device__ __forceinline__ uint4 mask_features(uint4 v, int f0, int N) {
   const int valid = N - f0;
@@ -437,58 +551,18 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
 
   Groups1<SMALL> grp;
   grp.init(p, group_lds);
-  const int total_chunks = grp.chunks_through(p.groups - 1);
-  const int last_end = grp.end(p.groups - 1);   // scale columns covered by groups
-  const int64_t cols = p.T / 32;
-  int64_t t0 = 0;          // first token of the unit
-  int ntok = 0;            // tokens of the unit (multiple of 32, <= 128)
-  int64_t tile_off = -1;   // byte offset of the unit's scale tile, -1: no scales
-  int64_t x_row0 = 0;      // element offset of the unit's first input row
-  int64_t q_col0 = 0;      // byte offset of the unit's first code in code row 0
-  if (ci < total_chunks) {
-    const int g = grp.count_cch_le(ci);
-    const int first_chunk = g ? grp.chunks_through(g - 1) : 0;
-    const int k = int(ci - first_chunk);
-    const int S = g ? grp.end(g - 1) : 0;
-    const int w = grp.end(g) - S;
-    const int C = g ? grp.width_through(g - 1) : 0;
-    const int W = (w + 3) & ~3;
-    t0 = 32 * int64_t(S + 4 * k);
-    ntok = 32 * min(4, w - 4 * k);
-    tile_off = p.padded_rows * C + (int64_t(fb) * (W / 4) + k) * 512;
-    if (p.group_tokens > 0) {   // group g's own input and code matrices
-      const int64_t tl = t0 - int64_t(g) * p.group_tokens;
-      x_row0 = int64_t(g) * p.x_gstride + tl * p.ld;
-      q_col0 = int64_t(g) * p.q_gstride + tl;
-    } else {
-      x_row0 = t0 * p.ld;
-      q_col0 = t0;
-    }
-  } else {
-    const int64_t trailing = (cols - last_end + 3) / 4;   // chunks of tokens after the last group
-    const int64_t c2 = ci - total_chunks;
-    if (c2 < trailing) {   // (never with group_tokens > 0: the groups cover every token)
-      t0 = 32 * (last_end + 4 * c2);
-      ntok = int(32 * min(int64_t(4), cols - last_end - 4 * c2));
-      x_row0 = t0 * p.ld;
-      q_col0 = t0;
-    } else {
-      // spare unit: a share of the zero tail of the scale allocation
-      const int64_t spare = (p.units / p.nb - total_chunks - trailing) * p.nb;
-      const int64_t part = (c2 - trailing) * p.nb + fb;
-      const int64_t lo = p.padded_rows * grp.width_through(p.groups - 1);
-      const int64_t len16 = (p.scale_bytes - lo + 15) >> 4;
-      const int64_t per = (len16 + spare - 1) / spare;
-      const int64_t b = lo + 16 * min(per * part, len16);
-      const int64_t e = min(lo + 16 * min(per * (part + 1), len16), p.scale_bytes);
-      const int64_t full = b + ((e - b) & ~int64_t(15));
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int64_t a = b + 16 * threadIdx.x; a < full; a += 16 * kThreads) *reinterpret_cast<u32x4 *>(p.scales + a) = z;
-      for (int64_t a = full + 4 * threadIdx.x; a < e; a += 4 * kThreads) *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
-      return;
-    }
+  const Dim1Unit un = dim1_unit(p, grp, ci, fb);
+  if (un.spare) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t a = un.zero.begin + 16 * threadIdx.x; a < un.zero.full; a += 16 * kThreads)
+      *reinterpret_cast<u32x4 *>(p.scales + a) = z;
+    for (int64_t a = un.zero.full + 4 * threadIdx.x; a < un.zero.end; a += 4 * kThreads)
+      *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
+    return;
   }
+  const int ntok = un.ntok;
+  const int64_t x_row0 = un.x_row0, q_col0 = un.q_col0, tile_off = un.tile_off;
 
   // stage the 128 x 128 bf16 tile: 16 pieces of 16 bytes per token row, 8 per lane
   {
@@ -572,17 +646,22 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Grid and launch of the dim1 cast; p holds the sources, outputs, strides,
-// groups and scale size (validated by the caller, scale_bytes > 0).
-int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
-  const int64_t lim = (int64_t(1) << 31) - 1;
+// Grid of the dim1 cast: p holds the sources, outputs, strides, groups and
+// scale size (validated by the caller, scale_bytes > 0); sets the feature
+// blocks and the units. False when the grid exceeds one launch.
+bool dim1_geometry(Q1Params &p, int64_t N) {
   p.N = int(N);
   p.nb = int((N + kTileFeat - 1) / kTileFeat);
   p.padded_rows = round_up(N, 128);
   // tile columns: every group's plus the trailing tokens' plus at least one spare
   const int64_t chunk_units = (p.T + kTileTok - 1) / kTileTok + p.groups + 1;
   p.units = chunk_units * p.nb;
-  if (p.units > lim) return MX_REARRANGE_ESHAPE;
+  return p.units <= max_grid(kThreads);
+}
+
+// Grid and launch of the dim1 cast.
+int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
+  if (!dim1_geometry(p, N)) return MX_REARRANGE_ESHAPE;
   const bool small = p.groups <= kWave;
   const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * p.groups * sizeof(int));
   const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)
@@ -595,11 +674,6 @@ int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
 }  // namespace
 
 extern "C" {
-
-int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t num_groups) {
-  if (rows < 0 || K < 0 || K % 32 != 0 || num_groups < 1) return -1;
-  return (rows + 128 * int64_t(num_groups)) * round_up(K / 32, 4);
-}
 
 int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_t row_stride,
                               const int32_t *group_end_offsets, int32_t num_groups, uint8_t *q,
@@ -624,18 +698,8 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
   p.q = q;
   p.scales = blocked_scales;
   p.ld = row_stride;
-  p.rows = int(rows);
-  p.K = int(K);
-  p.chunks = int((K + kUnitElems - 1) / kUnitElems);
-  p.groups = num_groups;
-  p.tile_cols = int(round_up(K / 32, 4) / 4);
-  p.units = rows * p.chunks;
-  p.scale_bytes = scale_bytes;
-  const int64_t waves = (p.units + kUnroll - 1) / kUnroll;
-  p.data_groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
-  p.pad_blocks = (rows + kTileRows - 1) / kTileRows + num_groups;
-  const int64_t grid = p.data_groups + p.pad_blocks;
-  if (grid > lim) return MX_REARRANGE_ESHAPE;
+  const int64_t grid = dim0_geometry(p, rows, K, num_groups);
+  if (grid > max_grid(kThreads)) return MX_REARRANGE_ESHAPE;
   const bool small = num_groups <= kWave;
   const size_t lds = small ? 0 : size_t(2) * num_groups * sizeof(int);
   const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim0_kernel<true>)
@@ -645,11 +709,6 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 
-
-int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_groups) {
-  if (T < 0 || N < 0 || T % 32 != 0 || num_groups < 1) return -1;
-  return round_up(N, 128) * (T / 32 + 4 * int64_t(num_groups));
-}
 
 int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t row_stride,
                               const int32_t *token_group_end_offsets, int32_t num_groups, uint8_t *qT,
@@ -678,11 +737,6 @@ int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t r
   p.groups = num_groups;
   p.scale_bytes = scale_bytes;
   return launch_dim1(p, N, stream);
-}
-
-int64_t mx_quantize_dim1_3d_scale_bytes(int64_t experts, int64_t K, int64_t N) {
-  if (experts < 0 || K < 0 || N < 0 || K % 32 != 0) return -1;
-  return experts * round_up(N, 128) * round_up(K / 32, 4);
 }
 
 int mx_quantize_dim1_3d(const uint16_t *w, int64_t experts, int64_t K, int64_t N, int64_t expert_stride,

@@ -57,6 +57,7 @@
 
 #include "group_table.h"
 #include "mx_rearrange.h"
+#include "write_ranges.h"
 
 namespace {
 
@@ -280,19 +281,15 @@ __device__ __forceinline__ void store16(uint8_t *dst, uint32_t a, uint32_t b, ui
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst));
 }
 
-// Zero-fill of part `part` of `parts` of the byte range [lo, hi); lo is
-// 16-byte aligned and hi a multiple of 4.
+// Zero-fill of part `part` of `parts` of the byte range [lo, hi) of an output
+// of `limit` bytes; lo is 16-byte aligned and hi a multiple of 4 (both clamped
+// into the output, write_ranges.h).
 template <int NT>
-__device__ __forceinline__ void zero_part(uint8_t *__restrict__ out, int64_t lo, int64_t hi, int64_t part,
-                                          int64_t parts) {
-  if (lo >= hi || parts <= 0) return;
-  const int64_t len16 = (hi - lo + 15) >> 4;
-  const int64_t per = (len16 + parts - 1) / parts;
-  const int64_t b = lo + 16 * min(per * part, len16);
-  const int64_t e = min(lo + 16 * min(per * (part + 1), len16), hi);
-  const int64_t full = b + ((e - b) & ~int64_t(15));
-  for (int64_t q = b + 16 * threadIdx.x; q < full; q += 16 * NT) store16(out + q, 0, 0, 0, 0);
-  for (int64_t q = full + 4 * threadIdx.x; q < e; q += 4 * NT) *reinterpret_cast<uint32_t *>(out + q) = 0u;
+__device__ __forceinline__ void zero_part(uint8_t *__restrict__ out, int64_t lo, int64_t hi, int64_t limit,
+                                          int64_t part, int64_t parts) {
+  const ZeroSpan z = zero_share(lo, hi, limit, part, parts);
+  for (int64_t q = z.begin + 16 * threadIdx.x; q < z.full; q += 16 * NT) store16(out + q, 0, 0, 0, 0);
+  for (int64_t q = z.full + 4 * threadIdx.x; q < z.end; q += 4 * NT) *reinterpret_cast<uint32_t *>(out + q) = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -584,7 +581,10 @@ __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Par
       const int k_lo = gs >= c_lo ? 0 : (c_lo - gs + 3) >> 2;
       const int k_hi = int(std::min<int64_t>(gw >> 2, (c_hi - gs + 3) >> 2));
       const int col0 = gs + 4 * k_lo;                   // first column of the run, in the window
-      uint8_t *dst = p.out + padded_rows * gb + block * kTileRows * gw + int64_t(512) * k_lo;
+      const int64_t dst_off = padded_rows * gb + block * kTileRows * gw + int64_t(512) * k_lo;
+      // (a correct table always passes: the run lies inside the output)
+      if (k_hi <= k_lo || !fits(dst_off, int64_t(512) * (k_hi - k_lo), p.out_bytes)) continue;
+      uint8_t *dst = p.out + dst_off;
       if (aligned && ((col0 - c_lo) & 3) == 0)
         emit_tiles<NT, false, true>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
       else
@@ -645,14 +645,15 @@ void rearrange_kernel(Params p) {
         const int ncols = min(p.unit_cols, p.cols - c0);
         const int tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
         uint8_t *dst = p.out + block * row_block_bytes + int64_t(c0) * kTileRows;
-        // the last condition, too, holds for every unit of a correct scan
-        if (nrows > 0 && ncols > 0 && (block + 1) * row_block_bytes <= p.out_bytes)
+        // the last two conditions, too, hold for every unit of a correct scan
+        if (nrows > 0 && ncols > 0 && row0 >= 0 && (block + 1) * row_block_bytes <= p.out_bytes)
           copy_unit<MODE>(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst);
       } else {
         const int64_t nblocks = p.units / p.per_row;
         const int64_t tail_units = int64_t(p.per_row) * (nblocks - h.first_unit);
         const int64_t tail_index = (block - h.first_unit) * p.per_row + slot;
-        zero_part<NT>(p.out, int64_t(h.first_unit) * row_block_bytes, p.out_bytes, tail_index, tail_units);
+        zero_part<NT>(p.out, int64_t(h.first_unit) * row_block_bytes, p.out_bytes, p.out_bytes, tail_index,
+                      tail_units);
       }
     } else {
       // the end offsets of the first 64 groups are loaded ahead of everything
@@ -676,7 +677,7 @@ void rearrange_kernel(Params p) {
         }
         const int64_t tail_cols = int64_t(p.cols) + 4 * int64_t(p.groups) - carry_width;
         const int64_t lo = padded_rows * carry_width + block * kTileRows * tail_cols;
-        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, slot - p.windows, p.tail_units);
+        zero_part<NT>(p.out, lo, lo + kTileRows * tail_cols, p.out_bytes, slot - p.windows, p.tail_units);
       }
     }
   }
@@ -817,24 +818,6 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
 }  // namespace
 
 extern "C" {
-
-int64_t mx_rearrange_M_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
-  if (rows < 0 || cols < 0 || num_groups < 1) return -1;
-  return (rows + 128 * int64_t(num_groups)) * round_up(cols, 4);
-}
-
-int64_t mx_rearrange_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
-  if (rows < 0 || cols < 0 || num_groups < 1) return -1;
-  return round_up(rows, 128) * (cols + 4 * int64_t(num_groups));
-}
-
-int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols) {
-  const int64_t lim = (int64_t(1) << 31) - 128;
-  if (experts < 0 || rows < 0 || cols < 0 || rows >= lim || cols >= lim) return -1;
-  const int64_t per_expert = round_up(rows, 128) * round_up(cols, 4);
-  if (per_expert > 0 && experts > INT64_MAX / per_expert) return -1;
-  return experts * per_expert;
-}
 
 int mx_block_rearrange_M_groups(const uint8_t *scales, int64_t rows, int64_t cols, int64_t row_stride,
                                 const int32_t *group_end_offsets, int32_t num_groups, uint8_t *out,

@@ -37,6 +37,7 @@
 
 #include "group_table.h"
 #include "mx_rearrange.h"
+#include "write_ranges.h"
 
 namespace {
 
@@ -72,6 +73,7 @@ struct UParams {
   uint8_t *out;
   int64_t ld;            // row stride of the row-major output
   int64_t units;
+  int64_t blocked_bytes; // size of the blocked input (the forward output allocation)
   int rows;
   int cols;
   int groups;
@@ -315,7 +317,7 @@ __device__ __forceinline__ void zero_region(uint8_t *out, int64_t ld, int64_t r0
                                             int64_t part, int64_t parts) {
   const int64_t w = c1 - c0;
   const int64_t total = (r1 - r0) * w;
-  if (total <= 0 || parts <= 0) return;
+  if (total <= 0 || parts <= 0 || part < 0) return;
   const int64_t per = (total + parts - 1) / parts;
   const int64_t b = min(per * part, total), e = min(per * (part + 1), total);
   for (int64_t s = b + threadIdx.x; s < e; s += GM::threads) {
@@ -347,9 +349,10 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
       const int start = g ? grp.end(g - 1) : 0;
       const int pstart = g ? grp.pend_at(g - 1) : 0;
       const int64_t k = ob - pstart / kTileRows;
-      const int row0 = start + int(k) * kTileRows;
+      const int64_t row0 = start + k * kTileRows;
       const int nrows = int(min(int64_t(kTileRows), int64_t(grp.end(g) - start) - k * kTileRows));
-      if (nrows <= 0 || ncols <= 0) return;
+      // (a correct table always passes the second test: the rows lie inside the output)
+      if (nrows <= 0 || ncols <= 0 || !fits(row0, nrows, p.rows)) return;
       uint4 v[GM::loads];
       issue_loads<GM>(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
                   uint32_t(tile_cols) * 512u);
@@ -358,7 +361,8 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
       // spare units: zero the rows after the last group
       const int64_t first_spare = grp.pend_at(p.groups - 1) / kTileRows;
       const int64_t parts = p.units - first_spare * p.per_row;
-      zero_region(p.out, p.ld, grp.end(p.groups - 1), p.rows, 0, p.cols, u - first_spare * p.per_row, parts);
+      zero_region(p.out, p.ld, clamp64(grp.end(p.groups - 1), 0, p.rows), p.rows, 0, p.cols,
+                  u - first_spare * p.per_row, parts);
     }
   } else {
     KGroups<SMALL> grp;
@@ -385,9 +389,11 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
       const int ntiles = ((hi - 1 - start) >> 2) - t0 + 1;
       const int W = (end - start + 3) & ~3;
       const int C = g ? grp.width_through(g - 1) : 0;
-      const uint8_t *src = p.blocked + padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(t0) * 512;
+      const int64_t src_off = padded_rows * C + rb * kTileRows * int64_t(W) + int64_t(t0) * 512;
+      // (a correct table always passes: the tiles read lie inside the blocked input)
+      if (ntiles <= 0 || !fits(src_off, int64_t(ntiles) * 512, p.blocked_bytes)) continue;
       uint4 v[GK::loads];
-      issue_loads<GK>(v, src, ntiles, uint32_t(ntiles) * 512u);
+      issue_loads<GK>(v, p.blocked + src_off, ntiles, uint32_t(ntiles) * 512u);
       scatter_window<GK>(strip, v, ntiles, start + 4 * t0 - c_lo, lo - c_lo, hi - c_lo);
     }
     __syncthreads();
@@ -433,9 +439,11 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
     p.per_row = int((cols + unit_cols - 1) / unit_cols);
     p.units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
   }
-  if (p.units > lim) return MX_REARRANGE_ESHAPE;
   const int pitch = wide ? GKWide::pitch : kgroups ? GKNarrow::pitch : GM::pitch;
   const int threads = wide ? GKWide::threads : kgroups ? GKNarrow::threads : GM::threads;
+  if (p.units > max_grid(threads)) return MX_REARRANGE_ESHAPE;
+  p.blocked_bytes = kgroups ? mx_rearrange_K_groups_out_bytes(rows, cols, groups)
+                            : mx_rearrange_M_groups_out_bytes(rows, cols, groups);
   const size_t lds = size_t(kTileRows) * pitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
   const void *fn = kgroups ? (small ? reinterpret_cast<const void *>(&unrearrange_kernel<true, true>)
                                     : reinterpret_cast<const void *>(&unrearrange_kernel<true, false>))

@@ -35,8 +35,12 @@ struct ihipStream_t;
 typedef struct ihipStream_t *hipStream_t;
 
 /* Rows of the padded matrix: rows + 128*num_groups (a bound on the padded total
- * for any group sizes); -1 for invalid sizes. */
-int64_t mx_pad_M_groups_out_rows(int64_t rows, int32_t num_groups);
+ * for any group sizes); -1 for invalid sizes. A static inline function of this
+ * header, not a library symbol. */
+static inline int64_t mx_pad_M_groups_out_rows(int64_t rows, int32_t num_groups) {
+  if (rows < 0 || num_groups < 1) return -1;
+  return rows + 128 * (int64_t)num_groups;
+}
 
 /*
  * data     device, rows x cols bytes, row r at data + r*row_stride (row_stride

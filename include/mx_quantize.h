@@ -42,12 +42,17 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t *hipStream_t;
 
+/* The size helpers below are static inline functions of this header, not library symbols. */
+
 /*
  * Bytes of the blocked scale output: (rows + 128*num_groups) * round_up(K/32, 4),
  * the M-groups output size for a (rows, K/32) scale matrix. -1 for invalid sizes
  * (negative, K not a multiple of 32, num_groups < 1).
  */
-int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t num_groups);
+static inline int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_t K, int32_t num_groups) {
+  if (rows < 0 || K < 0 || K % 32 != 0 || num_groups < 1) return -1;
+  return (rows + 128 * (int64_t)num_groups) * ((K / 32 + 3) / 4 * 4);
+}
 
 /*
  * x                  device pointer to bf16 values (raw 16-bit patterns), rows x K,
@@ -111,7 +116,10 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
  * Scale bytes: round_up(N, 128) * (T/32 + 4*num_groups); -1 for invalid sizes
  * (negative, T not a multiple of 32, num_groups < 1).
  */
-int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_groups);
+static inline int64_t mx_quantize_dim1_K_groups_scale_bytes(int64_t T, int64_t N, int32_t num_groups) {
+  if (T < 0 || N < 0 || T % 32 != 0 || num_groups < 1) return -1;
+  return (N + 127) / 128 * 128 * (T / 32 + 4 * (int64_t)num_groups);
+}
 
 /*
  * x                        device bf16 bit patterns, T x N, row t at x + t*row_stride
@@ -170,7 +178,10 @@ int mx_quantize_dim1_K_groups(const uint16_t *x, int64_t T, int64_t N, int64_t r
  * validation. Status codes as for mx_quantize_dim0_M_groups (MX_REARRANGE_EGROUPS
  * for E > 2048).
  */
-int64_t mx_quantize_dim1_3d_scale_bytes(int64_t experts, int64_t K, int64_t N);
+static inline int64_t mx_quantize_dim1_3d_scale_bytes(int64_t experts, int64_t K, int64_t N) {
+  if (experts < 0 || K < 0 || N < 0 || K % 32 != 0) return -1;
+  return experts * ((N + 127) / 128 * 128) * ((K / 32 + 3) / 4 * 4);
+}
 
 int mx_quantize_dim1_3d(const uint16_t *w, int64_t experts, int64_t K, int64_t N, int64_t expert_stride,
                         int64_t row_stride, uint8_t *q, uint8_t *blocked_scales, hipStream_t stream);

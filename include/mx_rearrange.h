@@ -95,19 +95,44 @@ typedef struct ihipStream_t *hipStream_t;
 #define MX_REARRANGE_ELAUNCH (-5)      /* the HIP launch failed */
 
 /*
+ * The size helpers and the status text are static inline functions of this
+ * header, not library symbols: the library exports only the entry points.
+ */
+
+/*
  * Output size in bytes for groups along M: (rows + 128*num_groups) *
  * round_up(cols, 4). This bounds the padded total for any group sizes, since
  * the sum of round_up(size_g, 128) is below rows + 128*num_groups. Returns -1
- * for invalid sizes.
+ * for invalid sizes (negative, num_groups < 1).
  */
-int64_t mx_rearrange_M_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups);
+static inline int64_t mx_rearrange_M_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
+  if (rows < 0 || cols < 0 || num_groups < 1) return -1;
+  return (rows + 128 * (int64_t)num_groups) * ((cols + 3) / 4 * 4);
+}
 
 /*
  * Output size in bytes for groups along K: round_up(rows, 128) *
  * (cols + 4*num_groups) — the byte count behind every bandwidth figure printed
- * on the K-groups pages. Returns -1 for invalid sizes.
+ * on the K-groups pages (the bench-script page's results table, the CuTeDSL
+ * page's tables). Returns -1 for invalid sizes.
  */
-int64_t mx_rearrange_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups);
+static inline int64_t mx_rearrange_K_groups_out_bytes(int64_t rows, int64_t cols, int32_t num_groups) {
+  if (rows < 0 || cols < 0 || num_groups < 1) return -1;
+  return (rows + 127) / 128 * 128 * (cols + 4 * (int64_t)num_groups);
+}
+
+/* Static text for a status code returned by any entry point of this library. */
+static inline const char *mx_rearrange_strerror(int status) {
+  switch (status) {
+    case MX_REARRANGE_OK: return "success";
+    case MX_REARRANGE_ENULL: return "a required pointer is NULL";
+    case MX_REARRANGE_ESHAPE: return "invalid shape or stride: negative, too large, or a row stride out of its range";
+    case MX_REARRANGE_EGROUPS: return "num_groups out of range (at least 1; the casts and the inverse also cap it)";
+    case MX_REARRANGE_EALIGN: return "a buffer or row stride is not aligned as the entry point requires";
+    case MX_REARRANGE_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
 
 /*
  * Groups along M (token groups): rows [offs[g-1], offs[g]) of `scales` become
@@ -144,7 +169,13 @@ int mx_block_rearrange_K_groups(const uint8_t *scales, int64_t rows, int64_t col
  * -1 for invalid sizes (negative, rows or cols >= 2^31 - 128, or a size that
  * does not fit in int64).
  */
-int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols);
+static inline int64_t mx_rearrange_3d_out_bytes(int64_t experts, int64_t rows, int64_t cols) {
+  const int64_t lim = ((int64_t)1 << 31) - 128;
+  if (experts < 0 || rows < 0 || cols < 0 || rows >= lim || cols >= lim) return -1;
+  const int64_t per_expert = (rows + 127) / 128 * 128 * ((cols + 3) / 4 * 4);
+  if (per_expert > 0 && experts > INT64_MAX / per_expert) return -1;
+  return experts * per_expert;
+}
 
 /*
  * scales         device pointer; element (e, i, j) at
@@ -191,9 +222,6 @@ int mx_block_unrearrange_M_groups(const uint8_t *blocked, int64_t rows, int64_t 
 int mx_block_unrearrange_K_groups(const uint8_t *blocked, int64_t rows, int64_t cols,
                                   const int32_t *group_end_offsets, int32_t num_groups,
                                   uint8_t *scales, int64_t row_stride, hipStream_t stream);
-
-/* Static text for a status code returned above. */
-const char *mx_rearrange_strerror(int status);
 
 #ifdef __cplusplus
 }

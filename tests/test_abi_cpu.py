@@ -5,6 +5,8 @@ arguments before any HIP call (no compute call is made here)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -23,30 +25,42 @@ def lib():
     return gsf.library()
 
 
-def declared_functions():
-    names = []
+def _header_texts():
     inc = os.path.join(ROOT, "include")
     for fname in sorted(os.listdir(inc)):
-        if not fname.endswith(".h"):
-            continue
-        text = open(os.path.join(inc, fname)).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        if fname.endswith(".h"):
+            yield re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, fname)).read(), flags=re.S)
+
+
+def declared_functions():
+    """Functions the headers declare without a body: the library's entry points."""
+    names = []
+    for text in _header_texts():
         for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M):
             names.append(m.group(1))
     return names
 
 
+def inline_helpers():
+    """Functions the headers define as static inline: size helpers and the status text."""
+    names = []
+    for text in _header_texts():
+        names += re.findall(r"^static inline [\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+ENTRY_POINTS = ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups", "mx_block_rearrange_3d",
+                "mx_quantize_dim0_M_groups", "mx_quantize_dim1_K_groups", "mx_quantize_dim1_3d",
+                "mx_pad_M_groups", "mx_unpad_M_groups", "mx_block_unrearrange_M_groups",
+                "mx_block_unrearrange_K_groups")
+HELPERS = ("mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_3d_out_bytes",
+           "mx_rearrange_strerror", "mx_quantize_dim0_M_groups_scale_bytes", "mx_quantize_dim1_K_groups_scale_bytes",
+           "mx_quantize_dim1_3d_scale_bytes", "mx_pad_M_groups_out_rows")
+
+
 def test_header_declares_entry_points():
-    names = declared_functions()
-    for want in ("mx_block_rearrange_M_groups", "mx_block_rearrange_K_groups",
-                 "mx_rearrange_M_groups_out_bytes", "mx_rearrange_K_groups_out_bytes", "mx_rearrange_strerror",
-                 "mx_block_rearrange_3d", "mx_rearrange_3d_out_bytes",
-                 "mx_quantize_dim0_M_groups", "mx_quantize_dim0_M_groups_scale_bytes",
-                 "mx_quantize_dim1_K_groups", "mx_quantize_dim1_K_groups_scale_bytes",
-                 "mx_pad_M_groups", "mx_unpad_M_groups", "mx_pad_M_groups_out_rows",
-                 "mx_block_unrearrange_M_groups", "mx_block_unrearrange_K_groups",
-                 "mx_quantize_dim1_3d", "mx_quantize_dim1_3d_scale_bytes"):
-        assert want in names
+    assert sorted(declared_functions()) == sorted(ENTRY_POINTS)
+    assert sorted(inline_helpers()) == sorted(HELPERS)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +68,68 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def test_out_bytes_match_oracle(lib):
+@pytest.mark.skipif(shutil.which("nm") is None, reason="needs nm")
+def test_library_exports_only_the_entry_points(lib):
+    from group_scale_factor_amd import _build
+
+    res = subprocess.run(["nm", "-D", "--defined-only", _build.LIBRARY], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in res.stdout.splitlines() if line.split() and
+                line.split()[-1].startswith("mx_")}
+    assert exported == set(ENTRY_POINTS)
+
+
+def _header_probe(tmp_path, lang):
+    """Compiles a program that includes every header and prints each helper's value for a list of
+    arguments, and each status text; returns its output lines (a dict keyed by the call text)."""
+    calls = []
+    for rows, cols, G in [(0, 0, 1), (1, 1, 1), (1024, 16, 4), (131072, 44, 8), (16640, 160, 16), (7168, 4096, 8),
+                          (28672, 8192, 8), (130, 10, 3), (5, 4097, 200), (-1, 4, 1), (4, -1, 1), (4, 4, 0),
+                          (2147483000, 5, 4), (3, 2147483000, 7)]:
+        calls += ["mx_rearrange_M_groups_out_bytes(%d, %d, %d)" % (rows, cols, G),
+                  "mx_rearrange_K_groups_out_bytes(%d, %d, %d)" % (rows, cols, G),
+                  "mx_pad_M_groups_out_rows(%d, %d)" % (rows, G)]
+    for E, rows, cols in [(0, 0, 0), (1, 1, 1), (16, 8192, 160), (64, 8192, 160), (3, 300, 45), (7, 0, 5),
+                          (-1, 4, 4), (1, 2147483520, 4), (1, 4, 2147483520), (1 << 40, 1 << 20, 1 << 10)]:
+        calls.append("mx_rearrange_3d_out_bytes(%dLL, %d, %d)" % (E, rows, cols))
+    for a, K, G in [(0, 32, 1), (1, 32, 1), (16640, 5120, 16), (1000, 640, 5), (7, 96, 3), (300, 0, 2), (4, 48, 1),
+                    (4, 64, 0), (-1, 64, 1), (131072, 7168, 8), (2048, 300, 5)]:
+        calls += ["mx_quantize_dim0_M_groups_scale_bytes(%d, %d, %d)" % (a, K, G),
+                  "mx_quantize_dim1_K_groups_scale_bytes(%d, %d, %d)" % (K, a, G),
+                  "mx_quantize_dim1_3d_scale_bytes(%d, %d, %d)" % (G, K, a)]
+    body = "".join('  printf("%%s=%%lld\\n", "%s", (long long)%s);\n' % (c, c) for c in calls)
+    body += "".join('  printf("strerror(%d)=%%s\\n", mx_rearrange_strerror(%d));\n' % (k, k) for k in range(-7, 3))
+    src = tmp_path / ("probe." + lang)
+    src.write_text('#include <stdio.h>\n#include "mx_rearrange.h"\n#include "mx_quantize.h"\n#include "mx_pad.h"\n'
+                   "int main(void) {\n" + body + "  return 0;\n}\n")
+    exe = str(tmp_path / ("probe_" + lang))
+    compiler = ["gcc", "-std=c11"] if lang == "c" else ["g++", "-std=c++17"]
+    res = subprocess.run(compiler + ["-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), "-o", exe,
+                                     str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    return dict(line.split("=", 1) for line in out.splitlines())
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None, reason="needs gcc and g++")
+@pytest.mark.parametrize("lang", ["c", "cpp"])
+def test_header_helpers_match_the_binding(tmp_path, lang):
+    """The binding restates the headers' static inline size helpers and status texts: both agree, in
+    C and in C++, on ordinary, empty, invalid and overflowing sizes."""
+    import group_scale_factor_amd as gsf
+
+    got = _header_probe(tmp_path, lang)
+    assert len(got) > 80
+    for call, value in got.items():
+        if call.startswith("strerror("):
+            assert gsf.mx_rearrange_strerror(int(call[9:-1])) == value, call
+            continue
+        name, args = call.split("(", 1)
+        args = [int(a.strip().rstrip("L")) for a in args.rstrip(")").split(",")]
+        assert getattr(gsf, name)(*args) == int(value), call
+
+
+def test_out_bytes_match_oracle():
+    import group_scale_factor_amd as gsf
     import oracle
 
     rng = np.random.default_rng(5)
@@ -62,10 +137,10 @@ def test_out_bytes_match_oracle(lib):
               (28672, 8192, 8), (130, 10, 3), (5, 4097, 200)]
     shapes += [(int(rng.integers(0, 5000)), int(rng.integers(0, 5000)), int(rng.integers(1, 300))) for _ in range(50)]
     for rows, cols, G in shapes:
-        assert lib.mx_rearrange_M_groups_out_bytes(rows, cols, G) == oracle.out_bytes("M", rows, cols, G)
-        assert lib.mx_rearrange_K_groups_out_bytes(rows, cols, G) == oracle.out_bytes("K", rows, cols, G)
-    assert lib.mx_rearrange_M_groups_out_bytes(-1, 4, 1) == -1
-    assert lib.mx_rearrange_K_groups_out_bytes(4, 4, 0) == -1
+        assert gsf.mx_rearrange_M_groups_out_bytes(rows, cols, G) == oracle.out_bytes("M", rows, cols, G)
+        assert gsf.mx_rearrange_K_groups_out_bytes(rows, cols, G) == oracle.out_bytes("K", rows, cols, G)
+    assert gsf.mx_rearrange_M_groups_out_bytes(-1, 4, 1) == -1
+    assert gsf.mx_rearrange_K_groups_out_bytes(4, 4, 0) == -1
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
@@ -97,17 +172,18 @@ def test_argument_validation(lib, fn):
         assert f(None, 0, 9, 9, FAKE, 2, None, None) == 0
 
 
-def test_3d_out_bytes_match_oracle(lib):
+def test_3d_out_bytes_match_oracle():
+    import group_scale_factor_amd as gsf
     import oracle
 
     rng = np.random.default_rng(6)
     shapes = [(0, 0, 0), (1, 1, 1), (16, 8192, 160), (64, 8192, 160), (3, 300, 45), (7, 0, 5), (2, 5, 0)]
     shapes += [tuple(int(x) for x in rng.integers(0, [70, 5000, 400])) for _ in range(50)]
     for E, rows, cols in shapes:
-        assert lib.mx_rearrange_3d_out_bytes(E, rows, cols) == oracle.out_bytes_3d(E, rows, cols)
-    assert lib.mx_rearrange_3d_out_bytes(-1, 4, 4) == -1
-    assert lib.mx_rearrange_3d_out_bytes(1, (1 << 31) - 128, 4) == -1
-    assert lib.mx_rearrange_3d_out_bytes(1 << 40, 1 << 20, 1 << 10) == -1   # past int64
+        assert gsf.mx_rearrange_3d_out_bytes(E, rows, cols) == oracle.out_bytes_3d(E, rows, cols)
+    assert gsf.mx_rearrange_3d_out_bytes(-1, 4, 4) == -1
+    assert gsf.mx_rearrange_3d_out_bytes(1, (1 << 31) - 128, 4) == -1
+    assert gsf.mx_rearrange_3d_out_bytes(1 << 40, 1 << 20, 1 << 10) == -1   # past int64
 
 
 def test_3d_argument_validation(lib):
@@ -133,13 +209,14 @@ def test_3d_argument_validation(lib):
     assert f(None, 3, 5, 0, 0, 0, None, None) == 0
 
 
-def test_quantize_sizes_match_oracle(lib):
+def test_quantize_sizes_match_oracle():
+    import group_scale_factor_amd as gsf
     import oracle
 
     for rows, K, G in [(0, 32, 1), (1, 32, 1), (16640, 5120, 16), (1000, 640, 5), (7, 96, 3), (300, 0, 2)]:
-        assert lib.mx_quantize_dim0_M_groups_scale_bytes(rows, K, G) == oracle.out_bytes("M", rows, K // 32, G)
-    assert lib.mx_quantize_dim0_M_groups_scale_bytes(4, 48, 1) == -1   # K not a multiple of 32
-    assert lib.mx_quantize_dim0_M_groups_scale_bytes(4, 64, 0) == -1
+        assert gsf.mx_quantize_dim0_M_groups_scale_bytes(rows, K, G) == oracle.out_bytes("M", rows, K // 32, G)
+    assert gsf.mx_quantize_dim0_M_groups_scale_bytes(4, 48, 1) == -1   # K not a multiple of 32
+    assert gsf.mx_quantize_dim0_M_groups_scale_bytes(4, 64, 0) == -1
 
 
 def test_quantize_argument_validation(lib):
@@ -168,11 +245,12 @@ def test_quantize_argument_validation(lib):
 
 
 def test_quantize_dim1_sizes_and_validation(lib):
+    import group_scale_factor_amd as gsf
     import oracle
 
     for T, N, G in [(0, 5, 1), (32, 1, 1), (131072, 7168, 8), (2048, 300, 5), (96, 0, 2)]:
-        assert lib.mx_quantize_dim1_K_groups_scale_bytes(T, N, G) == oracle.out_bytes("K", N, T // 32, G)
-    assert lib.mx_quantize_dim1_K_groups_scale_bytes(48, 4, 1) == -1
+        assert gsf.mx_quantize_dim1_K_groups_scale_bytes(T, N, G) == oracle.out_bytes("K", N, T // 32, G)
+    assert gsf.mx_quantize_dim1_K_groups_scale_bytes(48, 4, 1) == -1
     f = lib.mx_quantize_dim1_K_groups
     A = 0x10000
     cases = [
@@ -196,11 +274,12 @@ def test_quantize_dim1_sizes_and_validation(lib):
 
 
 def test_quantize_dim1_3d_sizes_and_validation(lib):
+    import group_scale_factor_amd as gsf
     import oracle
 
     for E, K, N in [(0, 64, 8), (1, 32, 1), (16, 5120, 8192), (3, 96, 130), (2, 0, 5), (4, 64, 0)]:
-        assert lib.mx_quantize_dim1_3d_scale_bytes(E, K, N) == oracle.out_bytes_3d(E, N, K // 32)
-    assert lib.mx_quantize_dim1_3d_scale_bytes(2, 48, 4) == -1
+        assert gsf.mx_quantize_dim1_3d_scale_bytes(E, K, N) == oracle.out_bytes_3d(E, N, K // 32)
+    assert gsf.mx_quantize_dim1_3d_scale_bytes(2, 48, 4) == -1
     f = lib.mx_quantize_dim1_3d
     A = 0x10000
     cases = [
@@ -225,11 +304,12 @@ def test_quantize_dim1_3d_sizes_and_validation(lib):
 
 
 def test_pad_sizes_and_validation(lib):
+    import group_scale_factor_amd as gsf
     import oracle
 
     for rows, G in [(0, 1), (5, 3), (16640, 16)]:
-        assert lib.mx_pad_M_groups_out_rows(rows, G) == oracle.default().lib.oracle_pad_M_groups_out_rows(rows, G)
-    assert lib.mx_pad_M_groups_out_rows(-1, 1) == -1 and lib.mx_pad_M_groups_out_rows(4, 0) == -1
+        assert gsf.mx_pad_M_groups_out_rows(rows, G) == oracle.default().lib.oracle_pad_M_groups_out_rows(rows, G)
+    assert gsf.mx_pad_M_groups_out_rows(-1, 1) == -1 and gsf.mx_pad_M_groups_out_rows(4, 0) == -1
     A = 0x10000
     pad, unpad = lib.mx_pad_M_groups, lib.mx_unpad_M_groups
     # (data, rows, cols, ld, offs, G, padded)
@@ -257,10 +337,13 @@ def test_unrearrange_validation(lib, fn):
     assert f(None, 0, 8, A, 1, None, 8, None) == 0     # nothing to write
 
 
-def test_strerror(lib):
+def test_strerror():
+    import group_scale_factor_amd as gsf
+
     for code in (0, -1, -2, -3, -4, -5, -6, 7):   # -6 and 7: not a status, "unknown status" text
-        s = lib.mx_rearrange_strerror(code)
-        assert isinstance(s, bytes) and len(s) > 0
+        s = gsf.mx_rearrange_strerror(code)
+        assert isinstance(s, str) and len(s) > 0
+    assert gsf.mx_rearrange_strerror(-6) == "unknown status"
 
 
 def test_binding_has_no_cpu_path():
@@ -293,7 +376,7 @@ def test_product_code_never_touches_the_oracle():
                 assert "oracle" not in text.lower(), os.path.join(dirpath, f)
     src = open(os.path.join(ROOT, "oracle", "mx_rearrange_oracle.c")).read()
     includes = set(re.findall(r"#include\s*(\S+)", src))
-    assert includes <= {"<stdint.h>", "<string.h>", "<math.h>", "<stdlib.h>"}, includes
+    assert includes <= {"<stdint.h>", "<string.h>", "<math.h>", "<stdlib.h>", "<pthread.h>"}, includes
 
 
 def test_no_reversed_operand_dpp_in_device_code():
@@ -342,3 +425,21 @@ def test_profile_digest_ignores_comments_only():
     assert bench.kernel_source_digest("m_groups_skinny", lambda p: files[p]) == d1
     files[bench.kernel_source("m_groups_skinny")] = b"long k;\n"
     assert bench.kernel_source_digest("m_groups_skinny", lambda p: files[p]) != d1
+
+
+def test_grids_past_one_launch_are_rejected(lib):
+    """A launch holds fewer than 2^32 work-items; entry points whose grid would not fit one launch
+    (outputs of over 100 GB) return MX_REARRANGE_ESHAPE before any HIP call, and the largest sizes
+    below that pass validation (checked here only up to the point of a launch: no GPU)."""
+    A = 0x10000   # 16-byte aligned fake pointer, never dereferenced
+    # inverse, M groups: ((2^30 / 128) + 1 row blocks) x 8 column windows > 2^32 / 128 units
+    assert lib.mx_block_unrearrange_M_groups(A, 1 << 30, 1024, A, 1, A, 1024, None) == -2
+    # inverse, K groups: 2^23 row blocks x 4 windows of 256 columns > 2^32 / 512 units
+    assert lib.mx_block_unrearrange_K_groups(A, 1 << 30, 1024, A, 1, A, 1024, None) == -2
+    # pad: 2^28 + 128 rows of one 1 KB unit, 2 units per wave, 2 waves per workgroup > 2^32 / 128
+    assert lib.mx_pad_M_groups(A, 1 << 28, 1024, 1024, A, 1, A, None) == -2
+    assert lib.mx_unpad_M_groups(A, 1 << 28, 1024, A, 1, A, 1024, None) == -2
+    # dim1 cast: (2^30 / 128 + 2) tile columns x 2 feature blocks > 2^32 / 256 units
+    assert lib.mx_quantize_dim1_K_groups(A, 1 << 30, 256, 256, A, 1, A, A, None) == -2
+    # dim0 cast: 2^30 rows of one 512-element unit, 4 units per wave, 4 waves per workgroup
+    assert lib.mx_quantize_dim0_M_groups(A, 1 << 30, 512, 512, A, 1, A, A, None) == -2

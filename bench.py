@@ -3,17 +3,36 @@
 
 A step is one rearrangement launch over one batch of synthetic scales (group
 scan, lookup, strip load, in-tile interleave, zero padding, stores and tail
-fill all happen inside that launch). The default workload is the M-groups
-skinny case: scales (131072, 44) with 44-byte rows, 8 groups. `--workload`
-selects any of the other named workloads, including the per-expert (3-D)
-weight scales, where a step is one launch over all experts.
+fill all happen inside that launch). The headline workload is the large
+K-groups case: scales (28672, 8192), 8 groups along K. The other four named
+rearrangement workloads (M groups (131072, 44), (16640, 160) and (1024, 16); K
+groups (7168, 4096)) are timed the same way in the same run and reported in
+the `configs` block of the same line. `--workload` selects any other named
+workload as the headline (per-expert scales, the casts, pad, the inverse).
 
-Timing: inputs are resident in HBM before the timed region. Steps rotate over
-enough copies of input and output (1 GiB by default, four times the 256 MB
-Infinity Cache) that each step reads its input from HBM rather than from a
-cache. The K timed steps are captured once in a HIP graph (the pages' own
-K-groups benchmark timed CUDA graphs of 1000 launches) and replayed once
-between two synchronisations; `--eager` launches them one by one instead.
+Timing protocol (the same for every workload):
+  * Inputs are uploaded once and rotated over enough copies of input and
+    output (1 GiB by default, four times the 256 MB Infinity Cache) that a
+    launch never finds its input in a cache left warm by a recent launch:
+    step i uses copy i mod copies, and between two uses of one copy the
+    other copies move at least 1 GiB through the caches.
+  * The K timed launches (steps W .. W+K-1) are captured in a HIP graph (the
+    pages' own K-groups benchmark timed CUDA graphs of 1000 launches), which
+    is replayed once beforehand (one-time costs). The warm-up then runs
+    max(W, copies) launches, steps W - max(W, copies) .. W-1: every copy is
+    used once, and the copy each timed launch uses was last used a whole
+    rotation earlier — the state of a long run's steady rotation, in which
+    nothing of it is cached but its pages are mapped (a warm-up of W launches
+    on other copies only, or with a cache flush before the timed launches,
+    measured 3-15% slower per launch at K = 20 than at K = 2000; this one
+    within 1-9%, the rest being a fixed cost of a few microseconds at the
+    start of the timed region).
+  * After a synchronisation a spin kernel holds the GPU while the host
+    enqueues the timed replays behind it; HIP events on the launch stream
+    bracket the K launches only, so host enqueue time stays outside the
+    interval. `ms_per_step`, `value` and `roofline.achieved` all come from that
+    one event interval; `wall_ms` is the host time between the two
+    synchronisations around it (spin kernel included).
 
 Bytes per step follow the pages' convention: every input scale byte read once
 plus the whole output allocation written once.
@@ -35,10 +54,15 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (read+write) and µs per scale rearrange, M- and K-groups"
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_WORKLOAD = "m_groups_skinny"
-# The pages' own figure for the same scale shape and operation, M groups at (131072, 44):
-# 19.46 us for the fallback CUDA kernel ("[mxfp8 moe training] fallback cuda kernel for when
-# input doesn't meet 2d TMA constraints", Benchmarks table). GPU not named on the page.
+DEFAULT_WORKLOAD = "k_groups_large"
+# the other named rearrangement workloads, timed in the same run and reported beside the headline
+SECONDARY = ("m_groups_skinny", "k_groups", "m_groups_experts", "m_groups_tiny")
+# The pages' own times for the same scale shapes and operation (GPU not named on the pages):
+# M groups (131072, 44), 19.46 us for the fallback CUDA kernel ("[mxfp8 moe training] fallback
+# cuda kernel for when input doesn't meet 2d TMA constraints", Benchmarks table); K groups
+# 7168 x 131072 and 28672 x 262144 data, i.e. scales (7168, 4096) and (28672, 8192), 49.08 and
+# 315.47 us for the CuTeDSL kernel ("Add CuTeDSL MXFP8 K-groups scale rearrange kernel",
+# realistic-shapes table).
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
 # kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
 # 3 = M narrow row segments, 2 = K column windows of rows on 128-byte lines (6: rows at
@@ -116,27 +140,28 @@ def in_bytes_of(w):
     return w.experts * w.rows * w.cols if w.kind == "3d" else w.rows * w.cols
 
 
-def blocked_bytes_of(lib, w):
-    """Size of the blocked buffer the inverse reads (the forward layout's allocation)."""
-    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "inv_M" else lib.mx_rearrange_K_groups_out_bytes
+def blocked_bytes_of(sizes, w):
+    """Size of the blocked buffer the inverse reads (the forward layout's allocation); `sizes` is the
+    binding module, which holds the size helpers of the C headers."""
+    size_fn = sizes.mx_rearrange_M_groups_out_bytes if w.kind == "inv_M" else sizes.mx_rearrange_K_groups_out_bytes
     return int(size_fn(w.rows, w.cols, w.num_groups))
 
 
-def out_bytes_of(lib, w):
+def out_bytes_of(sizes, w):
     """Bytes written per launch: the whole output allocation(s)."""
     if w.kind in INVERSE:
         return w.rows * w.cols
     if w.kind == "pad":
-        return int(lib.mx_pad_M_groups_out_rows(w.rows, w.num_groups)) * w.cols
+        return int(sizes.mx_pad_M_groups_out_rows(w.rows, w.num_groups)) * w.cols
     if w.kind == "quant":
-        return w.rows * w.K + int(lib.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
+        return w.rows * w.K + int(sizes.mx_quantize_dim0_M_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "quant_k":
-        return w.rows * w.K + int(lib.mx_quantize_dim1_K_groups_scale_bytes(w.rows, w.K, w.num_groups))
+        return w.rows * w.K + int(sizes.mx_quantize_dim1_K_groups_scale_bytes(w.rows, w.K, w.num_groups))
     if w.kind == "quant_3d":
-        return w.experts * w.N * w.K + int(lib.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N))
+        return w.experts * w.N * w.K + int(sizes.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N))
     if w.kind == "3d":
-        return int(lib.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
-    size_fn = lib.mx_rearrange_M_groups_out_bytes if w.kind == "M" else lib.mx_rearrange_K_groups_out_bytes
+        return int(sizes.mx_rearrange_3d_out_bytes(w.experts, w.rows, w.cols))
+    size_fn = sizes.mx_rearrange_M_groups_out_bytes if w.kind == "M" else sizes.mx_rearrange_K_groups_out_bytes
     return int(size_fn(w.rows, w.cols, w.num_groups))
 
 
@@ -154,11 +179,11 @@ class Job:
         self.w = w = workloads.make(name)
         self.kind = w.kind
         lib = gsf.library()
-        self.out_bytes = out_bytes_of(lib, w)
+        self.out_bytes = out_bytes_of(gsf, w)
         self.in_bytes = in_bytes_of(w)
         self.bytes_per_step = self.in_bytes + self.out_bytes
         self.copies = max(1, min(max_copies, math.ceil(rotate_bytes / max(self.bytes_per_step, 1))))
-        self.in_alloc = blocked_bytes_of(lib, w) if w.kind in INVERSE else self.in_bytes
+        self.in_alloc = blocked_bytes_of(gsf, w) if w.kind in INVERSE else self.in_bytes
         in_pitch = align_up(self.in_alloc, 256)
         # quant: codes, then the blocked scales from the next 256-byte boundary
         self.q_pitch = (align_up(w.rows * w.K, 256) if w.kind in ("quant", "quant_k")
@@ -215,7 +240,7 @@ class Job:
 
 
 def capture(job, first, count):
-    """A HIP graph of `count` launches starting at step `first`."""
+    """A HIP graph of `count` launches: steps first .. first+count-1."""
     torch = job.torch
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -229,13 +254,83 @@ def capture(job, first, count):
     return g
 
 
-def launch_floor_us(count=500):
+class Spinner:
+    """Holds the GPU busy for a given time with torch's spin kernel, so that work the host enqueues
+    behind it starts only once all of it is queued."""
+
+    def __init__(self):
+        import torch
+
+        self.torch = torch
+        if not hasattr(torch.cuda, "_sleep"):
+            raise RuntimeError("torch.cuda._sleep is needed to hold the GPU while the timed launches are enqueued")
+        cycles = 1 << 20
+        torch.cuda._sleep(cycles)   # first launch loads the kernel
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(cycles)
+        e1.record()
+        torch.cuda.synchronize()
+        self.us_per_cycle = max(e0.elapsed_time(e1) * 1e3 / cycles, 1e-6)
+
+    def hold(self, us):
+        self.torch.cuda._sleep(int(us / self.us_per_cycle))
+
+
+def timed_launches(job, K, W, spinner, eager=False):
+    """Runs the warm-up and the K timed launches of `job` by the protocol of the module docstring.
+
+    Returns (event seconds for the K launches, host wall seconds between the synchronisations around
+    them, host seconds the first enqueue of the timed launches took, warm-up launches run)."""
+    import time as _time
+
+    torch = job.torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # warm-up: every copy once, ending right before the first timed step (step W)
+    warm_steps = range(W - max(W, job.copies), W)
+    if eager:
+        for i in warm_steps:
+            job.step(i)
+        torch.cuda.synchronize()
+        t0 = _time.perf_counter()
+        spinner.hold(1000.0)
+        ev0.record()
+        for i in range(W, W + K):
+            job.step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3, _time.perf_counter() - t0, None, len(warm_steps)
+    chunk = min(K, job.copies)
+    full, rem = divmod(K, chunk)
+    g = capture(job, W, chunk)
+    g_rem = capture(job, W + full * chunk, rem) if rem else None
+    # one replay of each graph first (one-time costs), timing the host's enqueue of it
+    t = _time.perf_counter()
+    g.replay()
+    enqueue_s = _time.perf_counter() - t
+    if g_rem is not None:
+        g_rem.replay()
+    for i in warm_steps:
+        job.step(i)
+    torch.cuda.synchronize()
+    t0 = _time.perf_counter()
+    # hold the GPU while the host enqueues the replays behind the spin kernel
+    spinner.hold(max(300.0, 4e6 * enqueue_s))
+    ev0.record()
+    for _ in range(full):
+        g.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / 1e3, _time.perf_counter() - t0, enqueue_s, len(warm_steps)
+
+
+def launch_floor_us(spinner, count=500):
     """Graph-replay cost of an empty launch on this GPU (torch's spin kernel told to spin 0 cycles),
-    timed like the workload's launches; None when torch offers no such kernel."""
+    timed like the workload's launches."""
     import torch
 
-    if not hasattr(torch.cuda, "_sleep"):
-        return None
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -247,6 +342,7 @@ def launch_floor_us(count=500):
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spinner.hold(1000.0)
     e0.record()
     g.replay()
     e1.record()
@@ -267,6 +363,25 @@ def capture_same(job, count):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     return g
+
+
+def warm_figure(job, K, spinner):
+    """Secondary figure: launches back to back on one input/output copy, which stays in the MALL and
+    the L2s when it fits. Not an HBM figure."""
+    torch = job.torch
+    n_warm = min(K, 200)
+    g_warm = capture_same(job, n_warm)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spinner.hold(1000.0)
+    ew0.record()
+    g_warm.replay()
+    ew1.record()
+    torch.cuda.synchronize()
+    warm_us = ew0.elapsed_time(ew1) * 1e3 / n_warm
+    return {"us_per_launch": round(warm_us, 3), "GBps": round(job.bytes_per_step / warm_us / 1e3, 2),
+            "launches": n_warm, "note": "one input/output copy reused: cache-resident when it fits, not an HBM figure"}
 
 
 def copy_calibration(args):
@@ -391,10 +506,22 @@ def _time_calls(call, seconds, threads):
     return sum(counts), time.perf_counter() - t0
 
 
-def cpu_baseline(name, seconds, all_core_seconds=2.0):
+def _threaded_call(w, threads):
+    """One call of the oracle on the whole of workload w, shared among `threads` host threads, or None
+    when the oracle has no threaded form for this kind of workload."""
+    import oracle
+
+    if w.kind not in ("M", "K"):
+        return None
+    return lambda: oracle.rearrange(w.kind, w.scales, w.offs, threads=threads)
+
+
+def cpu_baseline(name, seconds, all_core_seconds=3.0):
     """The CPU oracle as it is, on (a bounded sample of) the same workload: single-threaded for about
-    `seconds`, then one copy per host core at once for about `all_core_seconds` (independent runs of
-    the unchanged oracle; their aggregate rate). Same byte convention as the GPU figure."""
+    `seconds`; then, for about `all_core_seconds`, one call of the whole workload shared among one
+    thread per host core (at most MAX_CPU_THREADS) over its (group, 128-row block) pieces, or, for
+    workloads without that form, independent single-threaded copies run at once. Same byte
+    convention as the GPU figure."""
     import workloads
 
     w = workloads.make(name)
@@ -412,9 +539,23 @@ def cpu_baseline(name, seconds, all_core_seconds=2.0):
         "host_cores": ncores,
     }
     threads = min(ncores, MAX_CPU_THREADS)
-    if all_core_seconds > 0 and threads > 1:
-        reps_mt, el_mt = _time_calls(call, all_core_seconds, threads)
+    if all_core_seconds <= 0 or threads <= 1:
+        return res
+    one_call = _threaded_call(w, threads)
+    if one_call is not None:
+        one_call()   # first touch of the output pages outside the timed calls, as for the 1-core figure
+        reps_mt, el_mt = _time_calls(one_call, all_core_seconds, 1)
         res["all_cores"] = {
+            "value": round(nbytes * reps_mt / el_mt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "us_per_call": round(el_mt / reps_mt * 1e6, 1),
+            "sample": "%d calls over %s in %.1f s, each call shared among %d threads over its (group, "
+                      "128-row block) pieces" % (reps_mt, what, el_mt, threads),
+        }
+    else:
+        reps_mt, el_mt = _time_calls(call, all_core_seconds, threads)
+        res["all_cores_copies"] = {
             "value": round(nbytes * reps_mt / el_mt / 1e9, 4),
             "unit": "GB/s",
             "cores": threads,
@@ -460,7 +601,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     written = kwrite * write_scale
     import group_scale_factor_amd as gsf
 
-    out_bytes = out_bytes_of(gsf.library(), w)
+    out_bytes = out_bytes_of(gsf, w)
     d = {
         "workload": name,
         "kernel": KERNEL_NAMES.get(name),
@@ -499,18 +640,89 @@ def hbm_traffic(name, kind):
     return d.get("hbm_bytes_per_launch")
 
 
+def config_of(w, job, args):
+    """The `config` object of a workload's line."""
+    return {
+        "workload": w.name,
+        "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales",
+                 "pad": "per-group row padding of MXFP8 data (M groups)",
+                 "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales",
+                 "inv_M": "inverse rearrangement (blocked -> row-major), M groups",
+                 "inv_K": "inverse rearrangement (blocked -> row-major), K groups",
+                 "quant_3d": "MXFP8 dim1 cast of stacked expert weights, per-expert codes and blocked scales"}.get(
+            w.kind, "%s-groups" % w.kind),
+        {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape", "quant_3d": "w_shape"}.get(
+            w.kind, "scales_shape"):
+            [w.rows, w.K] if w.kind in ("quant", "quant_k") else (
+                [w.experts, w.K, w.N] if w.kind == "quant_3d" else (
+                    [w.rows, w.cols] if w.kind in ("pad",) + INVERSE else list(w.scales.shape))),
+        "num_groups": w.experts if w.kind in ("3d", "quant_3d") else w.num_groups,
+        "bytes_per_step": job.bytes_per_step,
+        "rotating_copies": job.copies,
+        "launch": "eager" if args.eager else "hip_graph",
+        "parallelism": "single_gpu",
+    }
+
+
+def measure(name, K, W, args, spinner, floor_us):
+    """Times K launches of workload `name` (after W warm-up launches); returns (result fields, kind)."""
+    import torch
+
+    job = Job(name, rotate_bytes=args.rotate_mib << 20)
+    gpu_s, wall, enqueue_s, warm_launches = timed_launches(job, K, W, spinner, eager=args.eager)
+    us_per_launch = gpu_s / K * 1e6
+    achieved = job.bytes_per_step / (gpu_s / K) / 1e9
+    warm = None if args.eager or args.no_warm else warm_figure(job, K, spinner)
+    ideal_us = job.bytes_per_step / HBM_PEAK_GBPS / 1e3
+    pages_us = PAGES_US.get(name)
+    res = {
+        "value": round(achieved, 2),
+        "ms_per_step": round(us_per_launch / 1e3, 6),
+        "us_per_launch": round(us_per_launch, 3),
+        "steps": K,
+        "warmup": W,
+        "warmup_launches_run": warm_launches,
+        "wall_ms": round(wall * 1e3, 3),
+        "first_enqueue_us": round(enqueue_s * 1e6, 1) if enqueue_s is not None else None,
+        "vs_baseline": round(pages_us / us_per_launch, 3) if pages_us else None,
+        "config": config_of(job.w, job, args),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": hbm_traffic(name, job.kind),
+            "kernel": KERNEL_NAMES.get(name),
+            "avg_launch_us": round(us_per_launch, 3),
+            "launch_floor_us": round(floor_us, 3) if floor_us is not None else None,
+            "frac_ceiling": round(ideal_us / (floor_us + ideal_us), 4) if floor_us is not None else None,
+        },
+        "warm": warm,
+    }
+    kind = job.kind
+    del job
+    torch.cuda.empty_cache()
+    return res, kind
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="comma-separated workloads timed after the headline and reported in `configs` ('' for none)")
+    ap.add_argument("--secondary-min-steps", type=int, default=200,
+                    help="launches timed for each secondary workload: max(--steps, this)")
     ap.add_argument("--rotate-mib", type=int, default=1024, help="bytes of input+output rotated over")
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
-                    help="skip the secondary cache-resident timing (profiling runs: only the timed launches)")
+                    help="skip the secondary cache-resident timing and the launch floor (profiling runs: only "
+                         "the timed launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's plain device copy of the workload's input size instead "
                          "(reference kernel of known traffic for the HBM byte counters)")
@@ -526,6 +738,9 @@ def main():
         print("bench.py measures one GPU: the rearrangement has no multi-GPU path "
               "(each GPU converts its own groups independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -539,122 +754,42 @@ def main():
     if args.copy_calibration:
         copy_calibration(args)
         return
-    job = Job(args.workload, rotate_bytes=args.rotate_mib << 20)
     K, W = args.steps, args.warmup
-
-    if args.eager:
-        warm_launches = W
-        for i in range(W):
-            job.step(i)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record()
-        for i in range(W, W + K):
-            job.step(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        # One graph covers one pass over the rotating copies (its first replay
-        # is part of the warm-up); the timed region replays it back to back.
-        chunk = min(job.copies, K)
-        g = capture(job, 0, chunk)
-        rem = K % chunk
-        g_rem = capture(job, 0, rem) if rem else None
-        warm_replays = max(1, math.ceil(W / chunk))
-        for _ in range(warm_replays):
-            g.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        warm_launches = warm_replays * chunk + rem
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record()
-        for _ in range(K // chunk):
-            g.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    gpu_s = ev0.elapsed_time(ev1) / 1e3
-    warm = None
-    if not args.eager and not args.no_warm and K > 0:
-        # secondary figure: the same launches back to back on one input/output
-        # copy, which stays in the MALL/L2 when it fits (256 MB + 8 x 4 MB)
-        n_warm = min(K, 200)
-        g_warm = capture_same(job, n_warm)
-        g_warm.replay()
-        torch.cuda.synchronize()
-        ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ew0.record()
-        g_warm.replay()
-        ew1.record()
-        torch.cuda.synchronize()
-        warm_us = ew0.elapsed_time(ew1) * 1e3 / n_warm
-        warm = {"us_per_launch": round(warm_us, 3), "GBps": round(job.bytes_per_step / warm_us / 1e3, 2),
-                "launches": n_warm, "note": "one input/output copy reused: cache-resident when it fits, "
-                                            "not an HBM figure"}
-    # the fixed cost of one graph-replayed launch, and the fraction of peak one launch of these bytes could
-    # reach even if it moved them at the full peak rate (outside the timed region; skipped when profiling)
-    floor = launch_floor_us() if not args.eager and not args.no_warm and K > 0 else None
-    us_per_launch = gpu_s / K * 1e6
-    value = job.bytes_per_step * K / wall / 1e9
-    achieved = job.bytes_per_step / (gpu_s / K) / 1e9
-    pages_us = PAGES_US.get(args.workload)
-    w = job.w
+    spinner = Spinner()
+    # the fixed cost of one graph-replayed launch (outside every timed region; skipped when profiling)
+    floor = launch_floor_us(spinner) if not args.eager and not args.no_warm else None
+    head, kind = measure(args.workload, K, W, args, spinner, floor)
+    configs = {}
+    for name in [n for n in args.secondary.split(",") if n and n != args.workload]:
+        r, _ = measure(name, max(K, args.secondary_min_steps), W, args, spinner, floor)
+        cfg = r["config"]
+        configs[name] = {"us_per_launch": r["us_per_launch"], "value": r["value"], "unit": "GB/s",
+                         "frac": r["roofline"]["frac"], "frac_ceiling": r["roofline"]["frac_ceiling"],
+                         "traffic": r["roofline"]["traffic"], "kernel": r["roofline"]["kernel"],
+                         "steps": r["steps"], "warmup": r["warmup"], "vs_baseline": r["vs_baseline"],
+                         "scales_shape": cfg.get("scales_shape"), "num_groups": cfg["num_groups"],
+                         "bytes_per_step": cfg["bytes_per_step"], "rotating_copies": cfg["rotating_copies"]}
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "warmup_launches_run": warm_launches,
-        "ms_per_step": round(wall / K * 1e3, 6),
-        "us_per_launch": round(us_per_launch, 3),
+        "warmup_launches_run": head["warmup_launches_run"],
+        "ms_per_step": head["ms_per_step"],
+        "us_per_launch": head["us_per_launch"],
+        "wall_ms": head["wall_ms"],
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(pages_us / (wall / K * 1e6), 3) if pages_us else None,
-        "dtype": "bf16->e4m3 (f32 arithmetic)" if w.kind in ("quant", "quant_k", "quant_3d") else "u8",
+        "vs_baseline": head["vs_baseline"],
+        "dtype": "bf16->e4m3 (f32 arithmetic)" if kind in ("quant", "quant_k", "quant_3d") else "u8",
         "data": "synthetic",
-        "config": {
-            "workload": args.workload,
-            "kind": {"3d": "per-expert", "quant": "MXFP8 dim0 cast, M-groups blocked scales",
-                     "pad": "per-group row padding of MXFP8 data (M groups)",
-                     "quant_k": "MXFP8 dim1 cast (tokens x features), K-groups blocked scales",
-                     "inv_M": "inverse rearrangement (blocked -> row-major), M groups",
-                     "inv_K": "inverse rearrangement (blocked -> row-major), K groups",
-                     "quant_3d": "MXFP8 dim1 cast of stacked expert weights, per-expert codes and blocked scales"}.get(
-                w.kind, "%s-groups" % w.kind),
-            {"quant": "x_shape", "quant_k": "x_shape", "pad": "data_shape", "quant_3d": "w_shape"}.get(
-                w.kind, "scales_shape"):
-                [w.rows, w.K] if w.kind in ("quant", "quant_k") else (
-                    [w.experts, w.K, w.N] if w.kind == "quant_3d" else (
-                        [w.rows, w.cols] if w.kind in ("pad",) + INVERSE else list(w.scales.shape))),
-            "num_groups": w.experts if w.kind in ("3d", "quant_3d") else w.num_groups,
-            "bytes_per_step": job.bytes_per_step,
-            "rotating_copies": job.copies,
-            "launch": "eager" if args.eager else "hip_graph",
-            "parallelism": "single_gpu",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": hbm_traffic(args.workload, w.kind),
-            "kernel": KERNEL_NAMES.get(args.workload),
-            "avg_launch_us": round(us_per_launch, 3),
-            "launch_floor_us": round(floor, 3) if floor is not None else None,
-            "frac_ceiling": (round((job.bytes_per_step / HBM_PEAK_GBPS / 1e3) /
-                                   (floor + job.bytes_per_step / HBM_PEAK_GBPS / 1e3), 4)
-                             if floor is not None else None),
-        },
-        "warm": warm,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "configs": configs,
+        "warm": head["warm"],
+        "first_enqueue_us": head["first_enqueue_us"],
         "cpu_baseline": None,
     }
     if not args.no_cpu and args.cpu_seconds > 0 and int(os.environ.get("RANK", "0")) == 0:

@@ -53,6 +53,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "group_table.h"
@@ -69,10 +70,12 @@ namespace {
 constexpr int kMaxUnitCols = 112;
 constexpr int kMinUnitCols = 32;              // narrowest chunk the host splits M row blocks into
 // K groups: input windows of 256 columns (two 128-byte lines per row when rows
-// are line aligned). A group's tile starts 4*k columns after the group's first
-// column and belongs to the window holding that start, so a window's tiles
-// read up to 3 columns past it.
+// are line aligned), or 512 where that grid would need a small second pass
+// over the chip (see launch()). A group's tile starts 4*k columns after the
+// group's first column and belongs to the window holding that start, so a
+// window's tiles read up to 3 columns past it.
 constexpr int kWinCols = 256;
+constexpr int kWinColsWide = 512;
 constexpr int kWinColsAny = 128;              // windows of rows that do not start on 128-byte lines
 constexpr int kTailColsPerUnit = 128;         // K: tail units per row block = ceil(4G / this)
 constexpr int kTargetUnits = 1024;            // M: split row blocks into chunks until this many units
@@ -101,14 +104,18 @@ enum Mode : int {
   kModeMRows = 1,   // M groups, one row segment at a time
   kModeMRowsNarrow = 3,  // M groups, one row segment of at most kNarrowUnitCols at a time
   kModeKWindows = 2,  // K groups, column windows of rows that start 128-byte aligned
+  kModeKWindowsWide = 7,  // the same with windows of kWinColsWide columns
   kModeKWindowsAny = 6,  // K groups, column windows of rows at any alignment
   kMode3d = 4,      // per-expert matrices, one row segment at a time, no group lookup
   kMode3dWide = 5,  // the same with twice the threads, for grids of several units per CU slot
 };
 
 constexpr bool is_3d(int mode) { return mode == kMode3d || mode == kMode3dWide; }
-constexpr bool is_k(int mode) { return mode == kModeKWindows || mode == kModeKWindowsAny; }
-constexpr int win_cols_for(int mode) { return mode == kModeKWindows ? kWinCols : kWinColsAny; }
+constexpr bool is_k(int mode) { return mode == kModeKWindows || mode == kModeKWindowsWide || mode == kModeKWindowsAny; }
+constexpr bool is_line_window(int mode) { return mode == kModeKWindows || mode == kModeKWindowsWide; }
+constexpr int win_cols_for(int mode) {
+  return mode == kModeKWindows ? kWinCols : mode == kModeKWindowsWide ? kWinColsWide : kWinColsAny;
+}
 constexpr int win_span_for(int mode) { return win_cols_for(mode) + 3; }
 // 16-byte pieces covering a window row (and the 3 columns past it) at any alignment
 constexpr int win_pieces_for(int mode) { return (win_span_for(mode) + 30) / 16; }
@@ -125,7 +132,7 @@ constexpr int k3dMaxUnitCols = 160;
 // loads per lane, more units in flight).
 constexpr int threads_for(int mode) {
   return mode == kModeMFlat || mode == kModeMRowsNarrow       ? 128
-         : mode == kMode3dWide || mode == kModeKWindows ? 512
+         : mode == kMode3dWide || is_line_window(mode) ? 512
                                                         : 256;
 }
 constexpr int64_t k3dWideUnits = 2048;
@@ -163,7 +170,11 @@ static_assert(kNarrowUnitCols % 4 == 0 && kNarrowUnitCols >= kMinUnitCols, "narr
 static_assert(kTileRows * (16 * win_pieces_for(kModeKWindows) + 4) + kLdsSlack <= 64 * 1024 &&
                   kTileRows * (16 * win_pieces_for(kModeKWindowsAny) + 4) + kLdsSlack <= 64 * 1024,
               "LDS per workgroup");
-static_assert(win_pieces_for(kModeKWindows) * 16 >= kWinCols + 16,
+// wide windows take more than 64 KB of LDS (gfx950: up to 160 KB per workgroup, raised per kernel)
+constexpr int kWideLdsBytes = kTileRows * (16 * win_pieces_for(kModeKWindowsWide) + 4) + kLdsSlack + 32;
+static_assert(kWideLdsBytes <= 160 * 1024, "LDS per workgroup");
+static_assert(win_pieces_for(kModeKWindows) * 16 >= kWinCols + 16 &&
+                  win_pieces_for(kModeKWindowsWide) * 16 >= kWinColsWide + 16,
               "a window row and the piece past it fit one LDS row");
 
 struct Params {
@@ -423,20 +434,20 @@ __device__ __forceinline__ void stage_flat(uint8_t *__restrict__ lds, const uint
 }
 
 // Window staging for rows that start 128-byte aligned: LDS row r gets bytes
-// [0, kWinCols) of the window row, lines no other unit reads, loaded with
-// POLICY, and, when `extra`, bytes [kWinCols, kWinCols + 16), the first
+// [0, W) of the window row, lines no other unit reads, loaded with
+// POLICY, and, when `extra`, bytes [W, W + 16), the first
 // columns of the next window, loaded first and with the shared policy. Rows
 // past nrows load zeros. `between` runs once every load is issued and before
 // any is waited for.
-template <int NT, int POLICY, typename F>
+template <int NT, int W, int POLICY, typename F>
 __device__ __forceinline__ void stage_window(uint8_t *__restrict__ lds, int trash, __amdgpu_buffer_rsrc_t rsrc,
                                              int64_t ld, int nrows, bool extra, int pitch, F &&between) {
-  constexpr int kPieces = kWinCols / 16;
+  constexpr int kPieces = W / 16;
   constexpr int kMain = kTileRows * kPieces / NT;
   static_assert(kTileRows * kPieces % NT == 0 && NT >= kTileRows, "window staging covers 128 rows");
   const int re = int(threadIdx.x);
   const uint4 x = load16<kSharedLoadPolicy>(
-      rsrc, extra && re < nrows ? uint32_t(re) * uint32_t(ld) + kWinCols : kOutOfRange);
+      rsrc, extra && re < nrows ? uint32_t(re) * uint32_t(ld) + W : kOutOfRange);
   uint4 v[kMain];
 #pragma unroll
   for (int it = 0; it < kMain; ++it) {
@@ -448,7 +459,7 @@ __device__ __forceinline__ void stage_window(uint8_t *__restrict__ lds, int tras
   between();
   // every piece is written (the piece past the window, when there is none, to
   // the trash bytes), see stage_rows_n; LDS rows are 4-byte aligned
-  uint32_t *d = reinterpret_cast<uint32_t *>(lds + (extra && re < kTileRows ? re * pitch + kWinCols : trash));
+  uint32_t *d = reinterpret_cast<uint32_t *>(lds + (extra && re < kTileRows ? re * pitch + W : trash));
   d[0] = x.x;
   d[1] = x.y;
   d[2] = x.z;
@@ -544,7 +555,7 @@ template <int NT, int MODE>
 __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Params &p, int64_t block, int slot,
                                             __amdgpu_buffer_rsrc_t offs, int end_raw, int64_t padded_rows) {
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr bool LINE_ALIGNED = MODE == kModeKWindows;
+  constexpr bool LINE_ALIGNED = is_line_window(MODE);
   constexpr int W = win_cols_for(MODE);
   const int c_lo = slot * W;                            // < cols
   const int64_t c_hi = int64_t(c_lo) + W;
@@ -556,8 +567,8 @@ __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Par
   auto scan = [&] { first = k_slice(end_raw, 0, p.groups, p.cols, 0, 0); };
   if constexpr (LINE_ALIGNED) {
     const uint32_t span = uint32_t((int64_t(nrows - 1) * p.ld + seg + 15) & ~int64_t(15));
-    stage_window<NT, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > W,
-                                        p.pitch, scan);
+    stage_window<NT, W, kWindowLoadPolicy>(lds, p.trash, byte_buffer(row_base, span), p.ld, nrows, seg > W,
+                                           p.pitch, scan);
   } else {
     stage_rows<NT, load_iters_for(MODE), load_policy_for(MODE)>(lds, p.trash, row_base, p.ld, nrows, seg, p.pitch,
                                                                 p.pieces, scan);
@@ -694,6 +705,39 @@ bool sizes_ok(int64_t rows, int64_t cols, int64_t ld, int32_t groups) {
 
 int dispatch(Params &p, int mode, int64_t units, hipStream_t stream);
 
+// Workgroups of the K window kernels (256- and 512-column windows) that the
+// current GPU holds at once: CUs times the workgroups one CU holds (registers,
+// LDS, waves), as the runtime's occupancy query reports them, found once per
+// device. The 512-column kernel's LDS allowance is raised above 64 KB in the
+// same step. 0 when a query fails (the 256-column windows are used then).
+constexpr int kMaxDevices = 64;
+struct Resident {
+  int64_t narrow = 0, wide = 0;
+};
+
+Resident resident_windows() {
+  static std::once_flag once[kMaxDevices];
+  static Resident cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Resident();
+  std::call_once(once[dev], [dev] {
+    const void *narrow = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows>);
+    const void *wide = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide>);
+    int cus = 0, per_cu_narrow = 0, per_cu_wide = 0;
+    const size_t lds_narrow = size_t(kTileRows) * (16 * win_pieces_for(kModeKWindows) + 4) + kLdsSlack + 32;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipFuncSetAttribute(wide, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLdsBytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_narrow, narrow, threads_for(kModeKWindows),
+                                                     lds_narrow) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_wide, wide, threads_for(kModeKWindowsWide),
+                                                     kWideLdsBytes) != hipSuccess)
+      return;   // cache stays {0, 0}
+    cache[dev].narrow = int64_t(cus) * per_cu_narrow;
+    cache[dev].wide = int64_t(cus) * per_cu_wide;
+  });
+  return cache[dev];
+}
+
 int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int64_t ld,
            const int32_t *offs, int32_t groups, uint8_t *out, hipStream_t stream) {
   if (!sizes_ok(rows, cols, ld, groups)) return MX_REARRANGE_ESHAPE;
@@ -738,12 +782,26 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   } else {
     // windows stream their own lines when every row starts on a 128-byte line
     mode = ((reinterpret_cast<uintptr_t>(scales) | uintptr_t(ld)) & 127) == 0 ? kModeKWindows : kModeKWindowsAny;
-    p.unit_cols = mode == kModeKWindows ? win_cols_for(kModeKWindows) : win_cols_for(kModeKWindowsAny);
+    const int64_t row_blocks = (rows + kTileRows - 1) / kTileRows;
+    p.tail_units = int((4 * int64_t(groups) + kTailColsPerUnit - 1) / kTailColsPerUnit);
+    if (mode == kModeKWindows) {
+      // 512-column windows when the 256-column grid needs more than one pass
+      // over the workgroups the GPU holds at once but the 512-column grid fits
+      // in one: the second pass would run a few hundred workgroups on an
+      // otherwise idle chip (measured on (7168, 4096): 14.1 vs 15.3 us; on
+      // shapes with several passes or with room to spare 256 columns are
+      // faster, e.g. (28672, 8192) 82.4 vs 83.4, (4096, 4096) 10.5 vs 11.6)
+      const Resident res = resident_windows();
+      const int64_t units_narrow = row_blocks * ((cols + kWinCols - 1) / kWinCols + p.tail_units);
+      const int64_t units_wide = row_blocks * ((cols + kWinColsWide - 1) / kWinColsWide + p.tail_units);
+      if (res.narrow > 0 && res.wide > 0 && units_narrow > res.narrow && units_wide <= res.wide)
+        mode = kModeKWindowsWide;
+    }
+    p.unit_cols = win_cols_for(mode);
     // units per 128-row block: its input windows, then the tail units
     p.windows = int((cols + p.unit_cols - 1) / p.unit_cols);
-    p.tail_units = int((4 * int64_t(groups) + kTailColsPerUnit - 1) / kTailColsPerUnit);
     p.per_row = p.windows + p.tail_units;
-    units = ((rows + kTileRows - 1) / kTileRows) * p.per_row;
+    units = row_blocks * p.per_row;
   }
   return dispatch(p, mode, units, stream);
 }
@@ -804,6 +862,7 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
                    : mode == kMode3d    ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3d>)
                    : mode == kMode3dWide ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3dWide>)
                    : mode == kModeKWindows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows>)
+                   : mode == kModeKWindowsWide ? reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide>)
                                         : reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsAny>);
   const int threads = threads_for(mode);
   // one workgroup per unit; the grid is a multiple of 8, so a workgroup that

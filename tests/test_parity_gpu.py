@@ -219,6 +219,34 @@ def test_k_window_edges(env, line_aligned):
                  label="k-window-edges-%s" % ("lines" if line_aligned else "any"))
 
 
+def test_k_wide_windows(env):
+    """Shapes whose 256-column window grid needs a small second pass over the workgroups an MI355X holds at
+    once (3 per CU) while the 512-column grid fits in one (2 per CU), so the library takes 512-column windows:
+    random group widths, starts on either side of the 512-column window edges, tiles straddling them, empty
+    groups, short totals, strided rows on 128-byte lines."""
+    import workloads
+
+    rng = np.random.default_rng(36)
+    cases = [
+        (7168, 4096, 4096, "random", 8),
+        (7168, 3600, 3712, "random", 8),
+        (6400, 4096, 4096, "random", 40),
+        (5760, 4608, 4608, "random", 16),
+        (7040, 4000, 4096, "edges", 0),
+        (7168, 4096, 4224, "short", 8),
+    ]
+    for rows, cols, ld, how, G in cases:
+        if how == "random":
+            offs = workloads.random_offsets(rng, cols, G, p_empty=0.2, short_total=False)
+        elif how == "edges":   # starts at, just before and just after multiples of 512, a 1-column group, empty ones
+            offs = np.array([511, 512, 513, 1023, 1024, 1024, 1537, 1538, 2047, 2560, 3071, 3584, 3585, cols],
+                            np.int32)
+        else:
+            offs = workloads.random_offsets(rng, cols, G, p_empty=0.0, short_total=True)
+        A = workloads.random_scales(rng, rows, cols, ld)
+        run_case(env, "K", A, offs, misalign=0, label="k-wide-windows-%dx%d-%s" % (rows, cols, how))
+
+
 @pytest.mark.parametrize("kind", ["M", "K"])
 def test_wide_and_odd_shapes(env, kind):
     rng = np.random.default_rng(33)

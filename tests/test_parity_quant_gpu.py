@@ -72,6 +72,19 @@ def _compare(label, got, want):
                              % (label, bad.size, want.size, bad[0], got[bad[0]], want[bad[0]]))
 
 
+def compare_slices(label, tasks):
+    """Compares GPU codes with the oracle slice by slice, the oracle slices computed in parallel host
+    threads (the C oracle runs without the GIL). tasks: (slice label, want() -> codes, got codes)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    print("  %s: %d slices on %d host threads" % (label, len(tasks), threads), flush=True)
+    with ThreadPoolExecutor(threads) as pool:
+        futures = [(name, pool.submit(want), got) for name, want, got in tasks]
+        for name, fut, got in futures:
+            _compare("%s %s" % (label, name), np.ascontiguousarray(got).reshape(-1), fut.result().reshape(-1))
+
+
 def test_workload_small_bit_exact(env):
     import workloads
 
@@ -81,8 +94,8 @@ def test_workload_small_bit_exact(env):
 
 @pytest.mark.parametrize("name", ["quant_m_groups", "quant_m_groups_skinny"])
 def test_workload_full_size(env, name):
-    """(16640, 5120) and (131072, 1408): every scale byte against the oracle; codes on sampled rows (every
-    group's first and last rows and 256 seeded others), computed by the oracle one row at a time."""
+    """(16640, 5120) and (131072, 1408): every scale byte and every code against the oracle (the codes
+    in slices of 1024 rows, computed in parallel)."""
     gsf, oracle, torch = env
     import workloads
 
@@ -93,15 +106,12 @@ def test_workload_full_size(env, name):
     torch.cuda.synchronize()
     want_s = oracle.rearrange("M", oracle.scales_dim0(w.x), w.offs)
     _compare("full-size scales", s.cpu().numpy(), want_s)
-    rng = np.random.default_rng(50)
-    starts = np.concatenate([[0], w.offs[:-1]])
-    rows = set(rng.integers(0, w.rows, 256).tolist())
-    for a, b in zip(starts, w.offs):
-        if b > a:
-            rows.update([int(a), int(b) - 1])
-    rows = np.array(sorted(rows))
-    want_q, _ = oracle.quantize_dim0(np.ascontiguousarray(w.x[rows]))
-    _compare("full-size sampled codes", q.cpu().numpy()[rows].reshape(-1), want_q.reshape(-1))
+    got = q.cpu().numpy()
+    step = 1024
+    compare_slices("full-size codes", [
+        ("rows %d..%d" % (r, min(r + step, w.rows)),
+         (lambda r=r: oracle.quantize_dim0(np.ascontiguousarray(w.x[r:r + step]))[0]), got[r:r + step])
+        for r in range(0, w.rows, step)])
 
 
 def test_every_scale_and_code(env):
@@ -318,8 +328,8 @@ def test_dim1_workload_small(env):
 
 
 def test_dim1_workload_full_size(env):
-    """(131072, 7168): every scale byte; codes of 48 sampled feature columns (the first and last of each
-    128-feature block among them), computed by the oracle on those columns."""
+    """(131072, 7168): every scale byte and every code against the oracle (the codes in slices of 64
+    feature columns, computed in parallel)."""
     gsf, oracle, torch = env
     import workloads
 
@@ -331,11 +341,13 @@ def test_dim1_workload_full_size(env):
     del x
     want_s = oracle.rearrange("K", oracle.scales_dim1(w.x), w.offs // 32)
     _compare("dim1 full-size scales", s.cpu().numpy(), want_s)
-    rng = np.random.default_rng(60)
-    cols = np.unique(np.concatenate([rng.integers(0, w.K, 40), [0, 127, 128, 4095, 7040, w.K - 1]]))
-    want_q, _ = oracle.quantize_dim1(np.ascontiguousarray(w.x[:, cols]))
-    got = qT[torch.from_numpy(cols).cuda()].cpu().numpy()
-    _compare("dim1 full-size sampled codes", got.reshape(-1), want_q.reshape(-1))
+    got = qT.cpu().numpy()
+    del qT, s
+    step = 64
+    compare_slices("dim1 full-size codes", [
+        ("features %d..%d" % (f, min(f + step, w.K)),
+         (lambda f=f: oracle.quantize_dim1(np.ascontiguousarray(w.x[:, f:f + step]))[0]), got[f:f + step])
+        for f in range(0, w.K, step)])
 
 
 def test_dim1_hand_worked_blocks(env):
@@ -537,8 +549,8 @@ def test_dim1_3d_empty_shapes(env):
 
 
 def test_dim1_3d_full_size_and_bench_launch(env):
-    """The launches bench.py times on the (16, 5120, 8192) weights: every scale byte, and the codes of
-    three whole experts, against the oracle."""
+    """The launches bench.py times on the (16, 5120, 8192) weights: every scale byte and every code
+    against the oracle (the codes in slices of one expert x 1024 features, computed in parallel)."""
     import bench
 
     gsf, oracle, torch = env
@@ -553,9 +565,11 @@ def test_dim1_3d_full_size_and_bench_launch(env):
     scales = np.stack([oracle.scales_dim1(w.w[e]) for e in range(E)])        # (E, N, K/32)
     _compare("quant_3d_e16 scales", out[job.q_pitch: job.q_pitch + oracle.out_bytes_3d(E, N, K // 32)],
              oracle.rearrange_3d(scales))
-    for e in (0, 7, E - 1):
-        want_q, _ = oracle.quantize_dim1(w.w[e])
-        _compare("quant_3d_e16 codes of expert %d" % e, q[e].reshape(-1), want_q.reshape(-1))
+    step = 1024
+    compare_slices("quant_3d_e16 codes", [
+        ("expert %d features %d..%d" % (e, f, min(f + step, N)),
+         (lambda e=e, f=f: oracle.quantize_dim1(np.ascontiguousarray(w.w[e][:, f:f + step]))[0]), q[e, f:f + step])
+        for e in range(E) for f in range(0, N, step)])
 
 
 def test_dim0_cast_of_stacked_experts_gives_the_3d_layout(env):

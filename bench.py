@@ -65,11 +65,12 @@ SECONDARY = ("m_groups_skinny", "k_groups", "m_groups_experts", "m_groups_tiny")
 # realistic-shapes table).
 PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.47}
 # kernel instantiation per staging mode: 0 = M flat strips, 1 = M row segments,
-# 3 = M narrow row segments, 2 = K column windows of rows on 128-byte lines (6: rows at
-# any other alignment), 4 = per-expert row segments, 5 = the same with 512 threads (grids
-# of more than 2048 units)
+# 3 = M narrow row segments, 2 = K column windows of rows on 128-byte lines (7: the same with
+# 512-column windows, taken on MI355X for the (7168, 4096) shape; 6: rows at any other
+# alignment), 4 = per-expert row segments, 5 = the same with 512 threads (grids of more than
+# 2048 units)
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3>", "m_groups_skinny": "rearrange_kernel<0>",
-                "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<2>",
+                "m_groups_experts": "rearrange_kernel<3>", "k_groups": "rearrange_kernel<7>",
                 "k_groups_large": "rearrange_kernel<2>", "experts_3d_small": "rearrange_kernel<4>",
                 "experts_3d_e16": "rearrange_kernel<4>", "experts_3d_e64": "rearrange_kernel<5>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",

@@ -135,3 +135,45 @@ def test_pad_unpad_and_inverse(env):
         inv = gsf.mx_block_unrearrange_M_groups if kind == "M" else gsf.mx_block_unrearrange_K_groups
         out = torch.empty((f.rows, f.cols), dtype=torch.uint8, device="cuda")
         check_graph(torch, "inverse " + name, lambda: inv(blocked, f.rows, f.cols, o, out=out), [out])
+
+
+FIRST_CALL_CAPTURED = r"""
+import numpy as np, torch
+import group_scale_factor_amd as gsf
+rng = np.random.default_rng(5)
+rows, cols = 7168, 4096          # a shape whose grid takes the 512-column windows on MI355X
+scales = torch.from_numpy(rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)).cuda()
+offs = torch.from_numpy(np.array([1, 700, 701, 2049, 2050, 3000, 4001, 4096], np.int32)).cuda()
+out = torch.empty(gsf.mx_rearrange_K_groups_out_bytes(rows, cols, 8), dtype=torch.uint8, device="cuda")
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        gsf.mx_block_rearrange_K_groups(scales, offs, out=out)   # the process's first K-groups call
+torch.cuda.current_stream().wait_stream(s)
+out.fill_(0x5A)
+g.replay()
+torch.cuda.synchronize()
+got = out.clone()
+out.fill_(0xA5)
+gsf.mx_block_rearrange_K_groups(scales, offs, out=out)
+torch.cuda.synchronize()
+assert torch.equal(got, out), "captured first call differs from the eager call"
+print("first call captured: ok")
+"""
+
+
+def test_first_k_call_inside_a_capture():
+    """The library's first K-groups call in a process (which asks the runtime, once per device, how many
+    workgroups of each window kernel fit and raises the 512-column kernel's LDS allowance) may itself be
+    inside a graph capture: the captured launch replays to the eager result. Run in a fresh process of its
+    own, since this test process has made K-groups calls already."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("case graph: first K-groups call of a fresh process inside a capture", flush=True)
+    res = subprocess.run([sys.executable, "-c", FIRST_CALL_CAPTURED], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stdout[-2000:] + res.stderr[-4000:]

@@ -16,17 +16,17 @@ Timing protocol (the same for every workload):
     launch never finds its input in a cache left warm by a recent launch:
     step i uses copy i mod copies, and between two uses of one copy the
     other copies move at least 1 GiB through the caches.
-  * The K timed launches (steps W .. W+K-1) are captured in a HIP graph (the
+  * The K timed launches (steps W .. W+K-1) are captured in one HIP graph (the
     pages' own K-groups benchmark timed CUDA graphs of 1000 launches), which
-    is replayed once beforehand (one-time costs). The warm-up then runs
-    max(W, copies) launches, steps W - max(W, copies) .. W-1: every copy is
-    used once, and the copy each timed launch uses was last used a whole
-    rotation earlier — the state of a long run's steady rotation, in which
-    nothing of it is cached but its pages are mapped (a warm-up of W launches
-    on other copies only, or with a cache flush before the timed launches,
-    measured 3-15% slower per launch at K = 20 than at K = 2000; this one
-    within 1-9%, the rest being a fixed cost of a few microseconds at the
-    start of the timed region).
+    is replayed once beforehand (one-time costs). The warm-up then replays a
+    graph of one rotation pass, max(W, copies) launches, steps
+    W - max(W, copies) .. W-1, back to back for at least --warm-ms of GPU time
+    (20 ms): every copy is used, and the copy each timed launch uses was last
+    used a whole rotation earlier — the state of a long run's steady rotation,
+    in which nothing of it is cached but its pages are mapped and the clocks
+    have settled under load (a warm-up of W launches on other copies only, or
+    with a cache flush before the timed launches, measured 3-15% slower per
+    launch at K = 20 than at K = 2000).
   * After a synchronisation a spin kernel holds the GPU while the host
     enqueues the timed replays behind it; HIP events on the launch stream
     bracket the K launches only, so host enqueue time stays outside the
@@ -278,7 +278,7 @@ class Spinner:
         self.torch.cuda._sleep(int(us / self.us_per_cycle))
 
 
-def timed_launches(job, K, W, spinner, eager=False):
+def timed_launches(job, K, W, spinner, eager=False, warm_ms=20.0):
     """Runs the warm-up and the K timed launches of `job` by the protocol of the module docstring.
 
     Returns (event seconds for the K launches, host wall seconds between the synchronisations around
@@ -287,8 +287,9 @@ def timed_launches(job, K, W, spinner, eager=False):
 
     torch = job.torch
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # warm-up: every copy once, ending right before the first timed step (step W)
-    warm_steps = range(W - max(W, job.copies), W)
+    # one rotation pass: every copy once, ending right before the first timed step (step W)
+    first_warm = W - max(W, job.copies)
+    warm_steps = range(first_warm, W)
     if eager:
         for i in warm_steps:
             job.step(i)
@@ -301,30 +302,35 @@ def timed_launches(job, K, W, spinner, eager=False):
         ev1.record()
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / 1e3, _time.perf_counter() - t0, None, len(warm_steps)
-    chunk = min(K, job.copies)
-    full, rem = divmod(K, chunk)
-    g = capture(job, W, chunk)
-    g_rem = capture(job, W + full * chunk, rem) if rem else None
-    # one replay of each graph first (one-time costs), timing the host's enqueue of it
+    # one graph holds all K timed launches: a replay boundary inside the timed region would add a gap
+    # (about 8 us each under the tracer, between graphs of a few launches)
+    g = capture(job, W, K)
+    g_warm = capture(job, first_warm, len(warm_steps))
+    # one replay of each first (one-time costs), timing the host's enqueue of the timed graph and the
+    # GPU time of a rotation pass
     t = _time.perf_counter()
     g.replay()
     enqueue_s = _time.perf_counter() - t
-    if g_rem is not None:
-        g_rem.replay()
-    for i in warm_steps:
-        job.step(i)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    g_warm.replay()
+    w1.record()
+    torch.cuda.synchronize()
+    # rotation passes back to back for at least warm_ms of GPU time (clocks settled under load; the
+    # first short timed region of a process measured 1-2% slower without it), the last one ending
+    # right before step W
+    reps = max(1, math.ceil(warm_ms / max(w0.elapsed_time(w1), 1e-3)))
+    for _ in range(reps):
+        g_warm.replay()
     torch.cuda.synchronize()
     t0 = _time.perf_counter()
-    # hold the GPU while the host enqueues the replays behind the spin kernel
+    # hold the GPU while the host enqueues the replay behind the spin kernel
     spinner.hold(max(300.0, 4e6 * enqueue_s))
     ev0.record()
-    for _ in range(full):
-        g.replay()
-    if g_rem is not None:
-        g_rem.replay()
+    g.replay()
     ev1.record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / 1e3, _time.perf_counter() - t0, enqueue_s, len(warm_steps)
+    return ev0.elapsed_time(ev1) / 1e3, _time.perf_counter() - t0, enqueue_s, (reps + 1) * len(warm_steps)
 
 
 def launch_floor_us(spinner, count=500):
@@ -670,7 +676,8 @@ def measure(name, K, W, args, spinner, floor_us):
     import torch
 
     job = Job(name, rotate_bytes=args.rotate_mib << 20)
-    gpu_s, wall, enqueue_s, warm_launches = timed_launches(job, K, W, spinner, eager=args.eager)
+    gpu_s, wall, enqueue_s, warm_launches = timed_launches(job, K, W, spinner, eager=args.eager,
+                                                           warm_ms=args.warm_ms)
     us_per_launch = gpu_s / K * 1e6
     achieved = job.bytes_per_step / (gpu_s / K) / 1e9
     warm = None if args.eager or args.no_warm else warm_figure(job, K, spinner)
@@ -718,6 +725,8 @@ def main():
     ap.add_argument("--secondary-min-steps", type=int, default=200,
                     help="launches timed for each secondary workload: max(--steps, this)")
     ap.add_argument("--rotate-mib", type=int, default=1024, help="bytes of input+output rotated over")
+    ap.add_argument("--warm-ms", type=float, default=20.0,
+                    help="GPU time of the warm-up rotation passes before each timed region (at least one pass)")
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")

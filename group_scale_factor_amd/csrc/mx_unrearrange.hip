@@ -150,6 +150,29 @@ struct KGroups<false> {
   __device__ __forceinline__ int width_through(int g) const { return cws[g]; }
 };
 
+// End offset of group `lane` for the first 64 groups (0 past the last one),
+// loaded through a buffer resource: the range check, not a branch, keeps the
+// load unconditional, so it can be issued ahead of the tile loads and waited
+// for alone.
+__device__ __forceinline__ int first_ends(const int32_t *offs, int groups) {
+  const __amdgpu_buffer_rsrc_t r = byte_buffer(offs, 4 * uint32_t(min(groups, kWave)));
+  return __builtin_amdgcn_raw_buffer_load_b32(r, 4 * int(threadIdx.x & (kWave - 1)), 0, 0);
+}
+
+// The M-groups table of at most 64 groups from end offsets already loaded
+// (raw: lane g's end offset): clamped non-decreasing ends and padded
+// cumulative ends, as MGroups<true>::init forms them.
+__device__ __forceinline__ void init_loaded(MGroups<true> &grp, int raw, int groups, int rows) {
+  const int g = int(threadIdx.x & (kWave - 1));
+  grp.groups = groups;
+  int e = g < groups ? min(max(raw, 0), rows) : 0;
+  e = wave_inclusive_max(e);
+  const int prev = wave_shift_up(e, 0);
+  const int padded = g < groups ? (e - prev + kTileRows - 1) / kTileRows * kTileRows : 0;
+  grp.e = e;
+  grp.pend = wave_inclusive_sum(padded);
+}
+
 // A row segment of ncols bytes at p split by alignment: head_bytes single bytes,
 // head_dwords 4-byte aligned dwords, `chunks` 16-byte aligned chunks from
 // chunk0, tail_dwords dwords, then single bytes from tail_bytes0 to ncols.
@@ -336,14 +359,32 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
   const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
                                              : int64_t(blockIdx.x);
   if (!KGROUPS) {
-    MGroups<SMALL> grp;
-    grp.init(p.offs, p.groups, p.rows, group_lds);
-    if (u >= p.units) return;
     const int64_t ob = u / p.per_row;                  // output row block of the blocked layout
     const int cc = int(u - ob * p.per_row);
     const int c0 = cc * GM::cols;
     const int ncols = min(GM::cols, p.cols - c0);
     const int tile_cols = (ncols + 3) >> 2;
+    // The unit's tiles sit at a place fixed by its row block and column
+    // window, whatever the groups are: their loads go out first and the group
+    // table is scanned while they are in flight. (Units that turn out to lie
+    // past the last group load tiles of the zero tail they never use; nothing
+    // past the blocked input is read.)
+    const int64_t src_off = ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows;
+    const int64_t avail = u < p.units ? clamp64(p.blocked_bytes - src_off, 0, int64_t(tile_cols) * 512) : 0;
+    uint4 v[GM::loads];
+    MGroups<SMALL> grp;
+    if constexpr (SMALL) {
+      // the end offsets go out before the tiles, so the scan waits for them alone
+      const int raw = first_ends(p.offs, p.groups);
+      issue_loads<GM>(v, p.blocked + (avail > 0 ? src_off : 0), tile_cols, uint32_t(avail));
+      __builtin_amdgcn_sched_barrier(0);
+      init_loaded(grp, raw, p.groups, p.rows);
+    } else {
+      // (more than 64 groups: the table is scanned into LDS first)
+      grp.init(p.offs, p.groups, p.rows, group_lds);
+      issue_loads<GM>(v, p.blocked + (avail > 0 ? src_off : 0), tile_cols, uint32_t(avail));
+    }
+    if (u >= p.units) return;
     const int g = grp.count_pends_le(ob * kTileRows);
     if (g < p.groups) {
       const int start = g ? grp.end(g - 1) : 0;
@@ -353,9 +394,6 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
       const int nrows = int(min(int64_t(kTileRows), int64_t(grp.end(g) - start) - k * kTileRows));
       // (a correct table always passes the second test: the rows lie inside the output)
       if (nrows <= 0 || ncols <= 0 || !fits(row0, nrows, p.rows)) return;
-      uint4 v[GM::loads];
-      issue_loads<GM>(v, p.blocked + ob * kTileRows * int64_t(p.padded_cols) + int64_t(c0) * kTileRows, tile_cols,
-                  uint32_t(tile_cols) * 512u);
       unit_out<true>(strip, v, 0, tile_cols, nrows, ncols, p.out + int64_t(row0) * p.ld + c0, p.ld);
     } else {
       // spare units: zero the rows after the last group

@@ -34,6 +34,12 @@ Timing protocol (the same for every workload):
     one event interval; `wall_ms` is the host time between the two
     synchronisations around it (spin kernel included).
 
+Two secondary figures come from the same run, outside that interval: `warm`
+(launches back to back on one input/output copy, cache-resident when it fits)
+and `cold` (eager launches, each after an in-place update and a read of a
+512 MiB buffer that evict the MALL and the L2s, each between its own pair of
+events: median, p10 and p90 per launch, dispatch included).
+
 Bytes per step follow the pages' convention: every input scale byte read once
 plus the whole output allocation written once.
 
@@ -391,6 +397,47 @@ def warm_figure(job, K, spinner):
             "launches": n_warm, "note": "one input/output copy reused: cache-resident when it fits, not an HBM figure"}
 
 
+# Bytes of the buffer updated in place and read before each cold launch: more than the 256 MB MALL
+# plus the eight 4 MB L2s, so nothing of the launch's input or output is left in a cache.
+FLUSH_BYTES = 512 << 20
+# Cold launches per workload (fewer for workloads that move more than the MALL holds, whose launches
+# are long)
+COLD_LAUNCHES, COLD_LAUNCHES_LARGE = 200, 50
+
+
+def cold_figure(job, n, flush):
+    """Secondary figure: per-launch times with the caches flushed before every launch.
+
+    Before each launch `flush` (FLUSH_BYTES) is updated in place and then read once more: the update
+    evicts the MALL and the L2s, and the read leaves them holding clean lines, so that the launch pays
+    for no write-back of the flush's own data (measured after the update alone, the (28672, 8192)
+    K-groups kernel took 105.7 us instead of 88.0). Each launch is eager, between its own pair of HIP
+    events, so a pair holds one launch's dispatch and run, and nothing else. Reports the median, p10
+    and p90 over the n launches; a rocprofv3 kernel trace of the same run gives the kernel's own
+    durations."""
+    import numpy as np
+
+    torch = job.torch
+    words = flush.view(torch.int64)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        flush.add_(1)
+        torch.amax(words)
+        a.record()
+        job.step(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    med, p10, p90 = (float(np.percentile(us, q)) for q in (50, 10, 90))
+    return {"us_median": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
+            "GBps_median": round(job.bytes_per_step / med / 1e3, 2),
+            "frac_median": round(job.bytes_per_step / med / 1e3 / HBM_PEAK_GBPS, 4),
+            "launches": n, "flush_bytes": FLUSH_BYTES,
+            "note": "MALL and L2s flushed (512 MiB written, then read) before each launch; one event pair per "
+                    "eager launch (dispatch included)"}
+
+
 def copy_calibration(args):
     """K plain device-to-device copies of the workload's input size (reads N, writes N bytes each)."""
     import torch
@@ -671,8 +718,9 @@ def config_of(w, job, args):
     }
 
 
-def measure(name, K, W, args, spinner, floor_us):
-    """Times K launches of workload `name` (after W warm-up launches); returns (result fields, kind)."""
+def measure(name, K, W, args, spinner, floor_us, flush=None):
+    """Times K launches of workload `name` (after W warm-up launches); returns (result fields, kind).
+    With a flush buffer it also takes the cold figure."""
     import torch
 
     job = Job(name, rotate_bytes=args.rotate_mib << 20)
@@ -681,6 +729,9 @@ def measure(name, K, W, args, spinner, floor_us):
     us_per_launch = gpu_s / K * 1e6
     achieved = job.bytes_per_step / (gpu_s / K) / 1e9
     warm = None if args.eager or args.no_warm else warm_figure(job, K, spinner)
+    cold = None
+    if flush is not None:
+        cold = cold_figure(job, COLD_LAUNCHES_LARGE if job.bytes_per_step > (256 << 20) else COLD_LAUNCHES, flush)
     ideal_us = job.bytes_per_step / HBM_PEAK_GBPS / 1e3
     pages_us = PAGES_US.get(name)
     res = {
@@ -707,6 +758,7 @@ def measure(name, K, W, args, spinner, floor_us):
             "frac_ceiling": round(ideal_us / (floor_us + ideal_us), 4) if floor_us is not None else None,
         },
         "warm": warm,
+        "cold": cold,
     }
     kind = job.kind
     del job
@@ -731,8 +783,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
-                    help="skip the secondary cache-resident timing and the launch floor (profiling runs: only "
-                         "the timed launches)")
+                    help="skip the secondary cache-resident timing, the cold launches and the launch floor "
+                         "(profiling runs: only the timed launches)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the secondary figure of launches with the caches flushed before each one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's plain device copy of the workload's input size instead "
                          "(reference kernel of known traffic for the HBM byte counters)")
@@ -768,17 +822,21 @@ def main():
     spinner = Spinner()
     # the fixed cost of one graph-replayed launch (outside every timed region; skipped when profiling)
     floor = launch_floor_us(spinner) if not args.eager and not args.no_warm else None
-    head, kind = measure(args.workload, K, W, args, spinner, floor)
+    # the buffer rewritten before each cold launch (outside every timed region of the main figure)
+    flush = (torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+             if not args.no_warm and not args.no_cold else None)
+    head, kind = measure(args.workload, K, W, args, spinner, floor, flush)
     configs = {}
     for name in [n for n in args.secondary.split(",") if n and n != args.workload]:
-        r, _ = measure(name, max(K, args.secondary_min_steps), W, args, spinner, floor)
+        r, _ = measure(name, max(K, args.secondary_min_steps), W, args, spinner, floor, flush)
         cfg = r["config"]
         configs[name] = {"us_per_launch": r["us_per_launch"], "value": r["value"], "unit": "GB/s",
                          "frac": r["roofline"]["frac"], "frac_ceiling": r["roofline"]["frac_ceiling"],
                          "traffic": r["roofline"]["traffic"], "kernel": r["roofline"]["kernel"],
                          "steps": r["steps"], "warmup": r["warmup"], "vs_baseline": r["vs_baseline"],
                          "scales_shape": cfg.get("scales_shape"), "num_groups": cfg["num_groups"],
-                         "bytes_per_step": cfg["bytes_per_step"], "rotating_copies": cfg["rotating_copies"]}
+                         "bytes_per_step": cfg["bytes_per_step"], "rotating_copies": cfg["rotating_copies"],
+                         "cold": r["cold"]}
     res = {
         "metric": METRIC,
         "value": head["value"],
@@ -799,6 +857,7 @@ def main():
         "roofline": head["roofline"],
         "configs": configs,
         "warm": head["warm"],
+        "cold": head["cold"],
         "first_enqueue_us": head["first_enqueue_us"],
         "cpu_baseline": None,
     }

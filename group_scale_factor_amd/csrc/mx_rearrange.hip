@@ -21,8 +21,9 @@
 //     128 rows x a column chunk of one group, i.e. a run of whole output tiles
 //     that are contiguous in the output. K groups: 128 rows x a 256-column
 //     window of the input (two 128-byte lines per row when rows are so
-//     aligned), writing the tiles of every group whose tiles start in the
-//     window — one contiguous output run per such group. A K unit's input
+//     aligned; 512 columns where that makes the grid fit the workgroups the
+//     GPU holds at once), writing the tiles of every group whose tiles start
+//     in the window — one contiguous output run per such group. A K unit's input
 //     thus does not depend on the offsets: its loads are issued before the
 //     offsets are scanned, and the scan runs while they are in flight.
 //   * Group lookup: every wave loads the end offsets, one group per lane,

@@ -98,6 +98,13 @@ constexpr int kMRowsLoadPolicy = 2;
 constexpr int kWindowLoadPolicy = 2;
 constexpr int kSharedLoadPolicy = 0;
 constexpr int k3dLoadPolicy = 2;
+// Output stores are non-temporal. An M- or K-groups launch that moves more
+// bytes than the 256 MB MALL holds also sets sc1 on them (buffer instruction
+// cache policy: bit 1 nt, bit 4 sc1), in kernels built for it: measured 9%
+// faster on M groups of 336 MB, 0.5-2.5% on K shapes of 336 to 941 MB;
+// within 1% at 168-235 MB and 4-11% slower on smaller launches.
+constexpr int64_t kWriteThroughBytes = int64_t(256) << 20;
+constexpr int kStoreNtSc1 = 2 | 16;
 
 // Staging modes; each is its own kernel instantiation.
 enum Mode : int {
@@ -199,6 +206,7 @@ struct Params {
   int64_t row_blocks;     // per-expert matrices: 128-row blocks per expert
   int windows;            // K: column windows per row block (the first units of each)
   int tail_units;         // K: units per row block that zero-fill its slice of the tail
+  int write_through;      // M and K launches of more than kWriteThroughBytes: stores also carry sc1
 };
 
 __device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
@@ -485,13 +493,17 @@ __device__ __forceinline__ void stage_window(uint8_t *__restrict__ lds, int tras
 // row_off(r) = first + r*row_step (FLAT) or first + r*row_step + (addr + r*ld)
 // mod 16 (per-row staging, where `first` is the unit's column in the staged
 // segment).
-// Rows >= nrows and columns >= ncols are written as zero.
-template <int NT, bool FLAT, bool ALIGNED>
+// Rows >= nrows and columns >= ncols are written as zero. With WT the stores
+// go through a buffer resource over the run and carry sc1 as well.
+template <int NT, bool FLAT, bool ALIGNED, bool WT>
 __device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ lds, uint8_t *__restrict__ dst,
                                            int tile_cols, int nrows, int ncols, int first, int row_step,
                                            uintptr_t addr, int64_t ld) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const uint32_t *w32 = reinterpret_cast<const uint32_t *>(lds);
   const int n16 = tile_cols * 32;
+  __amdgpu_buffer_rsrc_t orsrc;
+  if constexpr (WT) orsrc = byte_buffer(dst, uint32_t(n16) * 16u);
   for (int v = threadIdx.x; v < n16; v += NT) {
     const int tc = v >> 5;
     const int i = v & 31;
@@ -514,13 +526,16 @@ __device__ __forceinline__ void emit_tiles(const uint8_t *__restrict__ lds, uint
       }
       w[q] = x;
     }
-    store16(dst + 16 * int64_t(v), w[0], w[1], w[2], w[3]);
+    if constexpr (WT)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, orsrc, 16 * v, 0, kStoreNtSc1);
+    else
+      store16(dst + 16 * int64_t(v), w[0], w[1], w[2], w[3]);
   }
 }
 
 // Stages one unit of `nrows` rows x `ncols` source columns starting at
 // row_base (row stride ld) and writes its tile_cols tiles at dst.
-template <int MODE>
+template <int MODE, bool WT>
 __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Params &p, const uint8_t *row_base,
                                           int nrows, int ncols, int tile_cols, uint8_t *dst) {
   constexpr int NT = threads_for(MODE);
@@ -539,9 +554,9 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
   const int first = FLAT ? int(a & 15) : 0;
   const int step = FLAT ? ncols : p.pitch;
   if (aligned)
-    emit_tiles<NT, FLAT, true>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
+    emit_tiles<NT, FLAT, true, WT>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
   else
-    emit_tiles<NT, FLAT, false>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
+    emit_tiles<NT, FLAT, false, WT>(lds, dst, tile_cols, nrows, ncols, first, step, a, p.ld);
 }
 
 // K groups: the unit of 128-row block `block` and input window `slot` (columns
@@ -552,7 +567,7 @@ __device__ __forceinline__ void copy_unit(uint8_t *__restrict__ lds, const Param
 // group's place: group g's blocked matrix starts at byte padded_rows * (padded
 // widths before g), its row block `block` 128 * width_g bytes further per
 // block, tile k 512*k on.
-template <int NT, int MODE>
+template <int NT, int MODE, bool WT>
 __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Params &p, int64_t block, int slot,
                                             __amdgpu_buffer_rsrc_t offs, int end_raw, int64_t padded_rows) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -598,9 +613,9 @@ __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Par
       if (k_hi <= k_lo || !fits(dst_off, int64_t(512) * (k_hi - k_lo), p.out_bytes)) continue;
       uint8_t *dst = p.out + dst_off;
       if (aligned && ((col0 - c_lo) & 3) == 0)
-        emit_tiles<NT, false, true>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
+        emit_tiles<NT, false, true, WT>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
       else
-        emit_tiles<NT, false, false>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
+        emit_tiles<NT, false, false, WT>(lds, dst, k_hi - k_lo, nrows, ge - col0, col0 - c_lo, p.pitch, a, p.ld);
     }
     carry_end = lane_value(sl.end, kWave - 1);
     carry_width = lane_value(sl.before + sl.width, kWave - 1);
@@ -614,7 +629,7 @@ __device__ __forceinline__ void window_unit(uint8_t *__restrict__ lds, const Par
 // next one on the CU loads while those stores drain.
 // ---------------------------------------------------------------------------
 
-template <int MODE>
+template <int MODE, bool WT>
 __global__ __launch_bounds__(threads_for(MODE)) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu)))
 void rearrange_kernel(Params p) {
   constexpr int NT = threads_for(MODE);
@@ -643,7 +658,7 @@ void rearrange_kernel(Params p) {
       const int tile_cols = min(p.unit_cols, p.padded_cols - c0) >> 2;
       uint8_t *dst = p.out + block * int64_t(kTileRows) * p.padded_cols + int64_t(c0) * kTileRows;
       if (nrows > 0 && ncols > 0)
-        copy_unit<MODE>(lds, p, p.src + e * p.expert_stride + int64_t(kTileRows) * rb * p.ld + c0, nrows, ncols,
+        copy_unit<MODE, WT>(lds, p, p.src + e * p.expert_stride + int64_t(kTileRows) * rb * p.ld + c0, nrows, ncols,
                         tile_cols, dst);
     } else if constexpr (!KGROUPS) {
       const GroupHit h = find_group(p.offs, p.groups, p.rows, int(block));
@@ -659,7 +674,7 @@ void rearrange_kernel(Params p) {
         uint8_t *dst = p.out + block * row_block_bytes + int64_t(c0) * kTileRows;
         // the last two conditions, too, hold for every unit of a correct scan
         if (nrows > 0 && ncols > 0 && row0 >= 0 && (block + 1) * row_block_bytes <= p.out_bytes)
-          copy_unit<MODE>(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst);
+          copy_unit<MODE, WT>(lds, p, p.src + int64_t(row0) * p.ld + c0, nrows, ncols, tile_cols, dst);
       } else {
         const int64_t nblocks = p.units / p.per_row;
         const int64_t tail_units = int64_t(p.per_row) * (nblocks - h.first_unit);
@@ -675,7 +690,7 @@ void rearrange_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t padded_rows = int64_t(((p.rows + kTileRows - 1) / kTileRows)) * kTileRows;
       if (slot < p.windows) {
-        window_unit<NT, MODE>(lds, p, block, slot, offs, end_raw, padded_rows);
+        window_unit<NT, MODE, WT>(lds, p, block, slot, offs, end_raw, padded_rows);
       } else {
         // tail: round_up(rows,128) * (cols + 4G - padded total) zero bytes, a
         // 128 * (cols + 4G - padded total) slice per 128-row block
@@ -722,8 +737,8 @@ Resident resident_windows() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Resident();
   std::call_once(once[dev], [dev] {
-    const void *narrow = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows>);
-    const void *wide = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide>);
+    const void *narrow = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows, false>);
+    const void *wide = reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide, false>);
     int cus = 0, per_cu_narrow = 0, per_cu_wide = 0;
     const size_t lds_narrow = size_t(kTileRows) * (16 * win_pieces_for(kModeKWindows) + 4) + kLdsSlack + 32;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -761,6 +776,7 @@ int launch(bool kgroups, const uint8_t *scales, int64_t rows, int64_t cols, int6
   p.cols = int(cols);
   p.groups = groups;
   p.padded_cols = int(round_up(cols, 4));
+  p.write_through = rows * cols + out_bytes > kWriteThroughBytes;
   int mode;
   int64_t units;
   if (!kgroups) {
@@ -842,6 +858,31 @@ int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
   return dispatch(p, units > k3dWideUnits ? kMode3dWide : kMode3d, units, stream);
 }
 
+// The kernel of a mode. The sc1 stores are built only for the modes that run
+// launches past the MALL size: M row segments and flat strips, K windows of
+// line-aligned rows (256 columns) and of other rows. Narrow M units and
+// 512-column K windows are chosen only for grids that fit the chip at once
+// (far smaller launches), and per-expert launches measured the same with and
+// without sc1 (336 MB: 57.4 us).
+template <int MODE>
+const void *kernel_of(bool wt) {
+  return wt ? reinterpret_cast<const void *>(&rearrange_kernel<MODE, true>)
+            : reinterpret_cast<const void *>(&rearrange_kernel<MODE, false>);
+}
+
+const void *kernel_for(int mode, bool wt) {
+  switch (mode) {
+    case kModeMFlat: return kernel_of<kModeMFlat>(wt);
+    case kModeMRows: return kernel_of<kModeMRows>(wt);
+    case kModeKWindows: return kernel_of<kModeKWindows>(wt);
+    case kModeKWindowsAny: return kernel_of<kModeKWindowsAny>(wt);
+    case kModeMRowsNarrow: return reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow, false>);
+    case kMode3d: return reinterpret_cast<const void *>(&rearrange_kernel<kMode3d, false>);
+    case kMode3dWide: return reinterpret_cast<const void *>(&rearrange_kernel<kMode3dWide, false>);
+    default: return reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide, false>);
+  }
+}
+
 int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
   // widest row segment of a unit; K windows always get room for a whole
   // window row and the piece past it
@@ -857,14 +898,7 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
   p.trash = int(lds_bytes);
   lds_bytes += 16;
 
-  const void *fn = mode == kModeMFlat   ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMFlat>)
-                   : mode == kModeMRows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRows>)
-                   : mode == kModeMRowsNarrow ? reinterpret_cast<const void *>(&rearrange_kernel<kModeMRowsNarrow>)
-                   : mode == kMode3d    ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3d>)
-                   : mode == kMode3dWide ? reinterpret_cast<const void *>(&rearrange_kernel<kMode3dWide>)
-                   : mode == kModeKWindows ? reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindows>)
-                   : mode == kModeKWindowsWide ? reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsWide>)
-                                        : reinterpret_cast<const void *>(&rearrange_kernel<kModeKWindowsAny>);
+  const void *fn = kernel_for(mode, p.write_through != 0);
   const int threads = threads_for(mode);
   // one workgroup per unit; the grid is a multiple of 8, so a workgroup that
   // loops (only past kMaxGrid units) stays on its XCD

@@ -300,6 +300,28 @@ def test_invalid_offsets_are_clamped(env, kind):
 # determinism, streams, errors
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# launches that move more than 256 MiB run kernels whose stores also carry sc1
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,rows,cols", [
+    ("M", 1 << 20, 160),     # row segments, 336 MB per launch
+    ("M", 6291456, 44),      # flat strips of packed 44-byte rows, 554 MB
+    ("K", 20480, 8196),      # windows of rows that do not start on 128-byte lines, 336 MB
+])
+def test_launches_past_the_mall_size(env, kind, rows, cols):
+    import workloads
+
+    gsf, oracle, torch = env
+    G = 8
+    rng = np.random.default_rng(41)
+    offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25)
+    size = gsf.mx_rearrange_M_groups_out_bytes if kind == "M" else gsf.mx_rearrange_K_groups_out_bytes
+    assert rows * cols + size(rows, cols, G) > (256 << 20), "the case must take the kernels built for large launches"
+    scales = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    run_case(env, kind, scales, offs, label="past the MALL size")
+
+
 def test_repeat_is_deterministic(env):
     import workloads
 

@@ -60,9 +60,11 @@ def check_device_code():
 
 
 def build(verbose=False):
-    """Compile libmxrearrange.so next to this file. Always recompiles."""
+    """Compile libmxrearrange.so next to this file. Always recompiles; the result replaces the library in
+    one step from a file of this process's own, so concurrent builds neither collide nor expose a
+    half-written library."""
     check_device_code()
-    tmp = LIBRARY + ".tmp"
+    tmp = "%s.tmp%d" % (LIBRARY, os.getpid())
     cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -26,13 +26,15 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 
 def compile_library(src, dst, verbose=False):
-    """Compile one oracle source file into a shared library (plain gcc -O2)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-pthread", "-o", dst + ".tmp", src,
-           "-lm"]
+    """Compile one oracle source file into a shared library (plain gcc -O2). The compiler writes a file of
+    this process's own and it replaces `dst` in one step, so processes building at once (parallel test
+    workers) neither collide nor load a half-written library."""
+    tmp = "%s.tmp%d" % (dst, os.getpid())
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-pthread", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(dst + ".tmp", dst)
+    os.replace(tmp, dst)
 
 
 def build(verbose=False):

@@ -42,7 +42,9 @@
 //     tile — from LDS. When the source is not 4-byte aligned each word is
 //     assembled from two aligned LDS words with v_alignbyte_b32. Bytes past
 //     the group's rows or columns are masked to zero.
-//   * Store: consecutive lanes write consecutive 16 bytes (global_store_dwordx4).
+//   * Store: consecutive lanes write consecutive 16 bytes, non-temporal
+//     (global_store_dwordx4 nt; buffer stores with sc1 as well for M and K
+//     launches that move more bytes than the MALL holds).
 //   * The whole output allocation is written exactly once by the same launch:
 //     work units past the last group's data zero-fill the tail, so the output
 //     needs no memset.
@@ -106,7 +108,8 @@ constexpr int k3dLoadPolicy = 2;
 constexpr int64_t kWriteThroughBytes = int64_t(256) << 20;
 constexpr int kStoreNtSc1 = 2 | 16;
 
-// Staging modes; each is its own kernel instantiation.
+// Staging modes; each is its own kernel instantiation (two for the modes that
+// also have the sc1-store variant, kernel_for()).
 enum Mode : int {
   kModeMFlat = 0,   // M groups, packed rows of <= 60 bytes, one contiguous range per 128-row strip
   kModeMRows = 1,   // M groups, one row segment at a time

@@ -74,12 +74,16 @@ PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.4
 # 3 = M narrow row segments, 2 = K column windows of rows on 128-byte lines (7: the same with
 # 512-column windows, taken on MI355X for the (7168, 4096) shape; 6: rows at any other
 # alignment), 4 = per-expert row segments, 5 = the same with 512 threads (grids of more than
-# 2048 units); the second argument is true for the M and K kernels whose stores also carry sc1
-# (launches that move more than 256 MiB)
-KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3, false>", "m_groups_skinny": "rearrange_kernel<0, false>",
-                "m_groups_experts": "rearrange_kernel<3, false>", "k_groups": "rearrange_kernel<7, false>",
-                "k_groups_large": "rearrange_kernel<2, true>", "experts_3d_small": "rearrange_kernel<4, false>",
-                "experts_3d_e16": "rearrange_kernel<4, false>", "experts_3d_e64": "rearrange_kernel<5, false>",
+# 2048 units); the second argument is true for kernels whose stores also carry sc1 (M and K
+# launches that move more than 256 MiB), the third for grids of more than one pass over the GPU,
+# whose row blocks are dealt to the XCDs in turn
+KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3, false, false>",
+                "m_groups_skinny": "rearrange_kernel<0, false, false>",
+                "m_groups_experts": "rearrange_kernel<3, false, false>", "k_groups": "rearrange_kernel<7, false, false>",
+                "k_groups_large": "rearrange_kernel<2, true, true>",
+                "experts_3d_small": "rearrange_kernel<4, false, false>",
+                "experts_3d_e16": "rearrange_kernel<4, false, false>",
+                "experts_3d_e64": "rearrange_kernel<5, false, true>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",
                 "quant_m_groups_skinny": "quantize_dim0_kernel",
                 "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",

@@ -126,6 +126,14 @@ def test_wide_rows_and_many_experts(env):
         run_3d(env, host_experts(rng, E, rows, cols), label="wide")
 
 
+@pytest.mark.parametrize("E,rows,cols", [(24, 8192, 160), (96, 8192, 160)])
+def test_multi_pass_grids(env, E, rows, cols):
+    # 1536 units of 256 threads and 6144 units of 512 threads: more than the GPU holds at once, so
+    # their row blocks are dealt to the XCDs in turn
+    rng = np.random.default_rng(44)
+    run_3d(env, host_experts(rng, E, rows, cols), label="multi-pass grid")
+
+
 def test_experts_sharing_one_matrix(env):
     # expert stride 0: every expert reads the same matrix (an expanded view)
     gsf, oracle, torch = env

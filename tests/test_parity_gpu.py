@@ -322,6 +322,31 @@ def test_launches_past_the_mall_size(env, kind, rows, cols):
     run_case(env, kind, scales, offs, label="past the MALL size")
 
 
+# --------------------------------------------------------------------------
+# grids of more than one pass over the GPU (row blocks dealt to the XCDs in
+# turn), below the size that takes the sc1 stores
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,rows,cols,ld", [
+    ("M", 1 << 18, 160, 160),    # row segments, 4112 units of 256 threads
+    ("M", 1 << 20, 44, 44),      # flat strips, 8200 units
+    ("M", 1 << 20, 32, 32),      # narrow row segments, 8200 units
+    ("K", 14336, 8192, 8192),    # 256-column windows of line-aligned rows, 3696 units, 235 MB
+    ("K", 8192, 8196, 8196),     # 128-column windows of other rows, 4224 units
+])
+def test_multi_pass_grids(env, kind, rows, cols, ld):
+    import workloads
+
+    gsf, oracle, torch = env
+    G = 8
+    rng = np.random.default_rng(43)
+    offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25)
+    size = gsf.mx_rearrange_M_groups_out_bytes if kind == "M" else gsf.mx_rearrange_K_groups_out_bytes
+    assert rows * cols + size(rows, cols, G) <= (256 << 20), "the case must stay below the sc1-store size"
+    scales = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    run_case(env, kind, scales, offs, label="multi-pass grid")
+
+
 def test_repeat_is_deterministic(env):
     import workloads
 

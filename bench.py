@@ -84,12 +84,13 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3, false, false>",
                 "experts_3d_small": "rearrange_kernel<4, false, false>",
                 "experts_3d_e16": "rearrange_kernel<4, false, false>",
                 "experts_3d_e64": "rearrange_kernel<5, false, true>",
-                "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel",
-                "quant_m_groups_skinny": "quantize_dim0_kernel",
+                "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel<true, true>",
+                "quant_m_groups_skinny": "quantize_dim0_kernel<true, true>",
                 "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",
-                "pad_m_groups_small": "pad_kernel<true, true, true>", "pad_m_groups": "pad_kernel<true, true, true>",
-                "inverse_m_groups_skinny": "unrearrange_kernel<false, true>",
-                "inverse_k_groups_large": "unrearrange_kernel<true, true>",
+                "pad_m_groups_small": "pad_kernel<true, true, true, false>",
+                "pad_m_groups": "pad_kernel<true, true, true, true>",
+                "inverse_m_groups_skinny": "unrearrange_kernel<false, true, false>",
+                "inverse_k_groups_large": "unrearrange_kernel<true, true, true>",
                 "quant_3d_small": "quantize_dim1_kernel", "quant_3d_e16": "quantize_dim1_kernel"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")

@@ -61,9 +61,9 @@
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
-#include <vector>
 
 #include "group_table.h"
+#include "launch_order.h"
 #include "mx_rearrange.h"
 #include "write_ranges.h"
 
@@ -644,18 +644,9 @@ void rearrange_kernel(Params p) {
   extern __shared__ __align__(16) uint8_t lds[];
   bool first_iter = true;
   for (int64_t vb = blockIdx.x; vb < p.vunits; vb += gridDim.x) {
-    // workgroup b runs on XCD b mod 8. Interleaved grids (IL): row block r
-    // (the units of one output or input row block, in order) goes to XCD r
-    // mod 8, so that the eight XCDs sweep neighbouring row blocks together;
-    // otherwise each XCD takes a contiguous range of units. Either way the
-    // units that share boundary lines run on one XCD, whose L2 then holds them.
-    int64_t unit;
-    if constexpr (IL) {
-      const int64_t k = vb >> 3;
-      unit = ((k / p.per_row) * 8 + (vb & 7)) * p.per_row + k % p.per_row;
-    } else {
-      unit = (vb & 7) * (p.vunits >> 3) + (vb >> 3);
-    }
+    // the order of units over the XCDs (launch_order.h): row blocks dealt in
+    // turn (IL) or contiguous ranges
+    const int64_t unit = unit_of_slot<IL>(vb, p.vunits, p.per_row);
     if (unit >= p.units) continue;
     if (!first_iter) __syncthreads();  // LDS of the previous unit is no longer read
     first_iter = false;
@@ -875,36 +866,6 @@ int launch_3d(const uint8_t *scales, int64_t experts, int64_t rows, int64_t cols
   return dispatch(p, units > k3dWideUnits ? kMode3dWide : kMode3d, units, stream);
 }
 
-// Workgroups of kernel `fn` (threads per workgroup, bytes of LDS) the current
-// GPU holds at once: CUs times the runtime's occupancy answer, kept per device,
-// kernel, size and LDS bytes. 0 when a query fails.
-int64_t resident_workgroups(const void *fn, int threads, size_t lds) {
-  struct Entry {
-    int dev;
-    const void *fn;
-    int threads;
-    size_t lds;
-    int64_t n;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    for (const Entry &e : cache)
-      if (e.dev == dev && e.fn == fn && e.threads == threads && e.lds == lds) return e.n;
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess)
-    return 0;
-  const int64_t n = int64_t(cus) * per_cu;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cache.size() < 1024) cache.push_back(Entry{dev, fn, threads, lds, n});
-  return n;
-}
-
 // The kernel of a mode: <MODE, WT (sc1 stores), IL (interleaved grid)>. The
 // sc1 stores are built for the modes that run launches past the MALL size (M
 // row segments and flat strips, K windows of line-aligned rows and of other
@@ -968,8 +929,7 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
   const int64_t resident = resident_workgroups(kernel_for(mode, false, false), threads, lds_bytes);
   const bool il = mode != kModeKWindowsWide && (wt || (resident > 0 && units > resident));
   const void *fn = kernel_for(mode, wt && is_write_through_mode(mode), il);
-  const int64_t blocks = units / p.per_row;
-  p.vunits = il ? int64_t(8) * ((blocks + 7) / 8) * p.per_row : round_up(units, 8);
+  p.vunits = slots_for(il, units, p.per_row);
   // one workgroup per unit slot; the grid is a multiple of 8, so a workgroup
   // that loops (only past kMaxGrid slots) stays on its XCD
   const int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);

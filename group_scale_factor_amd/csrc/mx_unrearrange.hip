@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "group_table.h"
+#include "launch_order.h"
 #include "mx_rearrange.h"
 #include "write_ranges.h"
 
@@ -349,15 +350,15 @@ __device__ __forceinline__ void zero_region(uint8_t *out, int64_t ld, int64_t r0
   }
 }
 
-template <bool KGROUPS, bool SMALL>
+template <bool KGROUPS, bool SMALL, bool IL>
 __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearrange_kernel(UParams p) {
   using GK = typename std::conditional<SMALL, GKWide, GKNarrow>::type;   // K window geometry
   extern __shared__ __align__(16) int ulds[];
   uint32_t *strip = reinterpret_cast<uint32_t *>(ulds);
   int *group_lds = ulds + kTileRows * UnitGeom<KGROUPS, SMALL>::pitch;
-  const int64_t n8 = int64_t(gridDim.x) / 8 * 8;
-  const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
-                                             : int64_t(blockIdx.x);
+  // the order of units over the XCDs (launch_order.h); slots past the last
+  // unit map to units >= p.units, which do nothing
+  const int64_t u = unit_of_slot<IL>(blockIdx.x, gridDim.x, p.per_row);
   if (!KGROUPS) {
     const int64_t ob = u / p.per_row;                  // output row block of the blocked layout
     const int cc = int(u - ob * p.per_row);
@@ -446,6 +447,17 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+template <bool KGROUPS, bool SMALL>
+const void *kernel_of(bool il) {
+  return il ? reinterpret_cast<const void *>(&unrearrange_kernel<KGROUPS, SMALL, true>)
+            : reinterpret_cast<const void *>(&unrearrange_kernel<KGROUPS, SMALL, false>);
+}
+
+const void *kernel_for(bool kgroups, bool small, bool il) {
+  return kgroups ? (small ? kernel_of<true, true>(il) : kernel_of<true, false>(il))
+                 : (small ? kernel_of<false, true>(il) : kernel_of<false, false>(il));
+}
+
 int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64_t cols, const int32_t *offs,
                        int32_t groups, uint8_t *out, int64_t ld, hipStream_t stream) {
   const int64_t lim = (int64_t(1) << 31) - 1;
@@ -479,16 +491,23 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
   }
   const int pitch = wide ? GKWide::pitch : kgroups ? GKNarrow::pitch : GM::pitch;
   const int threads = wide ? GKWide::threads : kgroups ? GKNarrow::threads : GM::threads;
-  if (p.units > max_grid(threads)) return MX_REARRANGE_ESHAPE;
+  if (slots_for(true, p.units, p.per_row) > max_grid(threads)) return MX_REARRANGE_ESHAPE;
   p.blocked_bytes = kgroups ? mx_rearrange_K_groups_out_bytes(rows, cols, groups)
                             : mx_rearrange_M_groups_out_bytes(rows, cols, groups);
   const size_t lds = size_t(kTileRows) * pitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
-  const void *fn = kgroups ? (small ? reinterpret_cast<const void *>(&unrearrange_kernel<true, true>)
-                                    : reinterpret_cast<const void *>(&unrearrange_kernel<true, false>))
-                           : (small ? reinterpret_cast<const void *>(&unrearrange_kernel<false, true>)
-                                    : reinterpret_cast<const void *>(&unrearrange_kernel<false, false>));
+  // A grid of more than one pass over the GPU deals whole row blocks to the
+  // XCDs in turn (launch_order.h): measured on (28672, 8192) K groups 80.7
+  // against 85.0 us. A grid of one pass keeps contiguous ranges (interleaved,
+  // the (131072, 44) M inverse took 4.89 against 4.58 us).
+  const bool il = [&] {
+    const void *plain = kernel_for(kgroups, small, false);
+    const int64_t resident = resident_workgroups(plain, threads, lds);
+    return resident > 0 && p.units > resident;
+  }();
+  const void *fn = kernel_for(kgroups, small, il);
+  const int64_t grid = slots_for(il, p.units, p.per_row);
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(threads), args, lds, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(threads), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

@@ -94,6 +94,18 @@ def test_workloads(env, name):
     run_pad(env, w.data, w.offs, label=name)
 
 
+@pytest.mark.parametrize("ld,G", [(5120, 80), (5123, 8)])
+def test_multi_pass_grids(env, ld, G):
+    # (16640, 5120) rows with 80 groups (table in LDS) on the 16-byte path, and 8 groups with a row stride
+    # that takes the byte path: more workgroups than the GPU holds at once, dealt to the XCDs in turn
+    import workloads
+
+    rng = np.random.default_rng(62)
+    data = rng.integers(0, 256, size=(16640, 5120), dtype=np.uint8)
+    offs = workloads.random_offsets(rng, 16640, G, p_empty=0.25)
+    run_pad(env, data, offs, ld=ld, label="multi-pass grid")
+
+
 def test_fuzz_aligned_and_unaligned(env):
     import workloads
 

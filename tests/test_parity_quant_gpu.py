@@ -223,6 +223,18 @@ def test_many_groups(env):
         run_quant(env, pins.random_bf16_rows(rng, rows, K), offs, label="many groups")
 
 
+def test_multi_pass_grid_many_groups(env):
+    # 2500 quantising workgroups, more than the GPU holds at once (row blocks dealt to the XCDs in
+    # turn), with the group table of 80 groups in LDS
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(61)
+    rows, K = 40000, 512
+    offs = workloads.random_offsets(rng, rows, 80, p_empty=0.25)
+    run_quant(env, pins.random_bf16_rows(rng, rows, K), offs, label="multi-pass grid, 80 groups")
+
+
 def test_invalid_offsets_are_clamped(env):
     import pins
 

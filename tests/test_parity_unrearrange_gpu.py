@@ -148,6 +148,19 @@ def _fuzz(env, kind, seed, n):
                     misalign=misalign, label="fuzz%s-%d" % (kind, i))
 
 
+@pytest.mark.parametrize("kind,rows,cols,G", [("M", 1 << 20, 44, 8), ("K", 14336, 8192, 100)])
+def test_multi_pass_grids(env, kind, rows, cols, G):
+    # 8200 M units of 128 threads; 7168 K windows of 128 columns (the table of 100 groups in LDS):
+    # more than the GPU holds at once, so row blocks are dealt to the XCDs in turn
+    import workloads
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(63)
+    offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25)
+    run_inverse(env, kind, random_blocked(rng, oracle, kind, rows, cols, G), rows, cols, offs,
+                label="multi-pass grid")
+
+
 def test_fuzz_M(env):
     _fuzz(env, "M", 62, 100)
 

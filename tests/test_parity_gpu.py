@@ -343,8 +343,47 @@ def test_multi_pass_grids(env, kind, rows, cols, ld):
     offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25)
     size = gsf.mx_rearrange_M_groups_out_bytes if kind == "M" else gsf.mx_rearrange_K_groups_out_bytes
     assert rows * cols + size(rows, cols, G) <= (256 << 20), "the case must stay below the sc1-store size"
-    scales = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
-    run_case(env, kind, scales, offs, label="multi-pass grid")
+    run_case(env, kind, workloads.random_scales(rng, rows, cols, ld), offs, label="multi-pass grid")
+
+
+def test_multi_pass_fuzz(env):
+    """Seeded random shapes whose grids take more than one pass over the GPU (row blocks dealt to the XCDs
+    in turn): ragged row counts, packed and strided rows, bases off 16-byte and 128-byte lines, 1 to 200
+    groups (tables past 64 groups), empty groups and short totals. A grid is multi-pass for certain when it
+    has more units than 256 CUs x 2048 threads / its workgroup size; each case checks a lower bound on its
+    unit count against that."""
+    import workloads
+
+    rng = np.random.default_rng(46)
+    layouts = ["M flat", "M packed", "M strided", "K line-aligned", "K other"] * 2
+    for i, layout in enumerate(layouts):
+        kind = layout[0]
+        G = int(rng.choice([1, 5, 8, 64, 65, 200]))
+        misalign = int(rng.choice([0, 1, 4, 16, 128]))
+        if kind == "M":
+            # flat strips (packed rows of <= 60 bytes, not whole 16-byte pieces), packed rows of whole
+            # pieces (row segments, narrow when chunked), rows with a stride
+            cols = int(rng.choice({"M flat": [20, 33, 44, 60], "M packed": [32, 48, 96, 160],
+                                   "M strided": [17, 44, 100, 160]}[layout]))
+            ld = cols + (int(rng.choice([1, 4, 16, 36])) if layout == "M strided" else 0)
+            rows = int(rng.integers(530_000, 800_000))
+            assert rows // 128 > 4096
+        else:
+            cols = int(rng.integers(6000, 8300))
+            rows = int(rng.integers(10240, 16000))
+            if layout == "K line-aligned":
+                ld, misalign = (cols + 127) // 128 * 128, int(rng.choice([0, 128]))
+            else:
+                ld = cols + int(rng.choice([0, 1, 5, 16]))
+                if (ld % 128 == 0) and misalign % 128 == 0:
+                    misalign = 4
+            # more than 512 windows of 512 columns (so not the one-pass wide windows), hence more than
+            # 1024 of 256 columns (512 threads) and 2048 of 128 columns (256 threads)
+            assert (rows // 128) * (cols // 512) > 512
+        offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25,
+                                        short_total=bool(rng.random() < 0.2))
+        run_case(env, kind, workloads.random_scales(rng, rows, cols, ld), offs, misalign=misalign,
+                 label="multi-pass fuzz %d (%s)" % (i, layout))
 
 
 def test_repeat_is_deterministic(env):

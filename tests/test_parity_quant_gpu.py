@@ -235,6 +235,25 @@ def test_multi_pass_grid_many_groups(env):
     run_quant(env, pins.random_bf16_rows(rng, rows, K), offs, label="multi-pass grid, 80 groups")
 
 
+def test_multi_pass_fuzz(env):
+    """Seeded random casts whose grids take more than one pass over the GPU (128-row blocks dealt to the
+    XCDs in turn): ragged row counts, K not a multiple of 512 (a partial last unit of each row), row strides,
+    group tables in registers and in LDS. Each case has more than 2048 quantising workgroups of 256 threads
+    (16 units of 512 elements each), more than the GPU holds at once."""
+    import pins
+    import workloads
+
+    rng = np.random.default_rng(65)
+    for i, K in enumerate([96, 544, 1408, 2048]):
+        chunks = (K + 511) // 512
+        rows = int(rng.integers(40_000 // chunks + 2000, 40_000 // chunks + 12_000))
+        assert rows * chunks // 16 > 2048
+        ld = K + 8 * int(rng.choice([0, 0, 1, 5]))
+        G = int(rng.choice([1, 8, 65, 200]))
+        offs = workloads.random_offsets(rng, rows, G, p_empty=0.25, short_total=bool(rng.random() < 0.2))
+        run_quant(env, pins.random_bf16_rows(rng, rows, K), offs, ld=ld, label="multi-pass fuzz %d" % i)
+
+
 def test_invalid_offsets_are_clamped(env):
     import pins
 

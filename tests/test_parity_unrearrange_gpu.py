@@ -161,6 +161,31 @@ def test_multi_pass_grids(env, kind, rows, cols, G):
                 label="multi-pass grid")
 
 
+def test_multi_pass_fuzz(env):
+    """Seeded random shapes whose inverse grids take more than one pass over the GPU: ragged row counts,
+    output strides and bases of every kind, group tables in registers and in LDS. M units run 128 threads
+    (more than 4096 units), K windows 512 or 256 threads (more than 1024 and 2048 units)."""
+    import workloads
+
+    gsf, oracle, torch = env
+    rng = np.random.default_rng(64)
+    for i in range(6):
+        kind = "M" if i % 2 == 0 else "K"
+        G = int(rng.choice([1, 8, 64, 65, 300]))
+        if kind == "M":
+            rows, cols = int(rng.integers(530_000, 800_000)), int(rng.choice([17, 44, 60, 100, 160]))
+            assert rows // 128 > 4096
+        else:
+            rows, cols = int(rng.integers(10240, 16000)), int(rng.integers(6000, 8300))
+            assert (rows // 128) * (cols // 256) > 1024
+        ld = cols + int(rng.choice([0, 1, 4, 16, 128 - cols % 128]))
+        misalign = int(rng.choice([0, 1, 4, 16, 128]))
+        offs = workloads.random_offsets(rng, rows if kind == "M" else cols, G, p_empty=0.25,
+                                        short_total=bool(rng.random() < 0.2))
+        run_inverse(env, kind, random_blocked(rng, oracle, kind, rows, cols, G), rows, cols, offs, ld=ld,
+                    misalign=misalign, label="multi-pass fuzz %d" % i)
+
+
 def test_fuzz_M(env):
     _fuzz(env, "M", 62, 100)
 

@@ -76,7 +76,8 @@ PAGES_US = {"m_groups_skinny": 19.46, "k_groups": 49.08, "k_groups_large": 315.4
 # alignment), 4 = per-expert row segments, 5 = the same with 512 threads (grids of more than
 # 2048 units); the second argument is true for kernels whose stores also carry sc1 (M and K
 # launches that move more than 256 MiB), the third for grids of more than one pass over the GPU,
-# whose row blocks are dealt to the XCDs in turn
+# whose row blocks are dealt to the XCDs in turn; quantize_dim1_kernel<SMALL, PAIR>: PAIR for two
+# feature blocks per workgroup (the per-expert cast of K a multiple of 128)
 KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3, false, false>",
                 "m_groups_skinny": "rearrange_kernel<0, false, false>",
                 "m_groups_experts": "rearrange_kernel<3, false, false>", "k_groups": "rearrange_kernel<7, false, false>",
@@ -86,12 +87,12 @@ KERNEL_NAMES = {"m_groups_tiny": "rearrange_kernel<3, false, false>",
                 "experts_3d_e64": "rearrange_kernel<5, false, true>",
                 "quant_m_groups_small": "quantize_dim0_kernel", "quant_m_groups": "quantize_dim0_kernel<true, true>",
                 "quant_m_groups_skinny": "quantize_dim0_kernel<true, true>",
-                "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel",
+                "quant_k_groups_small": "quantize_dim1_kernel", "quant_k_groups": "quantize_dim1_kernel<true, false>",
                 "pad_m_groups_small": "pad_kernel<true, true, true, false>",
                 "pad_m_groups": "pad_kernel<true, true, true, true>",
                 "inverse_m_groups_skinny": "unrearrange_kernel<false, true, false>",
                 "inverse_k_groups_large": "unrearrange_kernel<true, true, true>",
-                "quant_3d_small": "quantize_dim1_kernel", "quant_3d_e16": "quantize_dim1_kernel"}
+                "quant_3d_small": "quantize_dim1_kernel", "quant_3d_e16": "quantize_dim1_kernel<true, true>"}
 CSRC = os.path.join(ROOT, "group_scale_factor_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -347,11 +347,14 @@ struct Q1Params {
   int group_tokens;      // > 0: every group holds exactly this many tokens (stacked expert weights),
                          // each with its own input matrix and its own N x group_tokens code matrix
   int diagonal;          // unit order: 0 token chunks fastest, 1 diagonal over feature blocks
+                         // (with two feature blocks per workgroup, quantize_dim1_kernel<., true>)
   int64_t padded_rows;   // round_up(N, 128)
   int64_t scale_bytes;   // padded_rows * (T/32 + 4G)
   int64_t units;         // chunk_units * nb
+  int64_t wg_units;      // workgroups: chunk_units * nbw
   int N;
   int nb;                // feature blocks of 128
+  int nbw;               // feature-block groups of one workgroup each (nb, or ceil(nb/2) in pairs)
   int groups;
 };
 
@@ -530,53 +533,96 @@ __device__ __forceinline__ int scale_exponent(uint32_t m) {
   return s;
 }
 
-template <bool SMALL>
-__global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
-  extern __shared__ __align__(16) int lds1[];
-  uint32_t *tile = reinterpret_cast<uint32_t *>(lds1);
-  int *group_lds = lds1 + kTileDwords;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+// Feature blocks per workgroup: two with the diagonal order, else one.
+__host__ __device__ inline int dim1_blocks(const Q1Params &p) { return p.diagonal ? 2 : 1; }
 
-  // contiguous unit ranges per XCD (workgroup b runs on XCD b mod 8)
-  const int64_t n8 = p.units / 8 * 8;
-  const int64_t u = int64_t(blockIdx.x) < n8 ? (int64_t(blockIdx.x) & 7) * (n8 >> 3) + (int64_t(blockIdx.x) >> 3)
-                                             : int64_t(blockIdx.x);
-  // Token chunks vary fastest: units that run together write neighbouring
-  // pieces of the same transposed code rows, which meet in L2 as whole lines.
-  // When every unit writes whole lines (per-group codes, groups of a multiple
-  // of 128 tokens) the diagonal order instead spreads the units that run
-  // together over feature blocks, so their reads of the token rows do not all
-  // fall on the same column slice (4% faster at token rows 16 KB apart).
+// The unit (tile column ci, feature block fb) of half `half` of workgroup b,
+// with `blocks` feature blocks per workgroup. Workgroups form contiguous
+// ranges per XCD (workgroup b runs on XCD b mod 8). Token chunks vary fastest:
+// units that run together write neighbouring pieces of the same transposed
+// code rows, which meet in L2 as whole lines. When every unit writes whole
+// lines (per-group codes, groups of a multiple of 128 tokens) the diagonal
+// order instead spreads the units that run together over feature blocks, so
+// their reads of the token rows do not all fall on the same column slice (4%
+// faster at token rows 16 KB apart). live is false for the idle half of a
+// last, single block. A host test checks that every unit gets exactly one slot.
+struct Dim1Slot {
+  int64_t ci;
+  int fb;
+  bool live;
+};
+__host__ __device__ inline Dim1Slot dim1_slot(const Q1Params &p, int64_t b, int blocks, int half) {
+  const int64_t n8 = p.wg_units / 8 * 8;
+  const int64_t u = b < n8 ? (b & 7) * (n8 >> 3) + (b >> 3) : b;
   const int64_t chunk_units = p.units / p.nb;
-  const int64_t ci = u % chunk_units;           // tile column (chunk) index over all groups
-  const int fb = p.diagonal ? int((u / chunk_units + ci) % p.nb) : int(u / chunk_units);   // feature block
+  const int64_t ci = u % chunk_units;
+  const int fbw = p.diagonal ? int((u / chunk_units + ci) % p.nbw) : int(u / chunk_units);
+  const int fb = blocks * fbw + half;
+  return Dim1Slot{ci, fb, fb < p.nb};
+}
+
+// PAIR: one workgroup of twice the threads takes two neighbouring feature
+// blocks of the same token chunk; its halves quantise one block each from the
+// two staged tiles (each token row then reads 512 bytes, not 256). Used with
+// the diagonal order: 395.7 against 405.8 us on the (16, 5120, 8192) expert
+// weights; in token-chunk-first order on (131072, 7168) tokens it was slower
+// (579 against 550 us), so that order keeps one block per workgroup.
+template <bool PAIR>
+constexpr int dim1_threads() { return PAIR ? 2 * kThreads : kThreads; }
+// LDS of a paired workgroup at most: two staged tiles and the group table
+constexpr int kDim1PairMaxLds = 2 * kTileDwords * 4 + 3 * kMaxGroupsDim1 * 4;
+static_assert(kDim1PairMaxLds <= 160 * 1024 && kTileDwords * 4 + 3 * kMaxGroupsDim1 * 4 <= 64 * 1024,
+              "LDS per workgroup");
+
+template <bool SMALL, bool PAIR>
+__global__ __launch_bounds__(dim1_threads<PAIR>()) void quantize_dim1_kernel(Q1Params p) {
+  constexpr int kBlocks = PAIR ? 2 : 1;            // feature blocks per workgroup
+  constexpr int kThreadsW = dim1_threads<PAIR>();
+  extern __shared__ __align__(16) int lds1[];
+  int *group_lds = lds1 + kBlocks * kTileDwords;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave_w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int half = wave_w / kWavesPerGroup;          // the feature block of this half of the workgroup
+  const int wave = wave_w % kWavesPerGroup;
+  const int ht = int(threadIdx.x) % kThreads;        // thread index within the half
+  uint32_t *tile = reinterpret_cast<uint32_t *>(lds1) + half * kTileDwords;
+
+  const Dim1Slot sl = dim1_slot(p, blockIdx.x, kBlocks, half);
+  const int64_t ci = sl.ci;                     // tile column (chunk) index over all groups
+  const int fb = sl.fb;                         // feature block of this half
+  const int fb0 = fb - half;                    // first feature block of the workgroup
+  const bool live = sl.live;
 
   Groups1<SMALL> grp;
   grp.init(p, group_lds);
   const Dim1Unit un = dim1_unit(p, grp, ci, fb);
-  if (un.spare) {
+  if (un.spare) {   // (spare depends on ci only: the whole workgroup returns here)
+    if (!live) return;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t a = un.zero.begin + 16 * threadIdx.x; a < un.zero.full; a += 16 * kThreads)
+    for (int64_t a = un.zero.begin + 16 * ht; a < un.zero.full; a += 16 * kThreads)
       *reinterpret_cast<u32x4 *>(p.scales + a) = z;
-    for (int64_t a = un.zero.full + 4 * threadIdx.x; a < un.zero.end; a += 4 * kThreads)
+    for (int64_t a = un.zero.full + 4 * ht; a < un.zero.end; a += 4 * kThreads)
       *reinterpret_cast<uint32_t *>(p.scales + a) = 0u;
     return;
   }
   const int ntok = un.ntok;
   const int64_t x_row0 = un.x_row0, q_col0 = un.q_col0, tile_off = un.tile_off;
 
-  // stage the 128 x 128 bf16 tile: 16 pieces of 16 bytes per token row, 8 per lane
+  // stage the 128 x 128 bf16 tile of each feature block: 16 pieces of 16
+  // bytes per token row and block, 8 per lane (the token range is the same
+  // for both halves, it depends on ci only)
   {
-    const int f_base = fb * kTileFeat;
+    constexpr int kPieces = 16 * kBlocks;      // pieces per token row
+    const int f_base = fb0 * kTileFeat;
     const __amdgpu_buffer_rsrc_t rsrc =
         byte_buffer(p.x + x_row0 + f_base, uint32_t(int64_t(ntok) * p.ld * 2));
+    uint32_t *tiles = reinterpret_cast<uint32_t *>(lds1);
     uint4 v[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int slot = int(threadIdx.x) + it * kThreads;
-      const int t = slot >> 4, k = slot & 15;
+      const int slot = int(threadIdx.x) + it * kThreadsW;
+      const int t = slot / kPieces, k = slot % kPieces;
       const bool valid = t < ntok && f_base + 8 * k < p.N;
       const uint32_t off = valid ? uint32_t(t) * uint32_t(p.ld) * 2u + 16u * uint32_t(k) : kOutOfRange;
       const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(off), 0, kStreamPolicy);
@@ -584,12 +630,14 @@ __global__ __launch_bounds__(kThreads) void quantize_dim1_kernel(Q1Params p) {
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int slot = int(threadIdx.x) + it * kThreads;
-      const int t = slot >> 4, k = slot & 15;
-      *reinterpret_cast<uint4 *>(tile + tile_row(t) + 4 * k) = mask_features(v[it], f_base + 8 * k, p.N);
+      const int slot = int(threadIdx.x) + it * kThreadsW;
+      const int t = slot / kPieces, k = slot % kPieces;
+      *reinterpret_cast<uint4 *>(tiles + (k / 16) * kTileDwords + tile_row(t) + 4 * (k % 16)) =
+          mask_features(v[it], f_base + 8 * k, p.N);
     }
   }
   __syncthreads();
+  if (!live) return;
 
   // quantise two feature columns (2p, 2p+1) of one 32-token block (tb)
   const int pl = lane >> 2, tb = lane & 3;
@@ -659,18 +707,34 @@ bool dim1_geometry(Q1Params &p, int64_t N) {
   // tile columns: every group's plus the trailing tokens' plus at least one spare
   const int64_t chunk_units = (p.T + kTileTok - 1) / kTileTok + p.groups + 1;
   p.units = chunk_units * p.nb;
-  return p.units <= max_grid(kThreads);
+  const bool pair = dim1_blocks(p) == 2;
+  p.nbw = pair ? (p.nb + 1) / 2 : p.nb;
+  p.wg_units = chunk_units * p.nbw;
+  return p.wg_units <= max_grid(pair ? dim1_threads<true>() : dim1_threads<false>());
+}
+
+template <bool PAIR>
+const void *dim1_kernel_of(bool small) {
+  return small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true, PAIR>)
+               : reinterpret_cast<const void *>(&quantize_dim1_kernel<false, PAIR>);
 }
 
 // Grid and launch of the dim1 cast.
 int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
   if (!dim1_geometry(p, N)) return MX_REARRANGE_ESHAPE;
   const bool small = p.groups <= kWave;
-  const size_t lds = size_t(kTileDwords) * 4 + (small ? 0 : size_t(3) * p.groups * sizeof(int));
-  const void *fn = small ? reinterpret_cast<const void *>(&quantize_dim1_kernel<true>)
-                         : reinterpret_cast<const void *>(&quantize_dim1_kernel<false>);
+  const bool pair = dim1_blocks(p) == 2;
+  const size_t lds = size_t(pair ? 2 : 1) * kTileDwords * 4 + (small ? 0 : size_t(3) * p.groups * sizeof(int));
+  const void *fn = pair ? dim1_kernel_of<true>(small) : dim1_kernel_of<false>(small);
+  // two staged tiles take more than the default 64 KB of LDS (gfx950: up to
+  // 160 KB per workgroup); the allowance is always set to the same largest
+  // size, so that concurrent calls never lower it under one another
+  if (pair && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDim1PairMaxLds) != hipSuccess)
+    return MX_REARRANGE_ELAUNCH;
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.units)), dim3(kThreads), args, lds, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.wg_units)), dim3(unsigned(pair ? dim1_threads<true>()
+                                                                                          : dim1_threads<false>())),
+                                       args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

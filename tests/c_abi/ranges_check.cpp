@@ -125,14 +125,29 @@ std::vector<int64_t> random_offsets(std::mt19937_64 &rng, int G, int64_t total, 
 // dim1 cast
 // ---------------------------------------------------------------------------
 
-// Checks every unit of one launch; `exact` adds the exactly-once coverage checks.
+// Checks every unit of one launch, reached as the kernel reaches it (workgroup,
+// then the half of a workgroup of two feature blocks, dim1_slot); every unit
+// must be reached exactly once. `exact` adds the exactly-once coverage checks of
+// the bytes written.
 void check_dim1(const Q1Params &p, const Table1 &t, bool exact, const std::string &name) {
   const int64_t chunk_units = p.units / p.nb;
+  const int blocks = dim1_blocks(p);
   std::vector<uint8_t> scale_hits(exact ? size_t(p.scale_bytes) : 0, 0);
   std::vector<uint8_t> token_hits(exact ? size_t(p.T / 32) * p.nb : 0, 0);
+  std::vector<uint8_t> unit_hits(size_t(p.units), 0);
   const int64_t x_extent = p.group_tokens > 0 ? 0 : p.T * p.ld;   // elements
-  for (int fb = 0; fb < p.nb; ++fb) {
-    for (int64_t ci = 0; ci < chunk_units; ++ci) {
+  if (p.wg_units * blocks < p.units) fail(name + ": fewer unit slots than units");
+  for (int64_t wg = 0; wg < p.wg_units; ++wg) {
+    for (int half = 0; half < blocks; ++half) {
+      const Dim1Slot sl = dim1_slot(p, wg, blocks, half);
+      if (sl.ci < 0 || sl.ci >= chunk_units || sl.fb < 0 || sl.live != (sl.fb < p.nb)) {
+        fail(name + ": workgroup slot outside the units");
+        continue;
+      }
+      if (!sl.live) continue;
+      ++unit_hits[size_t(sl.fb) * chunk_units + sl.ci];
+      const int fb = sl.fb;
+      const int64_t ci = sl.ci;
       const Dim1Unit un = dim1_unit(p, t, ci, fb);
       if (un.spare) {
         const ZeroSpan &z = un.zero;
@@ -167,6 +182,11 @@ void check_dim1(const Q1Params &p, const Table1 &t, bool exact, const std::strin
       }
     }
   }
+  for (size_t k = 0; k < unit_hits.size(); ++k)
+    if (unit_hits[k] != 1) {
+      fail(name + ": unit " + std::to_string(k) + " reached " + std::to_string(unit_hits[k]) + " times");
+      break;
+    }
   if (exact) {
     for (int64_t b = 0; b < p.scale_bytes; ++b)
       if (scale_hits[size_t(b)] != 1) {
@@ -198,6 +218,8 @@ void dim1_cases(std::mt19937_64 &rng) {
       p.ld = N + 8 * int64_t(rng() % 3);
       p.x_gstride = K * p.ld + 8 * int64_t(rng() % 4);
       p.q_gstride = N * K;
+      // the entry point's rule (K a multiple of 128), and every other case too
+      p.diagonal = K % 128 == 0 || (it / 4) % 2 == 1;
       p.scale_bytes = mx_quantize_dim1_3d_scale_bytes(E, K, N);
     } else {
       p.T = 32 * int64_t(rng() % 40);

@@ -564,7 +564,7 @@ __host__ __device__ inline Dim1Slot dim1_slot(const Q1Params &p, int64_t b, int 
 // PAIR: one workgroup of twice the threads takes two neighbouring feature
 // blocks of the same token chunk; its halves quantise one block each from the
 // two staged tiles (each token row then reads 512 bytes, not 256). Used with
-// the diagonal order: 395.7 against 405.8 us on the (16, 5120, 8192) expert
+// the diagonal order: 395.4 against 405.8 us on the (16, 5120, 8192) expert
 // weights; in token-chunk-first order on (131072, 7168) tokens it was slower
 // (579 against 550 us), so that order keeps one block per workgroup.
 template <bool PAIR>

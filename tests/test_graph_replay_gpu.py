@@ -112,6 +112,19 @@ def test_quantize_dim0_dim1_and_experts(env):
     s3 = torch.empty(gsf.mx_quantize_dim1_3d_scale_bytes(w.experts, w.K, w.N), dtype=torch.uint8, device="cuda")
     check_graph(torch, "quant_3d_small", lambda: gsf.mx_quantize_dim1_3d(wt, q=q3, scales=s3), [q3, s3])
 
+    # K a multiple of 128: two feature blocks per workgroup (the kernel whose LDS allowance the host raises)
+    import pins
+
+    rng = np.random.default_rng(91)
+    E, K, N = 3, 256, 300
+    wb = np.zeros((E, K, 304), np.uint16)    # rows padded to 304 elements (16-byte strides)
+    for e in range(E):
+        wb[e, :, :N] = pins.random_bf16_rows(rng, K, N)
+    wp = torch.from_numpy(wb.view(np.int16)).cuda().view(torch.bfloat16)[:, :, :N]
+    qp = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
+    sp = torch.empty(gsf.mx_quantize_dim1_3d_scale_bytes(E, K, N), dtype=torch.uint8, device="cuda")
+    check_graph(torch, "quant_3d paired blocks", lambda: gsf.mx_quantize_dim1_3d(wp, q=qp, scales=sp), [qp, sp])
+
 
 def test_pad_unpad_and_inverse(env):
     import workloads

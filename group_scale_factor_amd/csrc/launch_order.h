@@ -4,11 +4,12 @@
 // Workgroup b of a launch runs on XCD b mod 8. A grid that fits the chip in
 // one pass (no more workgroups than the GPU holds at once) gives each XCD a
 // contiguous range of units: units that share cache lines at their edges run
-// under one L2. A larger grid deals whole row blocks (the `per_block` units of
-// one 128-row block, in order) to the XCDs in turn, so that the eight XCDs
-// sweep neighbouring row blocks of memory together, as a streaming copy does,
-// while a row block's shared lines still stay in one L2. Each kernel is built
-// in both orders; the host picks one per launch.
+// under one L2. A larger grid deals runs of `per_block` consecutive units
+// (whole 128-row blocks, or a part of one where its units share no lines but
+// the edges of the run) to the XCDs in turn, so that the eight XCDs sweep
+// neighbouring rows of memory together, as a streaming copy does, while the
+// lines shared inside a run stay in one L2. Each kernel is built in both
+// orders; the host picks one per launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +21,7 @@
 namespace {
 
 // Unit of workgroup slot `slot` in a grid of contiguous ranges (`slots` a
-// multiple of 8) or of interleaved row blocks of `per_block` units. Host and
+// multiple of 8) or of interleaved runs of `per_block` units. Host and
 // device: a CPU test checks that every unit gets exactly one slot.
 template <bool INTERLEAVED>
 __host__ __device__ inline int64_t unit_of_slot(int64_t slot, int64_t slots, int64_t per_block) {
@@ -32,9 +33,9 @@ __host__ __device__ inline int64_t unit_of_slot(int64_t slot, int64_t slots, int
   }
 }
 
-// Workgroup slots for `units` units of `per_block` per row block (the last
-// block may hold fewer): a multiple of 8 that covers every unit (slots past the
-// last unit do nothing).
+// Workgroup slots for `units` units in runs of `per_block` (the last run may
+// hold fewer): a multiple of 8 that covers every unit (slots past the last
+// unit do nothing).
 inline int64_t slots_for(bool interleaved, int64_t units, int64_t per_block) {
   if (interleaved) {
     const int64_t blocks = (units + per_block - 1) / per_block;

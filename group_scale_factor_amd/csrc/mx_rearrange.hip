@@ -51,9 +51,10 @@
 //   * Work units are spread over the 8 XCDs (workgroups are dealt to XCDs
 //     round-robin) so that units sharing boundary cache lines run on the same
 //     XCD, keeping those lines in one L2. Grids of more than one pass over
-//     the chip deal whole row blocks to the XCDs in turn, so that the chip as
-//     a whole reads neighbouring rows; one-pass grids give each XCD a
-//     contiguous range of units.
+//     the chip deal runs of units to the XCDs in turn (four row blocks for M
+//     and per-expert units; for K windows, 11 windows of a row block), so
+//     that the chip as a whole reads neighbouring rows; one-pass grids give
+//     each XCD a contiguous range of units.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -110,6 +111,10 @@ constexpr int k3dLoadPolicy = 2;
 // faster on M groups of 336 MB, 0.5-2.5% on K shapes of 336 to 941 MB;
 // within 1% at 168-235 MB and 4-11% slower on smaller launches.
 constexpr int64_t kWriteThroughBytes = int64_t(256) << 20;
+// Runs of the interleaved XCD order (dispatch()): K windows per run, M and
+// per-expert row blocks per run.
+constexpr int kKDealWindows = 11;
+constexpr int kMDealBlocks = 4;
 constexpr int kStoreNtSc1 = 2 | 16;
 
 // Staging modes; each is its own kernel instantiation (two for the modes that
@@ -200,6 +205,7 @@ struct Params {
   int64_t out_bytes;   // whole output allocation
   int64_t units;       // work units
   int64_t vunits;      // workgroup slots: a multiple of 8 covering every unit
+  int64_t deal;        // interleaved order: consecutive units dealt to one XCD at a time
   int rows;
   int cols;
   int groups;
@@ -644,9 +650,9 @@ void rearrange_kernel(Params p) {
   extern __shared__ __align__(16) uint8_t lds[];
   bool first_iter = true;
   for (int64_t vb = blockIdx.x; vb < p.vunits; vb += gridDim.x) {
-    // the order of units over the XCDs (launch_order.h): row blocks dealt in
-    // turn (IL) or contiguous ranges
-    const int64_t unit = unit_of_slot<IL>(vb, p.vunits, p.per_row);
+    // the order of units over the XCDs (launch_order.h): runs of p.deal units
+    // dealt in turn (IL) or contiguous ranges
+    const int64_t unit = unit_of_slot<IL>(vb, p.vunits, p.deal);
     if (unit >= p.units) continue;
     if (!first_iter) __syncthreads();  // LDS of the previous unit is no longer read
     first_iter = false;
@@ -919,8 +925,9 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
 
   const int threads = threads_for(mode);
   // A grid of more than one pass over the workgroups the GPU holds at once
-  // deals whole row blocks to the XCDs in turn (rows of every XCD's units are
-  // then neighbours in memory, and each pass reads one region of the input),
+  // deals runs of units (row blocks, or for K a part of one) to the XCDs in
+  // turn (rows of every XCD's units are then neighbours in memory, and each
+  // pass reads one region of the input),
   // measured 3-11% faster on such grids: (28672, 8192) K groups 75.8 against
   // 80.3 us, 64 x 8192 x 160 per-expert 28.85 against 30.1, (1048576, 160) M
   // groups 60.8 against 63.2. A grid of one pass keeps contiguous ranges per
@@ -929,7 +936,22 @@ int dispatch(Params &p, int mode, int64_t units, hipStream_t stream) {
   const int64_t resident = resident_workgroups(kernel_for(mode, false, false), threads, lds_bytes);
   const bool il = mode != kModeKWindowsWide && (wt || (resident > 0 && units > resident));
   const void *fn = kernel_for(mode, wt && is_write_through_mode(mode), il);
-  p.vunits = slots_for(il, units, p.per_row);
+  // The interleaved order deals runs of consecutive units to the XCDs in turn.
+  // M and per-expert units: four whole row blocks per run (a row block's units
+  // share lines at their edges), measured 60.1 against 60.9 us on (1048576,
+  // 160) M groups, 34.5 against 34.9 on (524288, 160), the same on (6291456,
+  // 44) and on 64 x 8192 x 160 per-expert scales; a run of half a row block
+  // took 83.4 us on (1048576, 160). K windows: runs of kKDealWindows windows
+  // when a row block holds at least twice that many units, else whole row
+  // blocks: (28672, 8192) 74.9 against 75.9 us, (8192, 16384) 44.2 against
+  // 45.1, (28672, 12288) 112.1 against 113.0, rows off 128-byte lines (14336,
+  // 8196) 43.0 against 43.7; with 4096 columns (17 units per row block) whole
+  // row blocks stayed best (runs of 11: 23.7 against 23.1 us on (14336, 4096)).
+  if (is_k(mode))
+    p.deal = p.per_row >= 2 * kKDealWindows ? kKDealWindows : p.per_row;
+  else
+    p.deal = int64_t(kMDealBlocks) * p.per_row;
+  p.vunits = slots_for(il, units, p.deal);
   // one workgroup per unit slot; the grid is a multiple of 8, so a workgroup
   // that loops (only past kMaxGrid slots) stays on its XCD
   const int64_t grid = std::min<int64_t>(p.vunits, kMaxGrid);

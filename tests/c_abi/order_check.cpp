@@ -1,11 +1,11 @@
 // Host check of how work units are dealt to workgroup slots (no GPU; built by
 // tests/test_launch_order.py with hipcc, host code only).
 //
-// For both orders of launch_order.h and many unit counts and row-block sizes
-// (whole and partial last blocks), the slots that slots_for() asks for, mapped
+// For both orders of launch_order.h and many unit counts and run lengths
+// (whole and partial last runs), the slots that slots_for() asks for, mapped
 // by unit_of_slot(), give every unit in [0, units) exactly one slot and give
 // the other slots units at or past `units` (which do nothing). In the
-// interleaved order the units of one row block also share an XCD (slot mod 8).
+// interleaved order the units of one run also share an XCD (slot mod 8).
 // Prints "ok" and exits 0 when every check holds.
 
 #include "../../group_scale_factor_amd/csrc/launch_order.h"
@@ -39,7 +39,7 @@ void check(int64_t units, int64_t per_block) {
       int &x = xcd_of_block[size_t(u / per_block)];
       if (x < 0) x = int(s & 7);
       else if (x != int(s & 7) && failures++ < 20)
-        std::fprintf(stderr, "row block %lld on two XCDs\n", (long long)(u / per_block));
+        std::fprintf(stderr, "run %lld on two XCDs\n", (long long)(u / per_block));
     }
   }
   for (int64_t u = 0; u < units; ++u)
@@ -56,7 +56,7 @@ void check(int64_t units, int64_t per_block) {
 int main() {
   std::mt19937_64 rng(7);
   for (int64_t units = 0; units <= 300; ++units)
-    for (int64_t per_block : {1, 2, 3, 7, 8, 13, 32, 33}) {
+    for (int64_t per_block : {1, 2, 3, 4, 7, 8, 11, 13, 32, 33, 44}) {
       check<false>(units, per_block);
       check<true>(units, per_block);
     }

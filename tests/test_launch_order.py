@@ -1,9 +1,10 @@
 """Host check of the order in which the kernels deal work units to workgroup slots (no GPU).
 
 tests/c_abi/order_check.cpp includes csrc/launch_order.h and runs, on the CPU, the very functions
-the kernels and their launches use: for both orders (contiguous ranges per XCD, row blocks dealt to
-the XCDs in turn) and many unit counts and row-block sizes, including a last row block that is
-only partly filled, every unit gets exactly one slot, and an interleaved row block stays on one XCD.
+the kernels and their launches use: for both orders (contiguous ranges per XCD, runs of units dealt
+to the XCDs in turn) and many unit counts and run lengths (among them the forward kernels' runs of
+11 K windows and of 4 row blocks), including a last run that is only partly filled, every unit gets
+exactly one slot, and an interleaved run stays on one XCD.
 """
 
 import os

@@ -62,6 +62,7 @@ using GKNarrow = UGeom<256, 128>;
 template <bool KGROUPS, bool SMALL>
 using UnitGeom = typename std::conditional<KGROUPS, typename std::conditional<SMALL, GKWide, GKNarrow>::type, GM>::type;
 constexpr int kUMaxGroups = 4096;
+constexpr int kUKDealWindows = 11;   // K windows per run of the interleaved XCD order
 constexpr int64_t kUMaxRowStride = int64_t(1) << 30;
 static_assert(kTileRows * GKWide::pitch * 4 <= 64 * 1024 &&
                   kTileRows * GKNarrow::pitch * 4 + 2 * kUMaxGroups * 4 <= 64 * 1024 &&
@@ -80,6 +81,7 @@ struct UParams {
   int groups;
   int padded_cols;       // M: round_up(cols, 4)
   int per_row;           // M: units per output row block; K: units per 128-row block
+  int64_t deal;          // interleaved order: consecutive units dealt to one XCD at a time
 };
 
 // K groups: clamped cumulative ends e (scale columns) and cumulative padded
@@ -358,7 +360,7 @@ __global__ __launch_bounds__((UnitGeom<KGROUPS, SMALL>::threads)) void unrearran
   int *group_lds = ulds + kTileRows * UnitGeom<KGROUPS, SMALL>::pitch;
   // the order of units over the XCDs (launch_order.h); slots past the last
   // unit map to units >= p.units, which do nothing
-  const int64_t u = unit_of_slot<IL>(blockIdx.x, gridDim.x, p.per_row);
+  const int64_t u = unit_of_slot<IL>(blockIdx.x, gridDim.x, p.deal);
   if (!KGROUPS) {
     const int64_t ob = u / p.per_row;                  // output row block of the blocked layout
     const int cc = int(u - ob * p.per_row);
@@ -491,13 +493,19 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
   }
   const int pitch = wide ? GKWide::pitch : kgroups ? GKNarrow::pitch : GM::pitch;
   const int threads = wide ? GKWide::threads : kgroups ? GKNarrow::threads : GM::threads;
-  if (slots_for(true, p.units, p.per_row) > max_grid(threads)) return MX_REARRANGE_ESHAPE;
+  // The interleaved order deals runs of consecutive units to the XCDs in
+  // turn: whole row blocks, or for K windows runs of kUKDealWindows when a
+  // row block holds at least twice that many (its windows share no output
+  // line): (28672, 8192) K inverse 79.3-79.9 against 80.6-81.1 us; runs of 8
+  // or 16 windows took 81.5-82.1 us.
+  p.deal = kgroups && p.per_row >= 2 * kUKDealWindows ? kUKDealWindows : p.per_row;
+  if (slots_for(true, p.units, p.deal) > max_grid(threads)) return MX_REARRANGE_ESHAPE;
   p.blocked_bytes = kgroups ? mx_rearrange_K_groups_out_bytes(rows, cols, groups)
                             : mx_rearrange_M_groups_out_bytes(rows, cols, groups);
   const size_t lds = size_t(kTileRows) * pitch * 4 + (small ? 0 : size_t(2) * groups * sizeof(int));
-  // A grid of more than one pass over the GPU deals whole row blocks to the
-  // XCDs in turn (launch_order.h): measured on (28672, 8192) K groups 80.7
-  // against 85.0 us. A grid of one pass keeps contiguous ranges (interleaved,
+  // A grid of more than one pass over the GPU deals runs of units (p.deal) to
+  // the XCDs in turn (launch_order.h): with whole row blocks, measured on
+  // (28672, 8192) K groups 80.7 against 85.0 us. A grid of one pass keeps contiguous ranges (interleaved,
   // the (131072, 44) M inverse took 4.89 against 4.58 us).
   const bool il = [&] {
     const void *plain = kernel_for(kgroups, small, false);
@@ -505,7 +513,7 @@ int launch_unrearrange(bool kgroups, const uint8_t *blocked, int64_t rows, int64
     return resident > 0 && p.units > resident;
   }();
   const void *fn = kernel_for(kgroups, small, il);
-  const int64_t grid = slots_for(il, p.units, p.per_row);
+  const int64_t grid = slots_for(il, p.units, p.deal);
   void *args[] = {&p};
   const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(threads), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;

@@ -57,6 +57,7 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr int kUnitElems = 512;       // elements per wave-unit: 16 blocks, 4 tile columns of scales
 constexpr int kUnroll = 4;            // units per wave, loads issued back to back (swept: 2..16)
+constexpr int kDim0DealWgs = 48;      // workgroups per run of the interleaved XCD order (dim0 cast)
 constexpr int kMaxGroups = 4096;      // LDS holds two int arrays of this many groups
 constexpr int64_t kMaxRowStride = int64_t(1) << 26;   // elements; keeps unit offsets in 32 bits
 constexpr int kStreamPolicy = 2;      // buffer load bit 1: non-temporal
@@ -78,7 +79,7 @@ struct QParams {
   int groups;
   int tile_cols;         // round_up(K/32, 4) / 4
   int64_t data_slots;    // workgroup slots of the quantising workgroups (a multiple of 8 covering them)
-  int64_t block_wgs;     // quantising workgroups per 128 input rows
+  int64_t deal;          // interleaved order: consecutive workgroups dealt to one XCD at a time
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -283,12 +284,9 @@ __global__ __launch_bounds__(kThreads) void quantize_dim0_kernel(QParams p) {
   MGroups<SMALL> grp;
   if (int64_t(blockIdx.x) < p.data_slots) {
     // Workgroup b runs on XCD b mod 8. Each XCD takes a contiguous range of
-    // units, or, for grids of more than one pass, whole 128-row blocks in turn
-    // (launch_order.h): either way the 32 rows whose scale words share a
-    // 128-byte line of a tile are written through one L2 (whole-line
-    // write-backs instead of partial ones from several XCDs). Slots past the
-    // last workgroup quantise nothing.
-    const int64_t b = unit_of_slot<IL>(blockIdx.x, p.data_slots, p.block_wgs);
+    // units, or, for grids of more than one pass, runs of p.deal workgroups in
+    // turn (launch_order.h). Slots past the last workgroup quantise nothing.
+    const int64_t b = unit_of_slot<IL>(blockIdx.x, p.data_slots, p.deal);
     // the data loads go out first; the group scan overlaps them
     const int64_t u0 = (b * kWavesPerGroup + wave) * kUnroll;
     uint4 v[kUnroll];
@@ -774,21 +772,26 @@ int mx_quantize_dim0_M_groups(const uint16_t *x, int64_t rows, int64_t K, int64_
   p.scales = blocked_scales;
   p.ld = row_stride;
   int64_t grid = dim0_geometry(p, rows, K, num_groups);
-  // a 128-row block is 128 * chunks units, a whole number of workgroups
-  p.block_wgs = int64_t(kTileRows) * p.chunks / (kWavesPerGroup * kUnroll);
-  if (grid - p.data_groups + slots_for(true, p.data_groups, p.block_wgs) > max_grid(kThreads))
+  if (grid - p.data_groups + slots_for(true, p.data_groups, int64_t(kDim0DealWgs)) > max_grid(kThreads))
     return MX_REARRANGE_ESHAPE;
   const bool small = num_groups <= kWave;
   const size_t lds = small ? 0 : size_t(2) * num_groups * sizeof(int);
-  // A grid of more than one pass over the GPU deals whole 128-row blocks to
-  // the XCDs in turn (launch_order.h): measured on the (131072, 1408) cast 92.0
-  // against 95.1 us and on (16640, 5120) 45.5 against 45.7. A grid of one pass
-  // keeps contiguous ranges.
+  // A grid of more than one pass over the GPU deals runs of kDim0DealWgs
+  // workgroups to the XCDs in turn (launch_order.h). With whole 128-row blocks
+  // as the runs (the 32 rows whose scale words share a tile line then write
+  // them through one L2) it measured 92.0 against 95.1 us on the (131072, 1408)
+  // cast and 45.5 against 45.7 on (16640, 5120) next to contiguous ranges;
+  // runs of 48 workgroups then measured faster or the same on six of seven
+  // shapes: (131072, 1408) 90.0 against 91.3 us, (16640, 5120) 45.0 against
+  // 45.5, (49152, 4096) 97.1 against 98.2, (262144, 512) 66.4 against 67.0,
+  // (100000, 1024) 52.2 against 52.5, (65536, 2048) the same, (32768, 7168)
+  // 114.1 against 113.9. A grid of one pass keeps contiguous ranges.
   const bool il = [&] {
     const int64_t resident = resident_workgroups(dim0_kernel_for(small, false), kThreads, lds);
     return resident > 0 && p.data_groups > resident;
   }();
-  p.data_slots = slots_for(il, p.data_groups, p.block_wgs);
+  p.deal = kDim0DealWgs;
+  p.data_slots = slots_for(il, p.data_groups, p.deal);
   grid = p.data_slots + p.pad_blocks;
   const void *fn = dim0_kernel_for(small, il);
   void *args[] = {&p};

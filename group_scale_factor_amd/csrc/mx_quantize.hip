@@ -58,6 +58,7 @@ constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr int kUnitElems = 512;       // elements per wave-unit: 16 blocks, 4 tile columns of scales
 constexpr int kUnroll = 4;            // units per wave, loads issued back to back (swept: 2..16)
 constexpr int kDim0DealWgs = 48;      // workgroups per run of the interleaved XCD order (dim0 cast)
+constexpr int kDim1DealUnits = 64;    // workgroups per run of the interleaved XCD order (2-D dim1 cast)
 constexpr int kMaxGroups = 4096;      // LDS holds two int arrays of this many groups
 constexpr int64_t kMaxRowStride = int64_t(1) << 26;   // elements; keeps unit offsets in 32 bits
 constexpr int kStreamPolicy = 2;      // buffer load bit 1: non-temporal
@@ -350,6 +351,8 @@ struct Q1Params {
   int64_t scale_bytes;   // padded_rows * (T/32 + 4G)
   int64_t units;         // chunk_units * nb
   int64_t wg_units;      // workgroups: chunk_units * nbw
+  int64_t deal;          // > 0: runs of this many workgroups dealt to the XCDs in turn; 0: contiguous ranges
+  int64_t slots;         // workgroups launched: wg_units, or more for runs (the extra ones do nothing)
   int N;
   int nb;                // feature blocks of 128
   int nbw;               // feature-block groups of one workgroup each (nb, or ceil(nb/2) in pairs)
@@ -536,27 +539,34 @@ __host__ __device__ inline int dim1_blocks(const Q1Params &p) { return p.diagona
 
 // The unit (tile column ci, feature block fb) of half `half` of workgroup b,
 // with `blocks` feature blocks per workgroup. Workgroups form contiguous
-// ranges per XCD (workgroup b runs on XCD b mod 8). Token chunks vary fastest:
+// ranges per XCD (workgroup b runs on XCD b mod 8), or, with p.deal > 0, runs
+// of p.deal workgroups dealt to the XCDs in turn. Token chunks vary fastest:
 // units that run together write neighbouring pieces of the same transposed
 // code rows, which meet in L2 as whole lines. When every unit writes whole
 // lines (per-group codes, groups of a multiple of 128 tokens) the diagonal
 // order instead spreads the units that run together over feature blocks, so
 // their reads of the token rows do not all fall on the same column slice (4%
 // faster at token rows 16 KB apart). live is false for the idle half of a
-// last, single block. A host test checks that every unit gets exactly one slot.
+// last, single block and for slots past the workgroups. A host test checks
+// that every unit gets exactly one slot.
 struct Dim1Slot {
   int64_t ci;
   int fb;
   bool live;
 };
 __host__ __device__ inline Dim1Slot dim1_slot(const Q1Params &p, int64_t b, int blocks, int half) {
-  const int64_t n8 = p.wg_units / 8 * 8;
-  const int64_t u = b < n8 ? (b & 7) * (n8 >> 3) + (b >> 3) : b;
+  int64_t u;
+  if (p.deal > 0) {
+    u = unit_of_slot<true>(b, p.slots, p.deal);
+  } else {
+    const int64_t n8 = p.wg_units / 8 * 8;
+    u = b < n8 ? (b & 7) * (n8 >> 3) + (b >> 3) : b;
+  }
   const int64_t chunk_units = p.units / p.nb;
   const int64_t ci = u % chunk_units;
   const int fbw = p.diagonal ? int((u / chunk_units + ci) % p.nbw) : int(u / chunk_units);
   const int fb = blocks * fbw + half;
-  return Dim1Slot{ci, fb, fb < p.nb};
+  return Dim1Slot{ci, fb, fb < p.nb && u < p.wg_units};
 }
 
 // PAIR: one workgroup of twice the threads takes two neighbouring feature
@@ -708,7 +718,9 @@ bool dim1_geometry(Q1Params &p, int64_t N) {
   const bool pair = dim1_blocks(p) == 2;
   p.nbw = pair ? (p.nb + 1) / 2 : p.nb;
   p.wg_units = chunk_units * p.nbw;
-  return p.wg_units <= max_grid(pair ? dim1_threads<true>() : dim1_threads<false>());
+  p.deal = 0;
+  p.slots = p.wg_units;
+  return slots_for(true, p.wg_units, kDim1DealUnits) <= max_grid(pair ? dim1_threads<true>() : dim1_threads<false>());
 }
 
 template <bool PAIR>
@@ -729,10 +741,24 @@ int launch_dim1(Q1Params &p, int64_t N, hipStream_t stream) {
   // size, so that concurrent calls never lower it under one another
   if (pair && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDim1PairMaxLds) != hipSuccess)
     return MX_REARRANGE_ELAUNCH;
+  const int threads = pair ? dim1_threads<true>() : dim1_threads<false>();
+  // The token-chunk-first order of a grid of more than one pass deals runs of
+  // kDim1DealUnits workgroups (token chunks of one feature block) to the XCDs
+  // in turn; units that run together on one XCD still complete each other's
+  // code lines in its L2. On 131072 x 7168 tokens: 528-529 us against 549-550
+  // with contiguous ranges per XCD (runs of 48 to 128: 526-530 us; 16: 543;
+  // 256: 537; whole feature blocks: 563). The diagonal order of the paired
+  // expert cast keeps contiguous ranges (runs of 64: the same; 16 and 256
+  // slower).
+  if (!pair) {
+    const int64_t resident = resident_workgroups(fn, threads, lds);
+    if (resident > 0 && p.wg_units > resident) {
+      p.deal = kDim1DealUnits;
+      p.slots = slots_for(true, p.wg_units, p.deal);
+    }
+  }
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.wg_units)), dim3(unsigned(pair ? dim1_threads<true>()
-                                                                                          : dim1_threads<false>())),
-                                       args, lds, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3(unsigned(p.slots)), dim3(unsigned(threads)), args, lds, stream);
   return e == hipSuccess ? MX_REARRANGE_OK : MX_REARRANGE_ELAUNCH;
 }
 

@@ -136,11 +136,11 @@ void check_dim1(const Q1Params &p, const Table1 &t, bool exact, const std::strin
   std::vector<uint8_t> token_hits(exact ? size_t(p.T / 32) * p.nb : 0, 0);
   std::vector<uint8_t> unit_hits(size_t(p.units), 0);
   const int64_t x_extent = p.group_tokens > 0 ? 0 : p.T * p.ld;   // elements
-  if (p.wg_units * blocks < p.units) fail(name + ": fewer unit slots than units");
-  for (int64_t wg = 0; wg < p.wg_units; ++wg) {
+  if (p.wg_units * blocks < p.units || p.slots < p.wg_units) fail(name + ": fewer unit slots than units");
+  for (int64_t wg = 0; wg < p.slots; ++wg) {
     for (int half = 0; half < blocks; ++half) {
       const Dim1Slot sl = dim1_slot(p, wg, blocks, half);
-      if (sl.ci < 0 || sl.ci >= chunk_units || sl.fb < 0 || sl.live != (sl.fb < p.nb)) {
+      if (sl.ci < 0 || sl.ci >= chunk_units || sl.fb < 0 || (sl.live && sl.fb >= p.nb)) {
         fail(name + ": workgroup slot outside the units");
         continue;
       }
@@ -234,7 +234,13 @@ void dim1_cases(std::mt19937_64 &rng) {
       fail("dim1 geometry rejected a small shape");
       continue;
     }
-    const std::string name = "dim1 case " + std::to_string(it);
+    // every third case in runs of workgroups dealt to the XCDs in turn (the order of large launches),
+    // with the launch's run length or a random one
+    if (it % 3 == 1) {
+      p.deal = it % 2 ? kDim1DealUnits : 1 + int64_t(rng() % 20);
+      p.slots = slots_for(true, p.wg_units, p.deal);
+    }
+    const std::string name = "dim1 case " + std::to_string(it) + (p.deal ? " (runs)" : "");
     // the correct table: exact coverage (offsets that break the order are clamped by the scan)
     check_dim1(p, scan1(p, offs, 1), true, name);
     // corrupted tables: bounds only

@@ -427,6 +427,29 @@ def test_profile_digest_ignores_comments_only():
     assert bench.kernel_source_digest("m_groups_skinny", lambda p: files[p]) != d1
 
 
+def test_counter_profiles_match_the_kernels():
+    """Every committed HBM counter profile was taken from the kernel code in the tree (its digest matches),
+    names the workload's own kernel source, and reads within a few percent of the algorithmic bytes on the
+    workloads larger than a few fixed per-launch fetches. A kernel changed after its counters were taken
+    fails here until they are taken again (bench.py would report its traffic as null meanwhile)."""
+    import json
+
+    import bench
+
+    paths = sorted(p for p in os.listdir(bench.PROFILES) if p.startswith("pmc_") and p.endswith(".json"))
+    assert len(paths) >= 14
+    for fname in paths:
+        with open(os.path.join(bench.PROFILES, fname)) as f:
+            d = json.load(f)
+        name = d["workload"]
+        assert fname == "pmc_%s.json" % name
+        assert d["kernel_source"] == os.path.basename(bench.kernel_source(name)), name
+        assert d["kernel_source_sha256_16"] == bench.kernel_source_digest(name), name
+        ratio = int(d["hbm_bytes_per_launch"]) / int(d["algorithmic_bytes_per_launch"])
+        if int(d["algorithmic_bytes_per_launch"]) >= 1 << 20:
+            assert 0.99 <= ratio <= 1.08, (name, ratio)
+
+
 def test_grids_past_one_launch_are_rejected(lib):
     """A launch holds fewer than 2^32 work-items; entry points whose grid would not fit one launch
     (outputs of over 100 GB) return MX_REARRANGE_ESHAPE before any HIP call, and the largest sizes

@@ -20,6 +20,7 @@
  * break this are clamped into [previous end, rows]. 1 <= num_groups <= 4096.
  * Sizes: rows + 128*num_groups < 2^31, cols < 2^31, row strides <= 2^30.
  * Ownership: the caller owns every buffer; nothing is allocated or kept.
+ * Calls are thread-safe, as for the entry points of mx_rearrange.h.
  * Errors: the MX_REARRANGE_* status codes of mx_rearrange.h, nothing enqueued.
  */
 #ifndef MX_PAD_H

@@ -82,6 +82,7 @@ static inline int64_t mx_quantize_dim0_M_groups_scale_bytes(int64_t rows, int64_
  * (the rest is the zero tail of the M-groups allocation).
  *
  * Ownership: the caller owns every buffer; nothing is allocated or kept.
+ * Calls are thread-safe, as for the entry points of mx_rearrange.h.
  * Errors (negative status, nothing enqueued): MX_REARRANGE_ESHAPE for sizes and
  * strides, MX_REARRANGE_EGROUPS for num_groups, MX_REARRANGE_ENULL for a missing
  * pointer, MX_REARRANGE_EALIGN for alignment, MX_REARRANGE_ELAUNCH when the

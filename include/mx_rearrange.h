@@ -64,8 +64,11 @@
  *   stream             HIP stream the single kernel is enqueued on (NULL: the
  *                      default stream).
  *
- * Ownership: the caller owns every buffer; the library allocates nothing,
- * keeps no state and holds no pointer after returning. Calls are thread-safe.
+ * Ownership: the caller owns every buffer; the library allocates nothing and
+ * holds no pointer after returning. Its only internal state is a per-device
+ * cache of kernel occupancy answers (which pick the grid order), filled under
+ * a lock on first use. Calls are thread-safe: any number of host threads may
+ * call any entry point at once, each on its own stream.
  *
  * Errors: a negative status is returned and nothing is enqueued when an
  * argument is invalid (see MX_REARRANGE_E*); the checks read no device memory.

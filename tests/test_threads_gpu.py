@@ -122,20 +122,31 @@ outs = [[[torch.empty(shape, dtype=torch.uint8, device=dev) for shape in c[2]] f
 torch.cuda.synchronize()
 failures = []
 start = threading.Barrier(THREADS)
+count_lock = threading.Lock()
+done = [0]
 
 
 def worker(t):
+    try:
+        run(t)
+    except BaseException as exc:   # a thread that dies must fail the run, not vanish
+        failures.append("thread %d raised %r" % (t, exc))
+
+
+def run(t):
     order = [(t * 5 + k) % len(cases) for k in range(len(cases))]
     if t % 2:
         order.reverse()
     with torch.cuda.stream(streams[t]):
-        start.wait()
+        start.wait(timeout=120)
         for rep in range(REPEATS):
             for i in order:
                 label, launch, _, wants = cases[i]
                 for o in outs[t][i]:
                     o.fill_((0x5A + 17 * t + rep) & 0xFF)
                 launch(outs[t][i])
+                with count_lock:
+                    done[0] += 1
             streams[t].synchronize()
             for i in order:
                 label, _, _, wants = cases[i]
@@ -150,8 +161,8 @@ for th in threads:
 for th in threads:
     th.join()
 torch.cuda.synchronize()
-print("threads %d, cases %d, repeats %d" % (THREADS, len(cases), REPEATS))
-if failures:
+print("threads %d, cases %d, repeats %d, calls %d" % (THREADS, len(cases), REPEATS, done[0]))
+if failures or done[0] != THREADS * REPEATS * len(cases):
     print("\n".join(failures[:20]))
     sys.exit(1)
 print("threaded calls: ok")
